@@ -1,0 +1,72 @@
+"""Selection probes: inputs whose output reveals, as exact integers, which cache positions a
+query attended to.  Tolerance-based parity cannot see a causal off-by-one (one extra position
+out of 32,768 moves the output far below any float tolerance), so these probes make the
+selected set itself observable.
+
+Count/bit-sum probe: with a zero query every score is 0 and every softmax weight is exactly
+1/n, so o_lat[r] = (1/n) * sum_{j selected} c_j[r].  Latent channels hold exact 0/1 values:
+  channel r < 17          : bit r of the position j
+  channels 17 .. 33       : bit (r-17) of a hash of j
+  channel 34              : 1 (so o_lat[34] * n == n)
+  channels 35 .. R-1      : 0
+Then round(o_lat[r] * n) = number of selected positions with that bit set, and
+n = round(exp(lse)) because lse = ln(sum_j exp(0)) = ln(n).  Comparing these integers with
+the ones computed from the expected set checks the set (up to collisions of all 35 bit sums,
+which a shifted or widened causal bound cannot produce).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+N_POS_BITS = 17
+N_HASH_BITS = 17
+ONE_CHANNEL = N_POS_BITS + N_HASH_BITS
+BF16_ONE = 0x3F80
+
+
+def position_hash(j: np.ndarray) -> np.ndarray:
+    j = np.asarray(j, dtype=np.uint64)
+    h = (j * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)
+    h ^= h >> np.uint64(15)
+    return (h * np.uint64(0x9E3779B1)) & np.uint64(0x1FFFF)
+
+
+def coded_cache(B: int, L_max: int, R: int, cache_len) -> np.ndarray:
+    """[B, L_max, R] bf16 bits with the position code in every valid row; rows at or past
+    cache_len[b] are NaN so any read of them poisons the output."""
+    assert R >= ONE_CHANNEL + 1
+    j = np.arange(L_max, dtype=np.int64)
+    bits = np.zeros((L_max, R), np.uint16)
+    for r in range(N_POS_BITS):
+        bits[:, r] = np.where((j >> r) & 1, BF16_ONE, 0)
+    hj = position_hash(j).astype(np.int64)
+    for r in range(N_HASH_BITS):
+        bits[:, N_POS_BITS + r] = np.where((hj >> r) & 1, BF16_ONE, 0)
+    bits[:, ONE_CHANNEL] = BF16_ONE
+    out = np.repeat(bits[None], B, axis=0)
+    for b in range(B):
+        out[b, int(cache_len[b]):] = 0x7FC0
+    return out
+
+
+def expected_counts(positions: np.ndarray) -> np.ndarray:
+    """The 35 integers the probe must recover for a selected set."""
+    p = np.asarray(positions, dtype=np.int64)
+    hj = position_hash(p).astype(np.int64)
+    cnt = [int(((p >> r) & 1).sum()) for r in range(N_POS_BITS)]
+    cnt += [int(((hj >> r) & 1).sum()) for r in range(N_HASH_BITS)]
+    cnt.append(int(p.size))
+    return np.array(cnt, np.int64)
+
+
+def decoded_counts(o_lat_row: np.ndarray, lse: float) -> tuple[np.ndarray, int]:
+    """Integers recovered from one (query, head) output row of the probe."""
+    n = int(np.rint(np.exp(float(lse))))
+    vals = np.asarray(o_lat_row[: ONE_CHANNEL + 1], np.float64) * n
+    return np.rint(vals).astype(np.int64), n
+
+
+def decode_error(o_lat_row: np.ndarray, n: int) -> float:
+    """Largest distance of o_lat*n from the nearest integer (should be << 0.5)."""
+    vals = np.asarray(o_lat_row[: ONE_CHANNEL + 1], np.float64) * n
+    return float(np.max(np.abs(vals - np.rint(vals))))
