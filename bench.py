@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the absorbed-MLA hot path on one MI355X.
+
+One step = the whole path over one batch: mla_absorb_q -> mla_latent_attn (split kernel +
+log-sum-exp merge) -> mla_up_v, on the single-token decode workload with batch 32, cache
+length 8192, 64 heads, 256-dim heads, latent 512 (bf16 inputs, fp32 outputs).  Inputs are
+resident in HBM before the timed region; three input sets rotate so the 256 MB Infinity Cache
+cannot hold the 256 MiB latent cache between steps.
+
+Prints ONE JSON line: value = latent-cache GB/s over whole steps (bytes of latent rows the
+path reads per step / step time).  `roofline` is the dominant call, the latent attention,
+timed with HIP events on the stream it is launched on.  `secondary` is the 6-position
+verification pass (batch 16, cache 32768) in TFLOP/s against the bf16 matrix-core peak.
+`cpu_baseline` is the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak
+NSETS = 3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("latent_attn.hip", "mla_device.h", "mla_internal.h"):
+        h.update(open(os.path.join(ROOT, "mla_latent_cache_absorb_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if recorded for this exact kernel
+    source (profiles/traffic_<workload>.md holds 'key: value' lines)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_latent_attn_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def visible_rows(w) -> int:
+    """Latent rows the attention reads: every visible position of every query (dense), or every
+    listed position (indexed).  Queries of one sequence share rows in the dense case."""
+    import numpy as np
+    if w.idx is not None:
+        return int(w.idx_len.sum())
+    B, Q = w.q.shape[:2]
+    return int(np.sum(w.cache_len.astype(np.int64)))  # the longest query's prefix covers the others
+
+
+def attended_positions(w) -> int:
+    """Sum over queries of the positions each attends to (for FLOP counts)."""
+    import numpy as np
+    if w.idx is not None:
+        return int(w.idx_len.astype(np.int64).sum())
+    B, Q = w.q.shape[:2]
+    return int(sum(int(w.cache_len[b]) - Q + i + 1 for b in range(B) for i in range(Q)))
+
+
+def to_device(w, dev):
+    import numpy as np
+    import torch
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    d = dict(q=bf(w.q), cache=bf(w.cache), w_k=bf(w.w_k), w_v=bf(w.w_v),
+             cache_len=torch.from_numpy(w.cache_len).to(dev))
+    if w.idx is not None:
+        d["idx"] = torch.from_numpy(w.idx).to(dev)
+        d["idx_len"] = torch.from_numpy(w.idx_len).to(dev)
+    return d
+
+
+def time_path(name: str, steps: int, warmup: int, nsets: int):
+    """Run the path; returns per-step and per-stage times (ms) and the workload."""
+    import torch
+    from mla_latent_cache_absorb_amd import binding, workloads as wl
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {nsets} input set(s) for {name}")
+    ws = [wl.make_workload(name, set_index=s) for s in range(nsets)]
+    sets = [to_device(w, dev) for w in ws]
+    w0 = ws[0]
+    B, Q, H, D = w0.q.shape
+    R = w0.cache.shape[2]
+    Lmax = int(w0.cache.shape[1])
+    indexed = w0.idx is not None
+    K_max = w0.idx.shape[2] if indexed else Lmax
+    splits = binding.mla_latent_attn_num_splits(B, Q, H, K_max, 0)
+    q_abs = torch.empty((B, Q, H, R), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev)
+    ws_bytes = binding.mla_latent_attn_workspace_size(B, Q, H, R, K_max, 0)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        d = sets[s % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        binding.mla_absorb_q(d["q"], d["w_k"], q_abs=q_abs)
+        if ev is not None:
+            ev[1].record(stream)
+        if indexed:
+            binding.mla_latent_attn_indexed(q_abs, d["cache"], d["cache_len"], d["idx"], d["idx_len"], Lmax,
+                                            w0.scale, 0, o_lat=o_lat, lse=lse, workspace=workspace)
+        else:
+            binding.mla_latent_attn(q_abs, d["cache"], d["cache_len"], Lmax, w0.scale, 0, o_lat=o_lat, lse=lse,
+                                    workspace=workspace)
+        if ev is not None:
+            ev[2].record(stream)
+        binding.mla_up_v(o_lat, d["w_v"], out=out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    # whole steps, back to back
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(steps):
+        step(warmup + s)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / steps
+    # per-stage durations, one event quadruple per step (same launches, same stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for s in range(steps):
+        step(warmup + steps + s, evs[s])
+    torch.cuda.synchronize()
+    stage = {k: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+             for j, k in enumerate(("absorb_q", "latent_attn", "up_v"))}
+    del sets
+    torch.cuda.empty_cache()
+    return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, splits=splits, workload=w0)
+
+
+def cpu_baseline(name: str, budget_s: float = 12.0):
+    """The fp64 oracle (expanded form) on whole sequences of the same workload, until about
+    budget_s of CPU time has been spent."""
+    import numpy as np
+    import oracle
+    from mla_latent_cache_absorb_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = wl.make_workload(name)
+    B = w.q.shape[0]
+    done, rows, t0 = 0, 0, time.perf_counter()
+    while done < B and time.perf_counter() - t0 < budget_s:
+        oracle.mla_reference(w.q, w.cache, w.w_k, w.w_v, w.cache_len, w.scale, idx=w.idx, idx_len=w.idx_len,
+                             batches=[done])
+        rows += int(w.cache_len[done]) if w.idx is None else int(w.idx_len[done].sum())
+        done += 1
+    dt = time.perf_counter() - t0
+    gbs = rows * w.cache.shape[2] * 2 / dt / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {B} sequences of {name} (all {w.q.shape[2]} heads, expanded fp64), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_b32_l8192")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_latent_cache_absorb_amd import binding, build as libbuild
+    if not os.path.exists(binding.LIB_PATH):
+        libbuild.build()
+    binding.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    r = time_path(args.workload, args.steps, args.warmup, NSETS)
+    w = r["workload"]
+    B, Q, H, D = w.q.shape
+    R = w.cache.shape[2]
+    latent_bytes = visible_rows(w) * R * 2
+    gbs = latent_bytes / (r["ms_step"] * 1e-3) / 1e9
+    attn_ms = r["stage_ms"]["latent_attn"]
+    achieved = latent_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.workload)
+    result = {
+        "metric": "absorbed-MLA attn: latent-cache GB/s (q_len=1) + TFLOP/s (q_len=6) vs roofline",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "q_len": Q, "cache_len": int(w.cache.shape[1]),
+                   "heads": H, "head_dim": D, "latent": R, "softmax_scale": w.scale, "splits": r["splits"],
+                   "input_sets_rotated": NSETS, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "mla_latent_attn (split kernel + merge)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic / (attn_ms * 1e-3) / 1e9, 2),
+                     "algorithmic_bytes_per_launch": latent_bytes, "avg_launch_ms": round(attn_ms, 6)},
+        "stages_ms": {k: round(v, 6) for k, v in r["stage_ms"].items()},
+        "tokens_per_s": round(B * Q / (r["ms_step"] * 1e-3), 1),
+    }
+    if not args.no_secondary:
+        torch.cuda.empty_cache()
+        s = time_path("verify_b16_q6_l32768", max(5, args.steps // 5), 3, 1)
+        ws2 = s["workload"]
+        flops = 4 * ws2.q.shape[2] * ws2.cache.shape[2] * attended_positions(ws2)
+        t_attn = s["stage_ms"]["latent_attn"] * 1e-3
+        tf = flops / t_attn / 1e12
+        result["secondary"] = {
+            "workload": "verify_b16_q6_l32768", "metric": "latent attention TFLOP/s (q_len=6)",
+            "value": round(tf, 2), "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS, "bound": "mfma",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "attn_flops": flops,
+            "ms_per_step": round(s["ms_step"], 6), "stages_ms": {k: round(v, 6) for k, v in s["stage_ms"].items()},
+            "splits": s["splits"]}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

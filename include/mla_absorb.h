@@ -1,0 +1,163 @@
+/*
+ * mla_absorb.h -- C ABI of libmla_absorb.so: absorbed Multi-head Latent Attention over a
+ * 512-wide bf16 latent KV cache, hand-written HIP kernels for AMD MI355X (gfx950).
+ *
+ * The operation (page "Module 05 -- MLA: Compressing Per-Token History", sections 1-4;
+ * colibri "GLM-5.3-Flash engine", section "MLA is absorbed"):
+ *   each cached token j is one latent c_j (width R = 512); head h rebuilds
+ *   k_{j,h} = U_h^K c_j and v_{j,h} = U_h^V c_j (U = D x R, D = 256).  Attention never
+ *   rebuilds them.  The three calls below are the three steps of the absorbed form:
+ *     1. mla_absorb_q     q~_h = (U_h^K)^T q_h, once per query and head;
+ *     2. mla_latent_attn  s_j = scale * q~_h . c_j over the visible positions, softmax,
+ *                         and the weighted sum kept in latent space, o_lat,h = sum_j a_j c_j;
+ *        mla_latent_attn_indexed: the same over an explicit list of positions per query
+ *                         (the consumer of a sparse selection such as DSA k-pooling, colibri
+ *                         "DSA with k-pooling");
+ *     3. mla_up_v         out_h = U_h^V o_lat,h, the one expansion at the end.
+ *   Composed, they equal ordinary softmax attention on the expanded keys and values
+ *   (an identity, not an approximation); the scores equal the expanded scores, with the
+ *   same scale.
+ *
+ * Conventions shared by every call
+ *   - All tensor arguments are DEVICE pointers owned by the caller (the library never
+ *     allocates, frees or keeps them), row-major and contiguous unless a stride is given,
+ *     16-byte aligned.  bf16 values are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work
+ *     on it: it never synchronises, never allocates and keeps no state between calls, so
+ *     calls on different streams may run concurrently.
+ *   - Supported shapes: R == 512, D == 256, H a positive multiple of 64 (the checkpoint
+ *     has H = 64).  Other shapes return MLA_ERR_SHAPE.
+ *   - On any error the call returns a negative status BEFORE enqueuing anything, so no
+ *     output is written.  MLA_ERR_HIP means a launch failed after validation.
+ *   - The current HIP device must be a gfx950 GPU (MLA_ERR_DEVICE otherwise).
+ *
+ * Query positions (page "Module 08 -- Vision, MTP, and Hybrid Serving State", section 2:
+ * the full model verifies the drafted tokens in one forward pass; page "Module 05",
+ * section 4: a query sees only j <= t):
+ *   a pass over Q new positions of sequence b appends their latents to the cache first;
+ *   query i (0 <= i < Q) then sits at position t = cache_len[b] - Q + i and, in the dense
+ *   call, sees every position j <= t.  Q = 1 is single-token decode; Q = 1 + k verifies k
+ *   drafted tokens.  Rolling back rejected drafts is a smaller cache_len (the latent cache
+ *   is truncatable by position, page "Module 08", section 3).
+ */
+#ifndef MLA_ABSORB_H
+#define MLA_ABSORB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,      /* a required pointer is NULL */
+  MLA_ERR_SHAPE = -2,     /* unsupported H, D or R, or a non-positive size */
+  MLA_ERR_ARG = -3,       /* another argument out of range (stride, num_splits, K_max, scale) */
+  MLA_ERR_WORKSPACE = -4, /* workspace smaller than mla_latent_attn_workspace_size() */
+  MLA_ERR_HIP = -5,       /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_DEVICE = -6     /* the current device is not a gfx950 GPU */
+};
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* mla_status_string(int status);
+
+/*
+ * Query absorption (page "Module 05", section 3: q~_h = (U_h^K)^T q_h, computed once per
+ * query and head, independent of the cached token it is scored against).
+ *   q      [rows][H][D] bf16   the queries (rows = batch * q_len)
+ *   w_k    [H][D][R]    bf16   U_h^K for every head, as stored in the checkpoint (D x R per head)
+ *   q_abs  [rows][H][R] bf16   output: prescale * (U_h^K)^T q_h, accumulated in fp32 and
+ *                              rounded to nearest-even bf16
+ *   prescale                   1.0f, or a power of two such as the softmax scale 1/16 (then
+ *                              pass scale = 1 to the attention call); must be finite
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (rows < 1 or unsupported dims), MLA_ERR_ARG
+ * (non-finite prescale), MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int32_t rows, int32_t H,
+                 int32_t D, int32_t R, float prescale, void* stream);
+
+/*
+ * Number of position splits a latent-attention call will use (split-K over the positions,
+ * each split a partial softmax merged by log-sum-exp).
+ *   max_positions  dense: the max_cache_len bound; indexed: K_max
+ *   num_splits     0 = choose automatically for the current device; otherwise the request,
+ *                  clamped to [1, 1024] and to the number of 32-position tiles, then lowered
+ *                  so that no split is empty once the positions are cut into equal runs of
+ *                  whole tiles (e.g. 8 tiles asked for 5 splits use 4 splits of 2 tiles)
+ * Returns the split count (>= 1), or a negative status for bad sizes.
+ */
+int32_t mla_latent_attn_num_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions,
+                                   int32_t num_splits);
+
+/*
+ * Workspace bytes a latent-attention call needs (0 when it uses one split): the split
+ * partials, [splits][B*Q][H][R] fp32 plus two [splits][B*Q][H] fp32 arrays.  Same
+ * arguments as mla_latent_attn_num_splits plus R.  Returns 0 on bad sizes as well; the
+ * attention calls reject a workspace that is too small.
+ */
+size_t mla_latent_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R,
+                                      int32_t max_positions, int32_t num_splits);
+
+/*
+ * Dense latent attention (page "Module 05", section 3: scores read the cached latent
+ * directly through the absorbed query; the value sum accumulates in latent space and is
+ * expanded later; the scale is that of the original q.k).
+ *   q_abs      [B][Q][H][R] bf16   absorbed queries (mla_absorb_q)
+ *   cache      bf16 latent rows: row j of sequence b starts at cache + b*cache_batch_stride
+ *              + j*R; cache_batch_stride (elements) >= max_cache_len * R
+ *   cache_len  [B] int32 (device)  positions held by each sequence, including the Q new ones
+ *   max_cache_len                  host-side bound on every cache_len[b] (>= Q)
+ *   scale                          softmax scale on q.k (1/16 for 256-wide heads); finite, > 0
+ *   num_splits                     0 = auto (see mla_latent_attn_num_splits)
+ *   o_lat      [B][Q][H][R] fp32   output: sum_j a_j c_j, a = softmax_j(scale * q~ . c_j)
+ *   lse        [B][Q][H] fp32      output (may be NULL): ln sum_j exp(scale * q~ . c_j)
+ *   workspace, workspace_bytes     caller-owned device scratch of at least
+ *                                  mla_latent_attn_workspace_size() bytes (may be NULL if 0)
+ * Device-side preconditions (not checked on the host): Q <= cache_len[b] <= max_cache_len.
+ * Cache rows at or past min(cache_len[b], max_cache_len) are never read.  A query whose
+ * visible set is empty (cache_len[b] < Q) gets o_lat = NaN and lse = -inf.
+ * Results are deterministic for a fixed num_splits (no atomics in any reduction).
+ */
+int mla_latent_attn(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
+                    const int32_t* cache_len, int32_t B, int32_t Q, int32_t H, int32_t R,
+                    int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Indexed latent attention: as mla_latent_attn, but query i of sequence b attends exactly
+ * to the positions idx[b][i][0 .. idx_len[b][i]-1] (the rows a sparse selector such as DSA
+ * k-pooling picked, plus the causal tail of the pass; colibri "DSA with k-pooling").
+ *   idx      [B][Q][K_max] int32 (device)  positions, sorted ascending, unique, causal
+ *   idx_len  [B][Q] int32 (device)         entries used per query, 1 <= idx_len <= K_max
+ *   K_max                                  slots per query in idx (>= 1)
+ * Index slots at or past idx_len are never read.  A position outside
+ * [0, min(cache_len[b], max_cache_len)) is skipped without being read (memory safety; the
+ * result for such input is not the attention over the listed positions).  A query with no
+ * usable position gets o_lat = NaN and lse = -inf.  Workspace: pass K_max as max_positions
+ * to mla_latent_attn_workspace_size.
+ */
+int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
+                            const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len,
+                            int32_t K_max, int32_t B, int32_t Q, int32_t H, int32_t R,
+                            int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Value up-projection (page "Module 05", section 3: U_h^V factors out of the sum over
+ * history, so the accumulated latent is expanded once, at the end).
+ *   o_lat  [rows][H][R] fp32   accumulated latents (mla_latent_attn)
+ *   w_v    [H][D][R]    bf16   U_h^V for every head, as stored in the checkpoint
+ *   out    [rows][H][D] fp32   output: U_h^V o_lat,h (o_lat is split into two bf16 terms
+ *                              before the bf16 matrix multiply, so it keeps ~16 mantissa bits)
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, int32_t H, int32_t D,
+             int32_t R, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_ABSORB_H */

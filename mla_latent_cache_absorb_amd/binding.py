@@ -1,0 +1,211 @@
+"""Python binding of libmla_absorb.so: the C ABI of include/mla_absorb.h with the same names.
+
+Argument marshalling only: tensors are torch tensors on the current HIP device (PyTorch is
+used for device memory and streams); every step of the computation runs in the library's
+HIP kernels.  There is no fallback: if the library is missing, `lib()` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
+
+# status codes (enum mla_status)
+MLA_OK = 0
+MLA_ERR_NULL = -1
+MLA_ERR_SHAPE = -2
+MLA_ERR_ARG = -3
+MLA_ERR_WORKSPACE = -4
+MLA_ERR_HIP = -5
+MLA_ERR_DEVICE = -6
+
+EXPORTS = ("mla_status_string", "mla_absorb_q", "mla_latent_attn_num_splits", "mla_latent_attn_workspace_size",
+           "mla_latent_attn", "mla_latent_attn_indexed", "mla_up_v")
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mla_latent_cache_absorb_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        L.mla_status_string.argtypes = [ctypes.c_int]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_absorb_q.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, vp]
+        L.mla_absorb_q.restype = ctypes.c_int
+        L.mla_latent_attn_num_splits.argtypes = [i32, i32, i32, i32, i32]
+        L.mla_latent_attn_num_splits.restype = i32
+        L.mla_latent_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.mla_latent_attn_workspace_size.restype = sz
+        L.mla_latent_attn.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+        L.mla_latent_attn.restype = ctypes.c_int
+        L.mla_latent_attn_indexed.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+                                              vp, vp, sz, vp]
+        L.mla_latent_attn_indexed.restype = ctypes.c_int
+        L.mla_up_v.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+        L.mla_up_v.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != MLA_OK:
+        raise MlaError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str, contiguous: bool = True):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype} tensor on the GPU")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ----------------------------------------------------------------------------------------
+def mla_absorb_q(q: torch.Tensor, w_k: torch.Tensor, q_abs: Optional[torch.Tensor] = None,
+                 prescale: float = 1.0, stream=None) -> torch.Tensor:
+    """q [..., H, D] bf16, w_k [H, D, R] bf16 -> q_abs [..., H, R] bf16 = prescale * W_k^T q."""
+    _need(q, torch.bfloat16, "q")
+    _need(w_k, torch.bfloat16, "w_k")
+    H, D, R = w_k.shape
+    rows = q.numel() // (H * D)
+    if q.shape[-2:] != (H, D):
+        raise ValueError("q must end in [H, D]")
+    if q_abs is None:
+        q_abs = torch.empty(q.shape[:-1] + (R,), dtype=torch.bfloat16, device=q.device)
+    _need(q_abs, torch.bfloat16, "q_abs")
+    _check(lib().mla_absorb_q(_ptr(q), _ptr(w_k), _ptr(q_abs), rows, H, D, R, float(prescale), _stream(stream)),
+           "mla_absorb_q")
+    return q_abs
+
+
+def mla_latent_attn_num_splits(B: int, Q: int, H: int, max_positions: int, num_splits: int = 0) -> int:
+    s = lib().mla_latent_attn_num_splits(B, Q, H, max_positions, num_splits)
+    _check(min(int(s), 0), "mla_latent_attn_num_splits")
+    return int(s)
+
+
+def mla_latent_attn_workspace_size(B: int, Q: int, H: int, R: int, max_positions: int, num_splits: int = 0) -> int:
+    return int(lib().mla_latent_attn_workspace_size(B, Q, H, R, max_positions, num_splits))
+
+
+def _cache_stride(cache: torch.Tensor) -> int:
+    if cache.dim() != 3 or cache.stride(2) != 1 or cache.stride(1) != cache.shape[2]:
+        raise ValueError("cache must be [B, L, R] with contiguous rows")
+    return int(cache.stride(0))
+
+
+def _attn_outputs(q_abs, o_lat, lse, want_lse):
+    B, Q, H, R = q_abs.shape
+    if o_lat is None:
+        o_lat = torch.empty((B, Q, H, R), dtype=torch.float32, device=q_abs.device)
+    _need(o_lat, torch.float32, "o_lat")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=q_abs.device)
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    return o_lat, lse
+
+
+def _workspace(workspace, need, device):
+    if need == 0:
+        return workspace
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def mla_latent_attn(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int,
+                    scale: float, num_splits: int = 0, o_lat=None, lse=None, workspace=None, want_lse=True,
+                    stream=None):
+    """Dense latent attention.  q_abs [B, Q, H, R] bf16; cache [B, L_max, R] bf16 (a view with any
+    batch stride); cache_len [B] int32 on the GPU.  Returns (o_lat [B, Q, H, R] fp32, lse [B, Q, H])."""
+    _need(q_abs, torch.bfloat16, "q_abs")
+    _need(cache, torch.bfloat16, "cache", contiguous=False)
+    _need(cache_len, torch.int32, "cache_len")
+    B, Q, H, R = q_abs.shape
+    o_lat, lse = _attn_outputs(q_abs, o_lat, lse, want_lse)
+    need = mla_latent_attn_workspace_size(B, Q, H, R, max_cache_len, num_splits)
+    workspace = _workspace(workspace, need, q_abs.device)
+    _check(lib().mla_latent_attn(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), B, Q, H, R,
+                                 int(max_cache_len), float(scale), int(num_splits), _ptr(o_lat), _ptr(lse),
+                                 _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)),
+           "mla_latent_attn")
+    return o_lat, lse
+
+
+def mla_latent_attn_indexed(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor, idx: torch.Tensor,
+                            idx_len: torch.Tensor, max_cache_len: int, scale: float, num_splits: int = 0,
+                            o_lat=None, lse=None, workspace=None, want_lse=True, stream=None):
+    """Indexed latent attention: idx [B, Q, K_max] int32 (sorted positions), idx_len [B, Q] int32."""
+    _need(q_abs, torch.bfloat16, "q_abs")
+    _need(cache, torch.bfloat16, "cache", contiguous=False)
+    _need(cache_len, torch.int32, "cache_len")
+    _need(idx, torch.int32, "idx")
+    _need(idx_len, torch.int32, "idx_len")
+    B, Q, H, R = q_abs.shape
+    K_max = idx.shape[-1]
+    o_lat, lse = _attn_outputs(q_abs, o_lat, lse, want_lse)
+    need = mla_latent_attn_workspace_size(B, Q, H, R, K_max, num_splits)
+    workspace = _workspace(workspace, need, q_abs.device)
+    _check(lib().mla_latent_attn_indexed(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
+                                         _ptr(idx_len), K_max, B, Q, H, R, int(max_cache_len), float(scale),
+                                         int(num_splits), _ptr(o_lat), _ptr(lse), _ptr(workspace),
+                                         0 if workspace is None else workspace.numel(), _stream(stream)),
+           "mla_latent_attn_indexed")
+    return o_lat, lse
+
+
+def mla_up_v(o_lat: torch.Tensor, w_v: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """o_lat [..., H, R] fp32, w_v [H, D, R] bf16 -> out [..., H, D] fp32 = W_v o_lat."""
+    _need(o_lat, torch.float32, "o_lat")
+    _need(w_v, torch.bfloat16, "w_v")
+    H, D, R = w_v.shape
+    if o_lat.shape[-2:] != (H, R):
+        raise ValueError("o_lat must end in [H, R]")
+    rows = o_lat.numel() // (H * R)
+    if out is None:
+        out = torch.empty(o_lat.shape[:-1] + (D,), dtype=torch.float32, device=o_lat.device)
+    _need(out, torch.float32, "out")
+    _check(lib().mla_up_v(_ptr(o_lat), _ptr(w_v), _ptr(out), rows, H, D, R, _stream(stream)), "mla_up_v")
+    return out
+
+
+def mla_forward(q, w_k, w_v, cache, cache_len, max_cache_len, scale, idx=None, idx_len=None, num_splits=0,
+                stream=None):
+    """The whole absorbed path: absorb_q -> latent attention (dense or indexed) -> up_v.
+    Returns (out [B, Q, H, D] fp32, lse [B, Q, H] fp32)."""
+    q_abs = mla_absorb_q(q, w_k, stream=stream)
+    if idx is None:
+        o_lat, lse = mla_latent_attn(q_abs, cache, cache_len, max_cache_len, scale, num_splits, stream=stream)
+    else:
+        o_lat, lse = mla_latent_attn_indexed(q_abs, cache, cache_len, idx, idx_len, max_cache_len, scale,
+                                             num_splits, stream=stream)
+    return mla_up_v(o_lat, w_v, stream=stream), lse

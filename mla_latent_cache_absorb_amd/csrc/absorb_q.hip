@@ -1,0 +1,106 @@
+// Query absorption for gfx950: q~_h = prescale * (U_h^K)^T q_h (page "Module 05 -- MLA:
+// Compressing Per-Token History", section 3: the pre-transformed query is computed once per
+// query and head, independently of the cached token it is later scored against).
+//
+// Per head this is a small GEMM, Q~^T[R x rows] = (U_h^K)^T[R x D] . Q_h^T[D x rows], bound by
+// reading U^K (16 MiB for 64 heads).  U^K is stored as in the checkpoint, [D][R] per head, so
+// its transpose is the A operand: a [256 d x 128 r] slab of it is staged in LDS (64 KiB,
+// 16-byte chunks swizzled per row) and read with the LDS transpose read.  The queries are the
+// B operand, 16-byte loads straight from memory.  Accumulation is fp32, the result is rounded
+// to nearest-even bf16.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kRBlock = 128;                 // latents per workgroup
+constexpr int kSlabRowBytes = kRBlock * 2;   // 256 B per d-row of the slab
+constexpr int kThreads = 128;
+
+__global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ w_k,
+                                                            uint16_t* __restrict__ q_abs, int rows,
+                                                            int H, float prescale) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slab[kHeadDim * kSlabRowBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nrb = kLatent / kRBlock;
+  const int h = blockIdx.x / nrb;
+  const int r0 = (blockIdx.x % nrb) * kRBlock;
+
+  // stage U_h^K[0:256][r0:r0+128]: one instruction moves 4 d-rows (lane s: row 4k + s/16,
+  // chunk slot s%16 holds global chunk (s%16) ^ swz(row))
+  {
+    const uint8_t* wsrc = (const uint8_t*)(w_k + ((size_t)h * kHeadDim) * kLatent + r0);
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+      const int inst = wave * 32 + k;
+      const int row = 4 * inst + (lane >> 4);
+      const int slot = lane & 15;
+      const uint8_t* src = wsrc + (size_t)row * kRowBytes + ((slot ^ swz(row)) << 4);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slab + inst * 1024), 16, 0, 0);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const int hl = lane & 31, hf = lane >> 5;
+  // transpose-read addressing: group g = lane/16 supplies d-rows 16ks + 8(g/2) + 4r2 + e and
+  // latent columns 32mb + 16(g&1) + 4c of the slab
+  const int g = lane >> 4, ip = lane & 15, te = ip >> 2, tc = ip & 3;
+  const int nblocks = (rows + 31) / 32;
+  for (int nb = 0; nb < nblocks; ++nb) {
+    const int row = nb * 32 + hl;
+    const bool rvalid = row < rows;
+    bf16x8 bq[16];
+    const uint16_t* qsrc = q + ((size_t)(rvalid ? row : 0) * H + h) * kHeadDim + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      bf16x8 v = *(const bf16x8*)(qsrc + 16 * ks);
+      if (!rvalid) v = (bf16x8)(s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      bq[ks] = v;
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int mb = 2 * wave + m;
+      f32x16 acc;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc[k] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        s16x4 part[2];
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+          const int d = 16 * ks + 8 * (g >> 1) + 4 * r2 + te;
+          const int chunk = 4 * mb + 2 * (g & 1) + (tc >> 1);
+          part[r2] = lds_read_tr16(slab + d * kSlabRowBytes + ((chunk ^ swz(d)) << 4) + ((tc & 1) << 3));
+        }
+        acc = mfma32(concat_bf16(part[0], part[1]), bq[ks], acc);
+      }
+      if (rvalid) {
+        // lane holds query row `row`, latents r0 + 32mb + 8ii + 4hf + j
+        uint16_t* dst = q_abs + ((size_t)row * H + h) * kLatent + r0 + 32 * mb + 4 * hf;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          s16x4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = (short)f32_to_bf16_bits(acc[4 * ii + j] * prescale);
+          *(s16x4*)(dst + 8 * ii) = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int rows, int H,
+                           float prescale, hipStream_t stream) {
+  void* args[] = {(void*)&q, (void*)&w_k, (void*)&q_abs, (void*)&rows, (void*)&H, (void*)&prescale};
+  const dim3 grid(H * (kLatent / kRBlock)), block(kThreads);
+  return hipLaunchKernel((const void*)&absorb_q_kernel, grid, block, args, 0, stream);
+}
+
+}  // namespace mla

@@ -1,0 +1,219 @@
+// C ABI of libmla_absorb (declared in include/mla_absorb.h): argument validation, device
+// checks, split sizing and kernel launches.  Every call validates on the host first and
+// enqueues nothing on error; it never allocates, synchronises or keeps per-call state.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "mla_absorb.h"
+#include "mla_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// per device: 0 = unknown, 1 = gfx950, -1 = other; compute-unit count
+std::atomic<int> g_dev_ok[kMaxDevices];
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+int check_device(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+  int ok = g_dev_ok[dev].load(std::memory_order_acquire);
+  if (ok == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_HIP;
+    ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_dev_ok[dev].store(ok, std::memory_order_release);
+  }
+  if (ok != 1) return MLA_ERR_DEVICE;
+  if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return MLA_OK;
+}
+
+// The split count: independent work units are (sequence, query, 64-head group); the
+// positions of each are cut into `s` contiguous splits of whole tiles.  The estimate charges
+// the rounds of resident workgroups (two per CU) times the tiles of one split, plus the
+// partial results each extra split writes and the merge reads back (a 128 KiB partial is
+// worth four 32 KiB tiles each way) and a fixed cost for the merge launch.
+int32_t choose_splits(int64_t units, int32_t max_positions, int cus) {
+  const int64_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
+  const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+  const int64_t smax = tiles < mla::kMaxSplits ? tiles : mla::kMaxSplits;
+  int32_t best = 1;
+  double best_cost = 1e300;
+  for (int64_t s = 1; s <= smax; ++s) {
+    const int64_t per = (tiles + s - 1) / s;
+    if ((s - 1) * per >= tiles) continue;  // would leave an empty split
+    const int64_t rounds = (units * s + slots - 1) / slots;
+    double cost = (double)rounds * (double)per;
+    if (s > 1) cost += (double)(units * s * 8) / (double)slots + 3.0;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = (int32_t)s;
+    }
+  }
+  return best;
+}
+
+// positions per split (whole tiles) for a split count
+int32_t split_length(int32_t max_positions, int32_t s) {
+  const int32_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
+  const int32_t per = (tiles + s - 1) / s;
+  return per * mla::kTilePositions;
+}
+
+bool supported(int32_t H, int32_t D, int32_t R) { return R == 512 && D == 256 && H > 0 && H % 64 == 0; }
+
+int resolve_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions, int32_t num_splits, int cus) {
+  if (B < 1 || Q < 1 || H < 64 || H % 64 != 0 || max_positions < 1) return MLA_ERR_SHAPE;
+  if (num_splits < 0) return MLA_ERR_ARG;
+  const int32_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
+  int32_t s;
+  if (num_splits == 0) {
+    s = choose_splits((int64_t)B * Q * (H / 64), max_positions, cus);
+  } else {
+    s = num_splits > mla::kMaxSplits ? mla::kMaxSplits : num_splits;
+    if (s > tiles) s = tiles;
+  }
+  // drop splits that would be empty once the positions are cut into whole tiles
+  const int32_t len = split_length(max_positions, s);
+  return (max_positions + len - 1) / len;
+}
+
+size_t workspace_bytes_for(int32_t B, int32_t Q, int32_t H, int32_t s) {
+  if (s <= 1) return 0;
+  const size_t rows = (size_t)s * B * Q * H;
+  return rows * 512 * sizeof(float) + rows * 2 * sizeof(float);
+}
+
+int device_cus_or_default() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+    if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      g_dev_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus > 0 ? cus : 256;
+}
+
+int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride, const int32_t* cache_len,
+                const int32_t* idx, const int32_t* idx_len, int32_t K_max, bool indexed, int32_t B, int32_t Q,
+                int32_t H, int32_t R, int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat,
+                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_abs || !cache || !cache_len || !o_lat) return MLA_ERR_NULL;
+  if (indexed && (!idx || !idx_len)) return MLA_ERR_NULL;
+  if (!supported(H, 256, R) || B < 1 || Q < 1 || max_cache_len < 1) return MLA_ERR_SHAPE;
+  if (max_cache_len < Q) return MLA_ERR_ARG;
+  if (cache_batch_stride < (int64_t)max_cache_len * R) return MLA_ERR_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return MLA_ERR_ARG;
+  if (indexed && K_max < 1) return MLA_ERR_ARG;
+  if (num_splits < 0) return MLA_ERR_ARG;
+  int cus = 0;
+  const int dst = check_device(&cus);
+  if (dst != MLA_OK) return dst;
+  const int32_t max_positions = indexed ? K_max : max_cache_len;
+  const int s = resolve_splits(B, Q, H, max_positions, num_splits, cus);
+  if (s < 1) return s;
+  const size_t need = workspace_bytes_for(B, Q, H, s);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  const int64_t total = (int64_t)B * Q * (H / 64) * s;
+  if (total > 0x7fffffff || (int64_t)B * Q * H > 0x7fffffff) return MLA_ERR_SHAPE;
+
+  mla::AttnArgs a;
+  a.q_abs = q_abs;
+  a.cache = (const uint8_t*)cache;
+  a.cache_bstride_bytes = cache_batch_stride * 2;
+  a.cache_len = cache_len;
+  a.idx = idx;
+  a.idx_len = idx_len;
+  a.K_max = indexed ? K_max : 0;
+  a.B = B;
+  a.Q = Q;
+  a.H = H;
+  a.HG = H / 64;
+  a.max_cache_len = max_cache_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_splits = s;
+  a.split_len = split_length(max_positions, s);
+  a.total_wg = (int32_t)total;
+  a.o_lat = o_lat;
+  a.lse = lse;
+  const size_t rows = (size_t)s * B * Q * H;
+  a.part_o = s > 1 ? (float*)workspace : nullptr;
+  a.part_ml = s > 1 ? (float*)workspace + rows * 512 : nullptr;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (mla::launch_latent_attn(a, indexed, st) != hipSuccess) return MLA_ERR_HIP;
+  if (s > 1 && mla::launch_combine(a, st) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "unsupported shape (need R == 512, D == 256, H a positive multiple of 64, sizes >= 1)";
+    case MLA_ERR_ARG: return "argument out of range";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    case MLA_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    default: return "unknown status";
+  }
+}
+
+int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int32_t rows, int32_t H, int32_t D,
+                 int32_t R, float prescale, void* stream) {
+  if (!q || !w_k || !q_abs) return MLA_ERR_NULL;
+  if (!supported(H, D, R) || rows < 1 || (int64_t)rows * H > 0x7fffffff) return MLA_ERR_SHAPE;
+  if (!isfinite(prescale)) return MLA_ERR_ARG;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  if (mla::launch_absorb_q(q, w_k, q_abs, rows, H, prescale, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int32_t mla_latent_attn_num_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions, int32_t num_splits) {
+  return resolve_splits(B, Q, H, max_positions, num_splits, device_cus_or_default());
+}
+
+size_t mla_latent_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_positions,
+                                      int32_t num_splits) {
+  if (R != 512) return 0;
+  const int s = resolve_splits(B, Q, H, max_positions, num_splits, device_cus_or_default());
+  if (s < 1) return 0;
+  return workspace_bytes_for(B, Q, H, s);
+}
+
+int mla_latent_attn(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride, const int32_t* cache_len,
+                    int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len, float scale, int32_t num_splits,
+                    float* o_lat, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_common(q_abs, cache, cache_batch_stride, cache_len, nullptr, nullptr, 0, false, B, Q, H, R,
+                     max_cache_len, scale, num_splits, o_lat, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
+                            const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t K_max,
+                            int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len, float scale,
+                            int32_t num_splits, float* o_lat, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return attn_common(q_abs, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, true, B, Q, H, R,
+                     max_cache_len, scale, num_splits, o_lat, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, int32_t H, int32_t D, int32_t R,
+             void* stream) {
+  if (!o_lat || !w_v || !out) return MLA_ERR_NULL;
+  if (!supported(H, D, R) || rows < 1 || (int64_t)rows * H > 0x7fffffff) return MLA_ERR_SHAPE;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  if (mla::launch_up_v(o_lat, w_v, out, rows, H, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+}  // extern "C"

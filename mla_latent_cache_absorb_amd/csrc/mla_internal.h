@@ -1,0 +1,38 @@
+// Host-side launch interface between the C ABI (mla_api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kTilePositions = 32;    // latent rows per LDS tile
+constexpr int kMaxSplits = 1024;
+
+struct AttnArgs {
+  const uint16_t* q_abs;          // [B][Q][H][R] bf16
+  const uint8_t* cache;           // latent rows (bytes)
+  int64_t cache_bstride_bytes;    // bytes between sequences
+  const int32_t* cache_len;       // [B]
+  const int32_t* idx;             // [B][Q][K_max] (indexed only)
+  const int32_t* idx_len;         // [B][Q]        (indexed only)
+  int32_t K_max;
+  int32_t B, Q, H, HG;            // HG = H / 64 head groups
+  int32_t max_cache_len;
+  float scale_log2;               // softmax scale * log2(e)
+  int32_t num_splits, split_len;  // split_len: positions (or index slots) per split, multiple of the tile
+  int32_t total_wg;
+  float* o_lat;                   // [B][Q][H][R] fp32 (written directly when num_splits == 1)
+  float* lse;                     // [B][Q][H] or null
+  float* part_o;                  // [S][B*Q][H][R] fp32 unnormalised partial sums
+  float* part_ml;                 // [S][B*Q][H][2] fp32 (running max in log2 units, sum)
+};
+
+hipError_t launch_latent_attn(const AttnArgs& a, bool indexed, hipStream_t stream);
+hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int rows, int H,
+                           float prescale, hipStream_t stream);
+hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H,
+                       hipStream_t stream);
+
+}  // namespace mla

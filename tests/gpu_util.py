@@ -1,0 +1,63 @@
+"""Helpers for the GPU tests: move workload arrays to the device and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def bf16(a: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bits -> bf16 tensor on the GPU (same bits)."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def i32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> uint16 bits on the host."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def tol(ref: np.ndarray) -> float:
+    """The parity bar on fp32 outputs: max|gpu - ref| <= 1e-2 * max|ref| + 1e-3."""
+    return 1e-2 * float(np.abs(ref).max()) + 1e-3
+
+
+def assert_parity(got, ref, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = float(np.abs(got - ref).max())
+    bar = tol(ref)
+    print(f"{what}: max|err| = {err:.3e}, bar {bar:.3e}, max|ref| = {float(np.abs(ref).max()):.3e}", flush=True)
+    assert err <= bar, f"{what}: max|err| {err:.3e} > {bar:.3e}"
+    return err
+
+
+def lse_bound(w, batches, queries, heads):
+    """Largest lse error the whole path can show, from its arithmetic: the absorbed query is
+    rounded to bf16 (relative error <= 2^-8 per element), which moves every score by at most
+    scale * 2^-8 * sum_r |q~_r c_jr|; lse moves by at most the largest score change.  Plus 1e-3
+    for fp32 exponentials, logarithms and sums.  Returns [nb, nq, nh]."""
+    import oracle
+    qt = np.abs(oracle.absorbed_query(w.q[np.ix_(batches)], w.w_k))  # [nb, Q, H, R]
+    out = np.zeros((len(batches), len(queries), len(heads)))
+    for ib, b in enumerate(batches):
+        L = int(w.cache_len[b])
+        for iq, i in enumerate(queries):
+            if w.idx is None:
+                pos = np.arange(L - w.q.shape[1] + i + 1)
+            else:
+                pos = w.idx[b, i, : w.idx_len[b, i]]
+            c = np.abs(oracle.bf16_bits_to_f64(w.cache[b, pos]))
+            m = c @ qt[ib, i][list(heads)].T                      # [T, nh]
+            out[ib, iq] = w.scale * 2.0 ** -8 * m.max(axis=0) + 1e-3
+    return out

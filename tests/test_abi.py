@@ -1,0 +1,86 @@
+"""The C ABI: the library builds, loads, exports every entry point include/mla_absorb.h
+declares, and its host-side validation answers without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_cache_absorb_amd import binding, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return binding.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mla_absorb.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert "mla_latent_attn" in names and "mla_latent_attn_indexed" in names
+    assert set(names) == set(binding.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), f"missing export {n}"
+    # exported with C linkage (no mangling)
+    out = os.popen(f"nm -D --defined-only {binding.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert binding.status_string(s)
+    assert "workspace" in binding.status_string(binding.MLA_ERR_WORKSPACE)
+
+
+def test_host_validation_without_device(L):
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)
+    # null pointers and shapes are rejected before any device call
+    assert L.mla_absorb_q(None, fake, fake, 1, 64, 256, 512, 1.0, None) == binding.MLA_ERR_NULL
+    assert L.mla_absorb_q(fake, fake, fake, 1, 64, 128, 512, 1.0, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_absorb_q(fake, fake, fake, 1, 48, 256, 512, 1.0, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_absorb_q(fake, fake, fake, 0, 64, 256, 512, 1.0, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_absorb_q(fake, fake, fake, 1, 64, 256, 512, float("nan"), None) == binding.MLA_ERR_ARG
+    assert L.mla_up_v(fake, None, fake, 1, 64, 256, 512, None) == binding.MLA_ERR_NULL
+    assert L.mla_up_v(fake, fake, fake, 1, 64, 256, 256, None) == binding.MLA_ERR_SHAPE
+    a = dict(q=fake, c=fake, st=512 * 100, cl=fake)
+    assert L.mla_latent_attn(fake, fake, 51200, None, 1, 1, 64, 512, 100, 0.0625, 0, fake, None, None, 0, None) \
+        == binding.MLA_ERR_NULL
+    assert L.mla_latent_attn(fake, fake, 51200, fake, 1, 1, 64, 512, 100, 0.0625, -1, fake, None, None, 0, None) \
+        == binding.MLA_ERR_ARG
+    # batch stride shorter than max_cache_len rows
+    assert L.mla_latent_attn(fake, fake, 512 * 99, fake, 1, 1, 64, 512, 100, 0.0625, 0, fake, None, None, 0, None) \
+        == binding.MLA_ERR_ARG
+    assert L.mla_latent_attn(fake, fake, 51200, fake, 1, 1, 64, 512, 100, -1.0, 0, fake, None, None, 0, None) \
+        == binding.MLA_ERR_ARG
+    assert L.mla_latent_attn(fake, fake, 51200, fake, 1, 4, 64, 512, 3, 0.0625, 0, fake, None, None, 0, None) \
+        == binding.MLA_ERR_ARG
+    assert L.mla_latent_attn_indexed(fake, fake, 51200, fake, None, fake, 8, 1, 1, 64, 512, 100, 0.0625, 0, fake,
+                                     None, None, 0, None) == binding.MLA_ERR_NULL
+    assert L.mla_latent_attn_indexed(fake, fake, 51200, fake, fake, fake, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake,
+                                     None, None, 0, None) == binding.MLA_ERR_ARG
+
+
+def test_split_sizing(L):
+    # at least one split; never more than one per 32-position tile; workspace matches the count
+    for B, Q, Lmax in ((1, 1, 1), (1, 1, 256), (32, 1, 8192), (16, 6, 32768), (4, 1, 131072), (32, 4, 2052)):
+        s = binding.mla_latent_attn_num_splits(B, Q, 64, Lmax, 0)
+        assert 1 <= s <= max(1, (Lmax + 31) // 32)
+        ws = binding.mla_latent_attn_workspace_size(B, Q, 64, 512, Lmax, 0)
+        assert ws == (0 if s == 1 else s * B * Q * 64 * (512 + 2) * 4)
+    # splits hold whole 32-position tiles and none is left empty
+    assert binding.mla_latent_attn_num_splits(1, 1, 64, 256, 8) == 8
+    assert binding.mla_latent_attn_num_splits(1, 1, 64, 256, 5) == 4   # 8 tiles as 2+2+2+2
+    assert binding.mla_latent_attn_num_splits(1, 1, 64, 64, 5) == 2    # two tiles at most
+    assert binding.mla_latent_attn_num_splits(1, 1, 64, 100, 3) == 2   # 4 tiles as 2+2
+    assert binding.mla_latent_attn_workspace_size(1, 1, 64, 512, 256, 1) == 0
