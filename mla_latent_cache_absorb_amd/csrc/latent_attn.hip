@@ -5,7 +5,7 @@
 // One workgroup = one (sequence b, query i, group of 64 heads, split of positions); four
 // waves, wave w owning heads 32*(w&1) .. +31 of the group and latents 256*(w>>1) .. +255.
 // Per tile of 32 cached latents (32 KiB, staged in LDS straight from HBM with
-// global_load_lds_dwordx4, double-buffered):
+// global_load_lds_dwordx4 while the previous tile is computed):
 //   scores    S^T[32 pos x 32 heads] = C[32 x 512] . Q~^T[512 x 32]: each wave of a head pair
 //             contracts its own 256 latents (16 MFMA 32x32x16; A = the tile row-major via
 //             ds_read_b128, B = the absorbed query held in VGPRs); the two partial sums are
@@ -16,6 +16,8 @@
 //             A = the SAME tile read transposed (ds_read_b64_tr_b16), B = P straight from
 //             the score registers (the K order of the MFMA is permuted to match them)
 // One latent row serves all 64 heads: the cache is read once per (query, split).
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -24,15 +26,20 @@ namespace mla {
 namespace {
 
 constexpr int kTile = kTilePositions;
-constexpr int kStages = 2;
+constexpr int kStages = 2;          // one tile computed while the next is in flight
 constexpr int kThreads = 256;
+constexpr int kRowsPerWave = kTile / 4;
 constexpr float kRescaleLog2 = 8.0f;
 
+// Two workgroups share a CU (8 waves, two per SIMD, 80 KiB of LDS each): gfx950 needs two
+// waves per SIMD to approach its LDS read bandwidth, and the other workgroup's waves fill the
+// matrix core while a wave waits at a barrier or on LDS.  Per wave and tile: 16 MFMAs for the
+// partial scores, 16 for the values.
 template <bool INDEXED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void latent_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages][kTile * kRowBytes];
-  __shared__ __attribute__((aligned(16))) float xbuf[4][16][64];  // partial scores, [wave][reg][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 xbuf[4][4][64];  // partial scores [wave][reg/4][lane]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps it in SGPRs
@@ -66,6 +73,7 @@ void latent_attn_kernel(AttnArgs a) {
   const int s_end = min(s_begin + a.split_len, n_slots);
   const int ntiles = s_end > s_begin ? (s_end - s_begin + kTile - 1) / kTile : 0;
   const uint8_t* seq = a.cache + (size_t)b * a.cache_bstride_bytes;
+  const float c2 = a.scale_log2;
 
   // absorbed query of head h0+hl as the B operand: latents 256lh + 16ks + 8hf .. +7
   bf16x8 qf[16];
@@ -74,6 +82,8 @@ void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) qf[ks] = *(const bf16x8*)(qrow + 16 * ks);
   }
+  // complete these loads here: the loop's waits then count tile copies only
+  wait_vmcnt<0>();
 
   f32x16 o[8];
 #pragma unroll
@@ -81,113 +91,108 @@ void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) o[mb][k] = 0.f;
   float m_run = -INFINITY;  // running maximum of scale*log2(e)*score
-  float l_run = 0.f;        // running sum of 2^(s - m_run)
+  float l_run = 0.f;        // running sum of 2^(scale*log2(e)*score - m_run)
 
   // ---- tile loader: wave w copies tile rows 8w .. 8w+7, one 1 KiB row per instruction;
-  // lane s of row r takes global chunk s ^ swz(r) into slot s (swz(r) depends on r mod 8 only).
-  // Rows past the split are clamped to its last valid row (read, then masked out), so every
-  // read stays inside the visible rows; indexed slots that name a position outside the cache
-  // read row 0 instead and are masked.
-  uint32_t voff[8];
-#pragma unroll
-  for (int rr = 0; rr < 8; ++rr) voff[rr] = (uint32_t)((lane ^ swz(rr)) << 4);
+  // lane s of row r takes global chunk s ^ swz(r) into slot s.
+  // Every row read is a visible row: rows past the split repeat its last row and indexed
+  // slots naming a position outside the cache read row 0; both are masked out of the scores.
+  // Index lists are read with scalar loads, so waiting for them never waits for tile copies.
+  const uint32_t lane16 = (uint32_t)lane << 4;
   const uint32_t lds0 = lds_addr(&smem[0][0]);
-  int idx_next = -1;  // indexed: the position of tile row (lane & 31) of the next tile to issue
-  auto fetch_idx = [&](int t) {
-    if constexpr (INDEXED) {
-      const int s = s_begin + t * kTile + (lane & 31);
-      idx_next = (t < ntiles && s < s_end) ? idx_row[s] : -1;
+  auto issue = [&](int t) {
+    const uint32_t dst = lds0 + (t % kStages) * (kTile * kRowBytes) + wave * kRowsPerWave * kRowBytes;
+    const int base = s_begin + t * kTile + wave * kRowsPerWave;
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerWave; ++rr) {
+      int p;
+      if constexpr (INDEXED) {
+        p = idx_row[min(base + rr, s_end - 1)];
+        p = (p >= 0 && p < L) ? p : 0;
+      } else {
+        p = min(base + rr, s_end - 1);
+      }
+      row_to_lds(seq + (size_t)p * kRowBytes, dst + rr * kRowBytes, lane16,
+                 (uint32_t)(swz(wave * kRowsPerWave + rr) << 4));
     }
   };
-  auto issue = [&](int t, int stage) -> uint32_t {
-    const uint32_t dst = lds0 + stage * (kTile * kRowBytes) + wave * 8 * kRowBytes;
+  // rows of tile t that hold a visible position (bit r = tile row r)
+  auto valid_rows = [&](int t) -> uint32_t {
     const int base = s_begin + t * kTile;
-    uint32_t valid;
+    const int nvalid = s_end - base;
+    uint32_t v = nvalid >= kTile ? 0xffffffffu : ((1u << nvalid) - 1u);
     if constexpr (INDEXED) {
-      const bool ok = idx_next >= 0 && idx_next < L;
-      const int rp = ok ? idx_next : 0;
-      valid = (uint32_t)__builtin_amdgcn_ballot_w64(ok);
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int p = __builtin_amdgcn_readlane(rp, wave * 8 + rr);
-        row_to_lds(seq + (size_t)p * kRowBytes, dst + rr * kRowBytes, voff[rr]);
-      }
-    } else {
-      const int nvalid = s_end - base;
-      valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int p = min(base + wave * 8 + rr, s_end - 1);
-        row_to_lds(seq + (size_t)p * kRowBytes, dst + rr * kRowBytes, voff[rr]);
+      for (int r = 0; r < kTile; ++r) {
+        const int p = idx_row[min(base + r, s_end - 1)];
+        if (!(p >= 0 && p < L)) v &= ~(1u << r);
       }
     }
-    return valid;
+    return v;
   };
 
   // ---- per-lane LDS addressing (byte offsets inside a stage)
-  // scores: A row = tile row (lane & 31), global chunk 32lh + 2ks + hf, stored at
-  // chunk ^ swz(row); with ks = 4u + v that is 32lh + 8u + ((2v + hf) ^ swz(row))
+  // scores: A row = tile row (lane & 31), global chunk 32lh + 2ks + hf; the swizzle flips
+  // its low four bits, so with ks = 8u + v it sits at 32lh + 16u + ((2v + hf) ^ swz(row))
   const int prow = lane & 31;
   const int psw = swz(prow);
-  int qk_off[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) qk_off[v] = prow * kRowBytes + 512 * lh + (((2 * v + hf) ^ psw) << 4);
-  // values: transpose read; group g = lane / 16 supplies rows 4(g/2) + e (+16ks + 8r2) and
-  // latent columns 256lh + 32mb + 16(g&1) + 4c; the chunk 32lh + 4mb + x is stored at
-  // 32lh + 4 (mb ^ sb) + (x ^ (sw & 3)), sb = sw >> 2
+  const int qk_base = prow * kRowBytes + 512 * lh;
+  // values: transpose read; group g = lane / 16 supplies tile rows trow + 8r2 (+16ks),
+  // trow = 4(g/2) + e, and latent columns 256lh + 32mb + 16(g&1) + 4c: global chunk
+  // 32lh + 16(mb>>2) + 4(mb&3) + x with x = 2(g&1) + c/2.  For rows trow + 8r2 the swizzle is
+  // 4 fh + fl(r2) with fh = trow & 3 and fl(r2) = ((trow >> 2) + 2 r2) & 3, so the chunk sits at
+  // 32lh + 16(mb>>2) + 4((mb&3) ^ fh) + (x ^ fl(r2)).
   const int g = lane >> 4, ip = lane & 15, te = ip >> 2, tc = ip & 3;
   const int trow = 4 * (g >> 1) + te;
-  const int tsw = swz(trow);
-  const int tx = (2 * (g & 1) + (tc >> 1)) ^ (tsw & 3);
-  const int tsb = tsw >> 2;
-  const int tr_base = trow * kRowBytes + 512 * lh + (tx << 4) + ((tc & 1) << 3);
-  const int tr_even = tr_base + 64 * tsb;
-  const int tr_odd = tr_base - 64 * tsb;
+  const int tx = 2 * (g & 1) + (tc >> 1);
+  const int tfh = trow & 3;
+  const int tr_b0 = trow * kRowBytes + 512 * lh + ((tx ^ ((trow >> 2) & 3)) << 4) + ((tc & 1) << 3);
+  const int tr_b1 = (trow + 8) * kRowBytes + 512 * lh + ((tx ^ (((trow >> 2) + 2) & 3)) << 4) + ((tc & 1) << 3);
 
-  uint32_t valid_cur = 0, valid_next = 0;
-  if (ntiles > 0) {
-    fetch_idx(0);
-    valid_cur = issue(0, 0);
-    fetch_idx(1);
-  }
-
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmcnt<0>();
-    __syncthreads();  // tile t is in LDS for every wave; all are done with tile t-1
-    if (t + 1 < ntiles) {
-      valid_next = issue(t + 1, (t + 1) & 1);
-      fetch_idx(t + 2);
-    }
-    const uint8_t* tile = smem[t & 1];
-
-    // ---- partial scores over this wave's 256 latents
-    f32x16 s;
+  // partial scores of tile t over this wave's 256 latents: sixteen k-steps in pairs (the
+  // other wave on the SIMD covers the read latency)
+  auto scores = [&](const uint8_t* tile, f32x16& sc) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) s[k] = 0.f;
+    for (int k = 0; k < 16; ++k) sc[k] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 av = *(const bf16x8*)(tile + qk_off[ks & 3] + 128 * (ks >> 2));
-      s = mfma32(av, qf[ks], s);
-    }
-    // swap halves with the partner wave (same heads, other latents) and add
+    for (int grp = 0; grp < 8; ++grp) {
+      bf16x8 av[2];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) xbuf[wave][k][lane] = s[k];
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) s[k] += xbuf[wave ^ 2][k][lane];
-
-    // ---- online softmax (lane column = head h0+hl; rows 8ii + 4hf + j = tile positions)
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 8 * ii + 4 * hf + j;
-        const float x = ((valid_cur >> r) & 1u) ? s[4 * ii + j] * a.scale_log2 : -INFINITY;
-        s[4 * ii + j] = x;
-        tmax = fmaxf(tmax, x);
+      for (int k = 0; k < 2; ++k) {
+        const int ks = 2 * grp + k;
+        av[k] = *(const bf16x8*)(tile + qk_base + 256 * (ks >> 3) + (((2 * (ks & 7) + hf) ^ psw) << 4));
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+#pragma unroll
+      for (int k = 0; k < 2; ++k) sc = mfma32(av[k], qf[2 * grp + k], sc);
+    }
+  };
+  // add the partner's partial (same heads, other latents) and mask rows past the visible set
+  auto complete_scores = [&](f32x16& sc, uint32_t valid) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 x = xbuf[wave ^ 2][k][lane];
+      sc[4 * k] += x[0];
+      sc[4 * k + 1] += x[1];
+      sc[4 * k + 2] += x[2];
+      sc[4 * k + 3] += x[3];
+    }
+    if (valid != 0xffffffffu) {
+      const uint32_t vb = valid >> (4 * hf);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (!((vb >> (8 * ii + j)) & 1u)) sc[4 * ii + j] = -INFINITY;
+    }
+  };
+  // online softmax of one tile's scores (lane column = head h0+hl; rows 8ii + 4hf + j are
+  // tile positions); returns P^T as the B operand of the value MFMAs: k-slot e < 4 is
+  // position 16ks + 4hf + e, e >= 4 is 16ks + 8 + 4hf + e - 4
+  auto softmax = [&](const f32x16& sc, bf16x8 (&pf)[2]) {
+    float tmax = sc[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) tmax = fmaxf(tmax, sc[k]);
+    tmax = half_swap_max(tmax) * c2;  // scale > 0 keeps the order
     const float m_new = fmaxf(m_run, tmax);
     const bool need = m_new > m_run + kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -195,42 +200,66 @@ void latent_attn_kernel(AttnArgs a) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
       l_run *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int k = 0; k < 16; ++k) o[mb][k] *= alpha;
+      for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
       m_run = m_use;
     }
     const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
     float psum = 0.f;
+    float p[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const float p = __builtin_amdgcn_exp2f(s[k] - msafe);
-      s[k] = p;
-      psum += p;
+      p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[k], c2, -msafe));
+      psum += p[k];
     }
-    psum += __shfl_xor(psum, 32);
-    l_run += psum;
-
-    // P^T as the B operand: k-slot e < 4 -> position 16ks + 4hf + e, e >= 4 -> 16ks + 8 + 4hf + e-4
-    bf16x8 pf[2];
+    l_run += half_swap_sum(psum);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)s[4 * (2 * ks + (e >> 2)) + (e & 3)];
-
-    // ---- values: O^T += C^T . P^T, A from the transpose read of the same tile
+      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)p[4 * (2 * ks + (e >> 2)) + (e & 3)];
+  };
+  // values: O^T += C^T . P^T, A from the transpose read of the tile; sixteen MFMAs in eight
+  // pairs, the reads of pair g+1 in flight while pair g computes
+  auto values = [&](const uint8_t* tile, const bf16x8 (&pf)[2]) {
+    s16x4 tv[2][2][2];
+    auto load_g = [&](int grp, int buf) {
+      const int ks = grp >> 2;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const int base = (mb & 1) ? tr_odd : tr_even;
-        const uint8_t* p0 = tile + base + 64 * mb + (16 * ks) * kRowBytes;
-        const s16x4 lo = lds_read_tr16(p0);
-        const s16x4 hi = lds_read_tr16(p0 + 8 * kRowBytes);
-        o[mb] = mfma32(concat_bf16(lo, hi), pf[ks], o[mb]);
+      for (int k = 0; k < 2; ++k) {
+        const int mb = 2 * (grp & 3) + k;
+        const int sh = 256 * (mb >> 2) + 64 * ((mb & 3) ^ tfh) + (16 * ks) * kRowBytes;
+        tv[buf][k][0] = lds_read_tr16(tile + tr_b0 + sh);
+        tv[buf][k][1] = lds_read_tr16(tile + tr_b1 + sh);
       }
+    };
+    load_g(0, 0);
+#pragma unroll
+    for (int grp = 0; grp < 8; ++grp) {
+      if (grp + 1 < 8) load_g(grp + 1, (grp + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int mb = 2 * (grp & 3) + k;
+        o[mb] = mfma32(concat_bf16(tv[grp & 1][k][0], tv[grp & 1][k][1]), pf[grp >> 2], o[mb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    valid_cur = valid_next;
+  };
+
+  if (ntiles > 0) issue(0);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<0>();  // tile t (the only copy in flight) has landed
+    __syncthreads();  // ... for every wave; every wave is done with tile t-1
+    if (t + 1 < ntiles) issue(t + 1);  // into the stage tile t-1 used
+    const uint8_t* tile = smem[t % kStages];
+    f32x16 s;
+    scores(tile, s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xbuf[wave][k][lane] = (f32x4){s[4 * k], s[4 * k + 1], s[4 * k + 2], s[4 * k + 3]};
+    __syncthreads();
+    complete_scores(s, valid_rows(t));
+    bf16x8 pf[2];
+    softmax(s, pf);
+    values(tile, pf);
   }
 
   // ---- results: lane holds head h0+hl, latents 256lh + 32mb + 8ii + 4hf + j

@@ -30,11 +30,13 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 // 16-byte-chunk swizzle for a row of an LDS tile: chunk c of row r lives at slot c ^ swz(r).
-// swz is a bijection of r mod 8 onto 0..7, chosen so that (a) eight consecutive rows at one
-// chunk hit eight different 16-byte bank groups (row-major operand reads), and (b) four
-// consecutive rows (aligned to 4) at two adjacent chunks hit eight different bank groups
-// (transpose reads).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// gfx950's LDS serves 256 bytes (64 banks x 4 bytes) per cycle, i.e. 16 lanes of a 16-byte
+// read or 32 lanes of an 8-byte read.  swz is a bijection of r mod 16 onto 0..15 chosen so
+// that (a) sixteen consecutive rows at one chunk hit sixteen different bank groups
+// (row-major operand reads), and (b) four consecutive rows (aligned to 4) at four adjacent
+// chunks (aligned to 4) hit sixteen different bank groups (transpose reads).  Rows must be a
+// multiple of 256 bytes long and hold at least 16 chunks.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
@@ -70,23 +72,70 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // One 1 KiB row, global -> LDS without passing through registers: lane s copies the 16
-// bytes at row + voff(s) to lds + 16 * s.  `row` and `lds` are wave-uniform (SGPRs);
-// voff is the lane's byte offset inside the row.  Issued from asm so that the compiler does
-// not wait for these copies before unrelated LDS reads: the caller waits (vmcnt) itself
-// before the copied data is read.  M0 is written one wait state before the copy uses it; the
-// kernels that call this use M0 for nothing else (no LDS-DMA builtins, no indirect register
-// indexing), so clobbering it is safe.
-__device__ __forceinline__ void row_to_lds(const uint8_t* row, uint32_t lds, uint32_t voff) {
+// bytes at row + (lane16(s) ^ sw) to lds + 16 * s, lane16 = 16 * s.  `row`, `lds` and `sw`
+// are wave-uniform (SGPRs).  Issued from asm so that the compiler does not wait for these
+// copies before unrelated LDS reads: the caller waits (vmcnt) itself before the copied data
+// is read.  The per-row lane offset is formed inside the asm, so no per-row register stays
+// live in the caller; the load reads it when it issues.  M0 is written one wait state before
+// the copy uses it; the kernels that call this use M0 for nothing else (no LDS-DMA builtins, no
+// indirect register indexing), so clobbering it is safe.
+__device__ __forceinline__ void row_to_lds(const uint8_t* row, uint32_t lds, uint32_t lane16, uint32_t sw) {
+  // the operands are wave-uniform by construction; readfirstlane makes them SGPRs for certain
+  const uint64_t ra = (uint64_t)(uintptr_t)row;
+  const uint64_t rs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ra >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ra);
+  const uint32_t ls = __builtin_amdgcn_readfirstlane(lds);
+  const uint32_t ss = __builtin_amdgcn_readfirstlane(sw);
+  uint32_t voff;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds), "v"(voff), "s"(row)
+      "s_mov_b32 m0, %1\n\t"
+      "v_xor_b32 %0, %2, %3\n\t"
+      "global_load_lds_dwordx4 %0, %4"
+      : "=&v"(voff)
+      : "s"(ls), "s"(ss), "v"(lane16), "s"(rs)
       : "memory", "m0");
 #pragma clang diagnostic pop
+}
+
+// acc *= alpha for an MFMA accumulator that lives in AGPRs, done in place (read, multiply,
+// write back one register at a time).  Written in asm so that the only other uses of the
+// accumulator are matrix-core operands and the compiler keeps it in AGPRs instead of copying
+// it to VGPRs around every use.  The leading s_nop covers the matrix core's write latency
+// should an MFMA that writes acc still be in flight; the trailing one covers a following
+// MFMA that reads acc as its accumulator input.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    float x = acc[k];
+    float tmp;
+    if (k == 0)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\tv_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\t"
+                   "v_accvgpr_write_b32 %0, %1"
+                   : "+a"(x), "=&v"(tmp) : "v"(alpha));
+    else if (k == 15)
+      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1\n\ts_nop 4"
+                   : "+a"(x), "=&v"(tmp) : "v"(alpha));
+    else
+      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                   : "+a"(x), "=&v"(tmp) : "v"(alpha));
+    acc[k] = x;
+  }
+}
+
+// Combine a value with the one in the other half of the wave (lane l and l ^ 32):
+// v_permlane32_swap(x, x) returns x's lanes 0-31 in both halves of its first result and lanes
+// 32-63 in both halves of the second, so one VALU op pairs every lane with its partner.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 // Map the hardware workgroup id to a logical id so that consecutive logical ids run on the
