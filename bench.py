@@ -36,7 +36,7 @@ def log(*a):
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("latent_attn.hip", "mla_device.h", "mla_internal.h"):
+    for f in ("latent_attn.hip", "mla_device.h", "mla_internal.h", "mla_api.hip"):
         h.update(open(os.path.join(ROOT, "mla_latent_cache_absorb_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -106,12 +106,12 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
     Lmax = int(w0.cache.shape[1])
     indexed = w0.idx is not None
     K_max = w0.idx.shape[2] if indexed else Lmax
-    splits = binding.mla_latent_attn_num_splits(B, Q, H, K_max, 0)
+    splits = binding.mla_latent_attn_num_splits(B, Q, H, K_max, 0, indexed=indexed)
     q_abs = torch.empty((B, Q, H, R), dtype=torch.bfloat16, device=dev)
     o_lat = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
     out = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev)
-    ws_bytes = binding.mla_latent_attn_workspace_size(B, Q, H, R, K_max, 0)
+    ws_bytes = binding.mla_latent_attn_workspace_size(B, Q, H, R, K_max, 0, indexed=indexed)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -193,6 +193,9 @@ def main():
     ap.add_argument("--workload", default="decode_b32_l8192")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device three times (a plain copy of known size, "
+                         "so that hardware byte counters can be scaled)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -208,6 +211,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 18  # int32 elements
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.calibrate_copy} MiB three times")
+        del src, dst
+        torch.cuda.empty_cache()
     r = time_path(args.workload, args.steps, args.warmup, NSETS)
     w = r["workload"]
     B, Q, H, D = w.q.shape

@@ -86,10 +86,13 @@ int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int32_
  *                  clamped to [1, 1024] and to the number of 32-position tiles, then lowered
  *                  so that no split is empty once the positions are cut into equal runs of
  *                  whole tiles (e.g. 8 tiles asked for 5 splits use 4 splits of 2 tiles)
+ *   indexed        0 for mla_latent_attn, 1 for mla_latent_attn_indexed (the automatic
+ *                  choice differs: single-query and indexed calls are priced as bandwidth
+ *                  bound, dense multi-query calls as matrix-core bound)
  * Returns the split count (>= 1), or a negative status for bad sizes.
  */
 int32_t mla_latent_attn_num_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions,
-                                   int32_t num_splits);
+                                   int32_t num_splits, int32_t indexed);
 
 /*
  * Workspace bytes a latent-attention call needs (0 when it uses one split): the split
@@ -98,7 +101,7 @@ int32_t mla_latent_attn_num_splits(int32_t B, int32_t Q, int32_t H, int32_t max_
  * attention calls reject a workspace that is too small.
  */
 size_t mla_latent_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R,
-                                      int32_t max_positions, int32_t num_splits);
+                                      int32_t max_positions, int32_t num_splits, int32_t indexed);
 
 /*
  * Dense latent attention (page "Module 05", section 3: scores read the cached latent

@@ -48,9 +48,9 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_absorb_q.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, vp]
         L.mla_absorb_q.restype = ctypes.c_int
-        L.mla_latent_attn_num_splits.argtypes = [i32, i32, i32, i32, i32]
+        L.mla_latent_attn_num_splits.argtypes = [i32, i32, i32, i32, i32, i32]
         L.mla_latent_attn_num_splits.restype = i32
-        L.mla_latent_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.mla_latent_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.mla_latent_attn_workspace_size.restype = sz
         L.mla_latent_attn.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
         L.mla_latent_attn.restype = ctypes.c_int
@@ -106,14 +106,16 @@ def mla_absorb_q(q: torch.Tensor, w_k: torch.Tensor, q_abs: Optional[torch.Tenso
     return q_abs
 
 
-def mla_latent_attn_num_splits(B: int, Q: int, H: int, max_positions: int, num_splits: int = 0) -> int:
-    s = lib().mla_latent_attn_num_splits(B, Q, H, max_positions, num_splits)
+def mla_latent_attn_num_splits(B: int, Q: int, H: int, max_positions: int, num_splits: int = 0,
+                               indexed: bool = False) -> int:
+    s = lib().mla_latent_attn_num_splits(B, Q, H, max_positions, num_splits, int(bool(indexed)))
     _check(min(int(s), 0), "mla_latent_attn_num_splits")
     return int(s)
 
 
-def mla_latent_attn_workspace_size(B: int, Q: int, H: int, R: int, max_positions: int, num_splits: int = 0) -> int:
-    return int(lib().mla_latent_attn_workspace_size(B, Q, H, R, max_positions, num_splits))
+def mla_latent_attn_workspace_size(B: int, Q: int, H: int, R: int, max_positions: int, num_splits: int = 0,
+                                   indexed: bool = False) -> int:
+    return int(lib().mla_latent_attn_workspace_size(B, Q, H, R, max_positions, num_splits, int(bool(indexed))))
 
 
 def _cache_stride(cache: torch.Tensor) -> int:
@@ -173,7 +175,7 @@ def mla_latent_attn_indexed(q_abs: torch.Tensor, cache: torch.Tensor, cache_len:
     B, Q, H, R = q_abs.shape
     K_max = idx.shape[-1]
     o_lat, lse = _attn_outputs(q_abs, o_lat, lse, want_lse)
-    need = mla_latent_attn_workspace_size(B, Q, H, R, K_max, num_splits)
+    need = mla_latent_attn_workspace_size(B, Q, H, R, K_max, num_splits, indexed=True)
     workspace = _workspace(workspace, need, q_abs.device)
     _check(lib().mla_latent_attn_indexed(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
                                          _ptr(idx_len), K_max, B, Q, H, R, int(max_cache_len), float(scale),

@@ -84,3 +84,13 @@ def test_split_sizing(L):
     assert binding.mla_latent_attn_num_splits(1, 1, 64, 64, 5) == 2    # two tiles at most
     assert binding.mla_latent_attn_num_splits(1, 1, 64, 100, 3) == 2   # 4 tiles as 2+2
     assert binding.mla_latent_attn_workspace_size(1, 1, 64, 512, 256, 1) == 0
+
+
+def test_split_choice_without_device(L):
+    # with no GPU visible the choice assumes 256 CUs: bandwidth-bound calls (one query, or
+    # index lists) get one workgroup per CU, dense multi-query calls two
+    assert binding.mla_latent_attn_num_splits(32, 1, 64, 8192, 0) == 8          # 256 workgroups
+    assert binding.mla_latent_attn_num_splits(4, 1, 64, 131072, 0) == 64        # 256 workgroups
+    assert binding.mla_latent_attn_num_splits(16, 6, 64, 32768, 0) == 5         # 480 workgroups
+    assert binding.mla_latent_attn_num_splits(32, 4, 64, 2052, 0, indexed=True) == 2
+    assert binding.mla_latent_attn_workspace_size(32, 4, 64, 512, 2052, 0, indexed=True) == 2 * 128 * 64 * 514 * 4

@@ -124,6 +124,27 @@ def test_indexed_latent_attn_matches_oracle():
         np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=1e-3)
 
 
+# ------------------------------------------------------------------ q_len sweep
+# Draft depths 0..7 (one to eight query positions per pass): the query-to-position mapping and
+# the causal tail of the last tile for every depth, dense and indexed, ragged lengths, through
+# the whole path (absorb, attention, up-projection).
+@pytest.mark.parametrize("Q", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_q_len_sweep_whole_path(Q):
+    spec = wl.make_spec(3, Q, 203, min_cache_len=Q, workload_id=500 + Q)
+    w = wl.make_workload(spec)
+    out, lse = run_path(w)
+    ref, lse_ref = oracle.mla_reference(w.q, w.cache, w.w_k, w.w_v, w.cache_len, w.scale)
+    assert_parity(out, ref, f"dense Q{Q} out")
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-2)
+    spec_i = wl.make_spec(2, Q, 300, min_cache_len=100, n_index=40, workload_id=520 + Q)
+    wi = wl.make_workload(spec_i)
+    out, lse = run_path(wi)
+    ref, lse_ref = oracle.mla_reference(wi.q, wi.cache, wi.w_k, wi.w_v, wi.cache_len, wi.scale, idx=wi.idx,
+                                        idx_len=wi.idx_len)
+    assert_parity(out, ref, f"indexed Q{Q} out")
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-2)
+
+
 # ------------------------------------------------------------------ whole path, small
 def test_decode_b1_l256_whole_output():
     w = wl.make_workload("decode_b1_l256")
