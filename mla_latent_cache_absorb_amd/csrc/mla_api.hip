@@ -32,17 +32,16 @@ int check_device(int* cus) {
   return MLA_OK;
 }
 
-// The split count: independent work units are (sequence, query, 64-head group); the
-// positions of each are cut into `s` contiguous splits of whole tiles.  The estimate charges
-// the rounds of resident workgroups times the tiles of one split, plus the partial results
-// each extra split writes and the merge reads back (a 128 KiB partial is worth four 32 KiB
-// tiles each way) and a fixed cost for the merge launch.  A memory-bound call (one query per
-// sequence, or index lists, whose rows no two queries share) is priced at one workgroup per
-// CU: a second one adds no HBM bandwidth, only more partials.  A dense multi-query call is
-// matrix-core bound and runs two workgroups per CU.
-int32_t choose_splits(int64_t units, int32_t max_positions, int cus, bool memory_bound) {
+// The split count.  Independent work units are (sequence, query unit, 64-head group), a
+// query unit being one query, or two queries of one sequence when several share its cache
+// (dense calls with Q > 1); the positions of each unit are cut into `s` contiguous splits of
+// whole tiles, one workgroup per CU.  The estimate charges the rounds of resident workgroups
+// times the tiles of one split, plus the partial results each extra split writes and the
+// merge reads back (a 128 KiB partial per query is worth four 32 KiB tiles each way) and a
+// fixed cost for the merge launch.
+int32_t choose_splits(int64_t units, int32_t queries_per_unit, int32_t max_positions, int cus) {
   const int64_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
-  const int64_t slots = (memory_bound ? 1 : 2) * (int64_t)(cus > 0 ? cus : 256);
+  const int64_t slots = cus > 0 ? cus : 256;
   const int64_t smax = tiles < mla::kMaxSplits ? tiles : mla::kMaxSplits;
   int32_t best = 1;
   double best_cost = 1e300;
@@ -51,7 +50,7 @@ int32_t choose_splits(int64_t units, int32_t max_positions, int cus, bool memory
     if ((s - 1) * per >= tiles) continue;  // would leave an empty split
     const int64_t rounds = (units * s + slots - 1) / slots;
     double cost = (double)rounds * (double)per;
-    if (s > 1) cost += (double)(units * s * 8) / (double)slots + 3.0;
+    if (s > 1) cost += (double)(units * queries_per_unit * s * 8) / (double)slots + 3.0;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = (int32_t)s;
@@ -69,14 +68,18 @@ int32_t split_length(int32_t max_positions, int32_t s) {
 
 bool supported(int32_t H, int32_t D, int32_t R) { return R == 512 && D == 256 && H > 0 && H % 64 == 0; }
 
+// queries handled by one workgroup: two for dense multi-query calls, else one
+int32_t queries_per_unit(int32_t Q, bool indexed) { return (!indexed && Q > 1) ? 2 : 1; }
+
 int resolve_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions, int32_t num_splits, int cus,
-                   bool memory_bound) {
+                   bool indexed) {
   if (B < 1 || Q < 1 || H < 64 || H % 64 != 0 || max_positions < 1) return MLA_ERR_SHAPE;
   if (num_splits < 0) return MLA_ERR_ARG;
   const int32_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
   int32_t s;
   if (num_splits == 0) {
-    s = choose_splits((int64_t)B * Q * (H / 64), max_positions, cus, memory_bound);
+    const int32_t qpu = queries_per_unit(Q, indexed);
+    s = choose_splits((int64_t)B * ((Q + qpu - 1) / qpu) * (H / 64), qpu, max_positions, cus);
   } else {
     s = num_splits > mla::kMaxSplits ? mla::kMaxSplits : num_splits;
     if (s > tiles) s = tiles;
@@ -118,11 +121,13 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   const int dst = check_device(&cus);
   if (dst != MLA_OK) return dst;
   const int32_t max_positions = indexed ? K_max : max_cache_len;
-  const int s = resolve_splits(B, Q, H, max_positions, num_splits, cus, indexed || Q == 1);
+  const int s = resolve_splits(B, Q, H, max_positions, num_splits, cus, indexed);
   if (s < 1) return s;
   const size_t need = workspace_bytes_for(B, Q, H, s);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
-  const int64_t total = (int64_t)B * Q * (H / 64) * s;
+  const int32_t qpu = queries_per_unit(Q, indexed);
+  const int32_t q_units = (Q + qpu - 1) / qpu;
+  const int64_t total = (int64_t)B * q_units * (H / 64) * s;
   if (total > 0x7fffffff || (int64_t)B * Q * H > 0x7fffffff) return MLA_ERR_SHAPE;
 
   mla::AttnArgs a;
@@ -137,6 +142,7 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   a.Q = Q;
   a.H = H;
   a.HG = H / 64;
+  a.q_units = q_units;
   a.max_cache_len = max_cache_len;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_splits = s;
@@ -184,13 +190,13 @@ int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int32_
 
 int32_t mla_latent_attn_num_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions, int32_t num_splits,
                                    int32_t indexed) {
-  return resolve_splits(B, Q, H, max_positions, num_splits, device_cus_or_default(), indexed != 0 || Q == 1);
+  return resolve_splits(B, Q, H, max_positions, num_splits, device_cus_or_default(), indexed != 0);
 }
 
 size_t mla_latent_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_positions,
                                       int32_t num_splits, int32_t indexed) {
   if (R != 512) return 0;
-  const int s = resolve_splits(B, Q, H, max_positions, num_splits, device_cus_or_default(), indexed != 0 || Q == 1);
+  const int s = resolve_splits(B, Q, H, max_positions, num_splits, device_cus_or_default(), indexed != 0);
   if (s < 1) return 0;
   return workspace_bytes_for(B, Q, H, s);
 }

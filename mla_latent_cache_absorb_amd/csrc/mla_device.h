@@ -99,6 +99,30 @@ __device__ __forceinline__ void row_to_lds(const uint8_t* row, uint32_t lds, uin
 #pragma clang diagnostic pop
 }
 
+// As row_to_lds, for a row `off` bytes past a wave-uniform `base`: the lane offset is
+// (lane16 ^ sw) + off, so consecutive rows share one base address.
+__device__ __forceinline__ void row_to_lds_at(const uint8_t* base, uint32_t off, uint32_t lds, uint32_t lane16,
+                                              uint32_t sw) {
+  const uint64_t ra = (uint64_t)(uintptr_t)base;
+  const uint64_t rs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ra >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ra);
+  const uint32_t ls = __builtin_amdgcn_readfirstlane(lds);
+  const uint32_t ss = __builtin_amdgcn_readfirstlane(sw);
+  const uint32_t os = __builtin_amdgcn_readfirstlane(off);
+  uint32_t voff;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "v_xor_b32 %0, %2, %3\n\t"
+      "v_add_u32 %0, %4, %0\n\t"
+      "global_load_lds_dwordx4 %0, %5"
+      : "=&v"(voff)
+      : "s"(ls), "s"(ss), "v"(lane16), "s"(os), "s"(rs)
+      : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // acc *= alpha for an MFMA accumulator that lives in AGPRs, done in place (read, multiply,
 // write back one register at a time).  Written in asm so that the only other uses of the
 // accumulator are matrix-core operands and the compiler keeps it in AGPRs instead of copying
@@ -122,6 +146,14 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
                    : "+a"(x), "=&v"(tmp) : "v"(alpha));
     acc[k] = x;
   }
+}
+
+// A copy of x that the compiler cannot see through.  Address arithmetic derived from it inside
+// a loop stays in the loop (recomputed with a VALU op or two per use) instead of being hoisted
+// into loop-invariant registers, which the big kernels cannot spare.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // Combine a value with the one in the other half of the wave (lane l and l ^ 32):
