@@ -40,6 +40,49 @@ constexpr int kTileBytes = kTile * kRowBytes;
 constexpr int kRowsPerWave = kTile / 4;   // rows each wave of the copying subgroup copies per tile
 constexpr float kRescaleLog2 = 8.0f;
 
+// Log-sum-exp merge of the split partials of one output row (b, i, head), exact up to rounding:
+// every split's sum is rescaled to the common maximum.  Thread t of a group of 128 owns
+// latents 4t .. 4t+3; splits are taken eight at a time with all their loads in flight.
+__device__ __forceinline__ void merge_row(const AttnArgs& a, size_t row, int t) {
+  const size_t rows = (size_t)a.B * a.Q * a.H;
+  const int S = a.num_splits;
+  const float* ml = a.part_ml + 2 * row;
+  const float* po = a.part_o + row * kLatent + 4 * t;
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float mm[8], ll[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = min(s0 + k, S - 1);
+      mm[k] = ml[2 * s * rows];
+      ll[k] = ml[2 * s * rows + 1];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (ll[k] > 0.f) M = fmaxf(M, mm[k]);
+  }
+  float Ls = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = *(const f32x4*)(po + (size_t)min(s0 + k, S - 1) * rows * kLatent);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = min(s0 + k, S - 1);
+      const float m = ml[2 * s * rows];
+      const float l = ml[2 * s * rows + 1];
+      const float w = (s0 + k < S && l > 0.f) ? __builtin_amdgcn_exp2f(m - M) : 0.f;
+      Ls += w * l;
+      acc += w * v[k];
+    }
+  }
+  const float inv = 1.0f / Ls;
+  *(f32x4*)(a.o_lat + row * kLatent + 4 * t) = acc * inv;
+  // __builtin_amdgcn_logf is the hardware base-2 logarithm
+  if (a.lse != nullptr && t == 0) a.lse[row] = (M + __builtin_amdgcn_logf(Ls)) * 0.69314718055994531f;
+}
+
 template <bool INDEXED, bool PAIR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void latent_attn_kernel(AttnArgs a) {
@@ -418,49 +461,8 @@ void latent_attn_kernel(AttnArgs a) {
   }
 }
 
-// Log-sum-exp merge of the split partials (exact up to rounding: every split's sum is
-// rescaled to the common maximum).  One workgroup per (b, i, head); thread t owns latents
-// 4t .. 4t+3.  Splits are taken eight at a time with all their loads in flight together.
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
-  const int row = blockIdx.x;  // (b*Q + i)*H + h
-  const int t = threadIdx.x;
-  const size_t rows = (size_t)a.B * a.Q * a.H;
-  const int S = a.num_splits;
-  const float* ml = a.part_ml + 2 * (size_t)row;
-  const float* po = a.part_o + (size_t)row * kLatent + 4 * t;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float mm[8], ll[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int s = min(s0 + k, S - 1);
-      mm[k] = ml[2 * s * rows];
-      ll[k] = ml[2 * s * rows + 1];
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (ll[k] > 0.f) M = fmaxf(M, mm[k]);
-  }
-  float Ls = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    f32x4 v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = *(const f32x4*)(po + (size_t)min(s0 + k, S - 1) * rows * kLatent);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int s = min(s0 + k, S - 1);
-      const float m = ml[2 * s * rows];
-      const float l = ml[2 * s * rows + 1];
-      const float w = (s0 + k < S && l > 0.f) ? __builtin_amdgcn_exp2f(m - M) : 0.f;
-      Ls += w * l;
-      acc += w * v[k];
-    }
-  }
-  const float inv = 1.0f / Ls;
-  *(f32x4*)(a.o_lat + (size_t)row * kLatent + 4 * t) = acc * inv;
-  if (a.lse != nullptr && t == 0) a.lse[row] = (M + __builtin_amdgcn_logf(Ls)) * 0.69314718055994531f;
-}
+// Merge of the split partials: one workgroup of 128 threads per (b, i, head).
+__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) { merge_row(a, blockIdx.x, threadIdx.x); }
 
 }  // namespace
 

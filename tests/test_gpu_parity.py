@@ -124,6 +124,23 @@ def test_indexed_latent_attn_matches_oracle():
         np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=1e-3)
 
 
+# ------------------------------------------------------------------ many splits
+def test_many_splits_more_workgroups_than_cus():
+    # more split workgroups than CUs (several rounds of workgroups), ragged lengths
+    B, L = 48, 1024
+    spec = wl.make_spec(B, 1, L, min_cache_len=200, workload_id=620)
+    w = wl.make_workload(spec)
+    qa = bf16(wl.latent_query_bits(spec))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    splits = 8
+    assert B * splits > cus
+    o, lse = binding.mla_latent_attn(qa, bf16(w.cache), i32(w.cache_len), L, w.scale, splits)
+    torch.cuda.synchronize()
+    ref, lse_ref = oracle.latent_attention(F(bits(qa)), w.cache, w.cache_len, w.scale)
+    assert_parity(o.cpu().numpy(), ref, "separate merge")
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=1e-3)
+
+
 # ------------------------------------------------------------------ q_len sweep
 # Draft depths 0..7 (one to eight query positions per pass): the query-to-position mapping and
 # the causal tail of the last tile for every depth, dense and indexed, ragged lengths, through
