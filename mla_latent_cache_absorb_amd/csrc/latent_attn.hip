@@ -2,30 +2,25 @@
 // directly on the cached 512-wide latents (page "Module 05 -- MLA: Compressing Per-Token
 // History", section 3; colibri "MLA is absorbed").
 //
-// One workgroup per CU: 512 threads, two subgroups of four waves.  In a subgroup, wave w owns
-// heads 32*(w&1) .. +31 of a group of 64 and latents 256*(w>>1) .. +255.  Tiles of 32 cached
-// latents (32 KiB) are copied from HBM straight into a four-tile LDS ring with
-// global_load_lds_dwordx4, two tiles ahead of use.  Each tile passes two phases per subgroup:
-//   A  scores    S^T[32 pos x 32 heads] = C[32 x 512] . Q~^T[512 x 32]: each wave contracts its
-//                own 256 latents (16 MFMA 32x32x16; A operand = the tile row-major via
-//                ds_read_b128, B operand = the absorbed query held in VGPRs) and posts its
-//                partial sum to LDS for the wave holding the other 256 latents
-//   B  softmax   add the partner's partial, mask, online softmax per head = per lane column
-//                (the running maximum only moves when it grows by more than 2^8, so the
-//                accumulator is rarely rescaled); then
-//      values    O^T[256 x 32 heads] += C^T[256 x 32 pos] . P^T[32 pos x 32 heads] (16 MFMA;
-//                A = the SAME tile read transposed with ds_read_b64_tr_b16, B = P straight
-//                from the score registers, the MFMA's K order permuted to match them)
-// The subgroups run one phase apart, so between two barriers one subgroup is in phase A
-// (matrix core + row reads) while the other is in phase B (VALU + transpose reads + matrix
-// core): on every SIMD one wave of each kind.
-//   PAIR (dense, several queries): the subgroups take queries 2u and 2u+1 of a sequence over
-//        the same tiles, so one copy of a tile serves both.
-//   otherwise (one query, or index lists): the subgroups take alternate tiles of one query's
-//        split and merge their two partial softmaxes through LDS at the end.
-// One latent row serves all 64 heads: the cache is read once per (query pair, split).
-#include <type_traits>
-
+// One workgroup = one (sequence b, query i, group of 64 heads, split of positions), one per
+// CU: 768 threads in twelve waves with two roles.  Tiles of 32 cached latents (32 KiB) are
+// copied from HBM straight into a four-tile LDS ring with global_load_lds_dwordx4, two tiles
+// ahead of use; one barrier opens each step.
+//   score waves (0-3), wave s owning heads 16s .. 16s+15 of the group, in step t on tile t:
+//     S^T[32 pos x 16 heads] = C[32 x 512] . Q~^T[512 x 16] over all 512 latents (32 MFMA
+//     16x16x32; A operand = tile rows via ds_read_b128, B operand = the absorbed query held in
+//     VGPRs for the whole kernel); online softmax per head (the running maximum moves only
+//     when it grows by more than 2^8, so the accumulators are rarely rescaled); P is posted
+//     to LDS in bf16 with the step's rescale factor
+//   value waves (4-11), wave 4+v owning heads 32(v>>2) .. +31 and latents 128(v&3) .. +127,
+//     in step t on tile t-1: O^T[128 x 32 heads] = O^T * alpha + C^T[128 x 32 pos] .
+//     P^T[32 pos x 32 heads] (8 MFMA 32x32x16; A operand = the same tile read transposed with
+//     ds_read_b64_tr_b16, B operand = P from LDS); they also copy the tiles, four rows each
+// Each SIMD runs one score wave and two value waves, so its matrix core has work from both
+// halves of the computation while either role waits on LDS, and no wave holds both the
+// query registers and the accumulators.  One latent row serves all 64 heads: the cache is read
+// once per (query, split); the queries of one split are placed on one XCD and share the tiles
+// through its L2.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -34,15 +29,31 @@ namespace mla {
 namespace {
 
 constexpr int kTile = kTilePositions;
-constexpr int kThreads = 512;
+constexpr int kThreads = 768;
 constexpr int kRing = 4;                  // LDS tiles: two in use, two in flight
 constexpr int kTileBytes = kTile * kRowBytes;
-constexpr int kRowsPerWave = kTile / 4;   // rows each wave of the copying subgroup copies per tile
+constexpr int kRowsPerVWave = kTile / 8;  // rows each value wave copies per tile
+constexpr int kPStride = 80;              // bytes per head in the P buffer: 32 bf16 + padding
 constexpr float kRescaleLog2 = 8.0f;
 
-// Log-sum-exp merge of the split partials of one output row (b, i, head), exact up to rounding:
-// every split's sum is rescaled to the common maximum.  Thread t of a group of 128 owns
-// latents 4t .. 4t+3; splits are taken eight at a time with all their loads in flight.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 (one head's column of a 16x16 MFMA result)
+__device__ __forceinline__ float quad_max(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  return half_swap_max(x);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  return half_swap_sum(x);
+}
+
 __device__ __forceinline__ void merge_row(const AttnArgs& a, size_t row, int t) {
   const size_t rows = (size_t)a.B * a.Q * a.H;
   const int S = a.num_splits;
@@ -83,381 +94,266 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, size_t row, int t) 
   if (a.lse != nullptr && t == 0) a.lse[row] = (M + __builtin_amdgcn_logf(Ls)) * 0.69314718055994531f;
 }
 
-template <bool INDEXED, bool PAIR>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+
+template <bool INDEXED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void latent_attn_kernel(AttnArgs a) {
-  static_assert(!(INDEXED && PAIR), "index lists are per query");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing][kTileBytes];
-  __shared__ __attribute__((aligned(16))) f32x4 xbuf[2][4][4][64];  // partial scores [subgroup][wave][reg/4][lane]
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][64 * kPStride];  // P [head][pos] bf16
+  __shared__ float abuf[2][64];                                            // rescale factor per head
+  __shared__ float mlbuf[2][64];                                           // final (m, l) per head
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps it in SGPRs
-  const int sg = wave >> 2;       // subgroup
-  const int w4 = wave & 3;        // wave within the subgroup
-  const int hh = w4 & 1;          // head half of the group
-  const int lh = w4 >> 1;         // latent half
   const int wg = xcd_remap(blockIdx.x, a.total_wg);
-  // logical order (b, head group, split, query unit): the query units of one split of one
-  // sequence are adjacent, so they run on the same XCD and share the tile through its L2
-  const int qu = wg % a.q_units;
-  int rest = wg / a.q_units;
+  // logical order (b, head group, split, query): the queries of one split of one sequence are
+  // adjacent, so they run on the same XCD and share the tile through its L2
+  const int i = wg % a.Q;
+  int rest = wg / a.Q;
   const int split = rest % a.num_splits;
   rest /= a.num_splits;
   const int hg = rest % a.HG;
   const int b = rest / a.HG;
-  const int i = PAIR ? 2 * qu + sg : qu;  // this subgroup's query
-  const bool active = i < a.Q;            // PAIR with odd Q: the last unit has one query
-  const int bq = b * a.Q + (active ? i : a.Q - 1);
-  const int h0 = hg * 64 + hh * 32;
-  const int hl = lane & 31;
-  const int hf = lane >> 5;
+  const int bq = b * a.Q + i;
 
   const int L = min(a.cache_len[b], a.max_cache_len);
-  int n_slots, n_range;  // visible slots of this subgroup's query / of the unit's longest query
+  int n_slots;
   const int32_t* idx_row = nullptr;
   if constexpr (INDEXED) {
     idx_row = a.idx + (size_t)bq * a.K_max;
     n_slots = L > 0 ? min(a.idx_len[bq], a.K_max) : 0;
-    n_range = n_slots;
   } else {
-    n_slots = active ? L - a.Q + i + 1 : 0;  // positions 0 .. cache_len - Q + i
-    n_range = PAIR ? L - a.Q + min(2 * qu + 1, a.Q - 1) + 1 : n_slots;
+    n_slots = L - a.Q + i + 1;  // positions 0 .. cache_len - Q + i
   }
   n_slots = max(n_slots, 0);
-  n_range = max(n_range, 0);
   const int s_begin = split * a.split_len;
-  const int s_end = min(s_begin + a.split_len, n_range);
-  const int my_end = min(s_begin + a.split_len, n_slots);
+  const int s_end = min(s_begin + a.split_len, n_slots);
   const int ntiles = s_end > s_begin ? (s_end - s_begin + kTile - 1) / kTile : 0;
   const uint8_t* seq = a.cache + (size_t)b * a.cache_bstride_bytes;
-  const float c2 = a.scale_log2;
-
-  // absorbed query of head h0+hl as the B operand: latents 256lh + 16ks + 8hf .. +7
-  bf16x8 qf[16];
-  {
-    const uint16_t* qrow = a.q_abs + ((size_t)bq * a.H + h0 + hl) * kLatent + 256 * lh + 8 * hf;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = *(const bf16x8*)(qrow + 16 * ks);
-  }
-
-  f32x16 o[8];
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int k = 0; k < 16; ++k) o[mb][k] = 0.f;
-  float m_run = -INFINITY;  // running maximum of scale*log2(e)*score
-  float l_run = 0.f;        // running sum of 2^(scale*log2(e)*score - m_run)
-
-  // ---- tile loader: tiles are copied by the four waves of one subgroup, wave w4 taking
-  // rows 8w4 .. 8w4+7, one 1 KiB row per instruction, lane s of row r taking global chunk
-  // s ^ swz(r) into slot s.  Every row read is a visible row: rows past the split repeat its
-  // last row and indexed slots naming a position outside the cache read row 0; both are
-  // masked out of the scores.  Index lists are read with scalar loads, so waiting for them
-  // never waits for tile copies.
   const uint32_t lane16 = (uint32_t)lane << 4;
   const uint32_t lds0 = lds_addr(&smem[0][0]);
-  auto issue_row = [&](int t, int rr) {
-    const int r = w4 * kRowsPerWave + rr;
-    const int slot = s_begin + t * kTile + r;
-    const uint32_t dst = lds0 + (t % kRing) * kTileBytes + r * kRowBytes;
-    if constexpr (INDEXED) {
-      int p = idx_row[min(slot, s_end - 1)];
-      p = (p >= 0 && p < L) ? p : 0;
-      row_to_lds(seq + (size_t)p * kRowBytes, dst, lane16, (uint32_t)(swz(r) << 4));
-    } else {
-      // positions are consecutive: one base per tile, the row as a byte offset
-      const int first = s_begin + t * kTile;
-      const int row = min(r, s_end - 1 - first);
-      row_to_lds_at(seq + (size_t)first * kRowBytes, (uint32_t)(row * kRowBytes), dst, lane16,
-                    (uint32_t)(swz(r) << 4));
-    }
-  };
-  // rows of tile t that hold a position visible to this subgroup's query (bit r = tile row r)
-  auto valid_rows = [&](int t) -> uint32_t {
-    const int base = s_begin + t * kTile;
-    const int nvalid = my_end - base;
-    uint32_t v = nvalid >= kTile ? 0xffffffffu : (nvalid <= 0 ? 0u : ((1u << nvalid) - 1u));
-    if constexpr (INDEXED) {
+
+  if (wave < 4) {
+    // ======================= score waves =======================
+    const int s = wave;
+    const int c = lane & 15, G = lane >> 4;  // head 16s + c; k / row group G
+    const int h = hg * 64 + 16 * s + c;
+    const float c2 = a.scale_log2;
+    // absorbed query as the B operand: latents 32ks + 8G .. +7
+    bf16x8 qf[16];
+    {
+      const uint16_t* qrow = a.q_abs + ((size_t)bq * a.H + h) * kLatent + 8 * G;
 #pragma unroll
-      for (int r = 0; r < kTile; ++r) {
-        const int p = idx_row[min(base + r, s_end - 1)];
-        if (!(p >= 0 && p < L)) v &= ~(1u << r);
+      for (int ks = 0; ks < 16; ++ks) qf[ks] = *(const bf16x8*)(qrow + 32 * ks);
+    }
+    float m_run = -INFINITY;  // running maximum of scale*log2(e)*score (this lane's head)
+    float l_run = 0.f;        // running sum of 2^(scale*log2(e)*score - m_run)
+    // A operand: MFMA row m = lane & 15 of block blk reads tile row 16 blk + 4(m & 3) + (m >> 2)
+    // (rows transposed within each 16, for which swz(row) = m: the sixteen lanes of a read then
+    // fall in distinct LDS banks), chunk 4ks + G, stored at chunk ^ m =
+    // 16(ks >> 2) + 4((ks & 3) ^ (m >> 2)) + (G ^ (m & 3)).  Result register jj of block blk
+    // therefore holds tile position 16 blk + 4jj + G.
+    const int qk_lane = (4 * (c & 3) + (c >> 2)) * kRowBytes + ((G ^ (c & 3)) << 4);
+    const int qk_hi = c >> 2;
+    wait_vmcnt<0>();
+    __syncthreads();  // the first two tiles have landed (copied by the value waves)
+
+    for (int t = 0; t <= ntiles; ++t) {
+      __syncthreads();  // step t opens: tile t is in LDS; the value waves read P of step t-1
+      if (t == ntiles) break;
+      const uint8_t* rb = smem[t % kRing] + qk_lane;
+      const int hi = opaque(qk_hi);
+      auto rd = [&](int n) {  // n = 2 ks + block
+        const int ks = n >> 1;
+        return *(const bf16x8*)(rb + 16 * kRowBytes * (n & 1) + 256 * (ks >> 2) + (((ks & 3) ^ hi) << 6));
+      };
+      f32x4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      constexpr int kAhead = 7;  // reads in flight ahead of the MFMA that consumes them
+      bf16x8 av[kAhead + 1];
+#pragma unroll
+      for (int n = 0; n < kAhead; ++n) av[n] = rd(n);
+#pragma unroll
+      for (int n = 0; n < 32; ++n) {
+        if (n + kAhead < 32) av[(n + kAhead) % (kAhead + 1)] = rd(n + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        sc[n & 1] = mfma16(av[n % (kAhead + 1)], qf[n >> 1], sc[n & 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    return v;
-  };
-
-  // ---- per-lane LDS addressing (byte offsets inside a stage)
-  // scores: A row = tile row (lane & 31), global chunk 32lh + 2ks + hf; the swizzle flips
-  // its low four bits, so with ks = 8u + v it sits at 32lh + 16u + ((2v + hf) ^ swz(row))
-  const int prow = lane & 31;
-  const int psw = swz(prow);
-  const int qk_base = prow * kRowBytes + 512 * lh;
-  // values: transpose read; group g = lane / 16 supplies tile rows trow + 8r2 (+16ks),
-  // trow = 4(g/2) + e, and latent columns 256lh + 32mb + 16(g&1) + 4c: global chunk
-  // 32lh + 16(mb>>2) + 4(mb&3) + x with x = 2(g&1) + c/2.  For rows trow + 8r2 the swizzle is
-  // 4 fh + fl(r2) with fh = trow & 3 and fl(r2) = ((trow >> 2) + 2 r2) & 3, so the chunk sits at
-  // 32lh + 16(mb>>2) + 4((mb&3) ^ fh) + (x ^ fl(r2)).
-  const int g = lane >> 4, ip = lane & 15, te = ip >> 2, tc = ip & 3;
-  const int trow = 4 * (g >> 1) + te;
-  const int tx = 2 * (g & 1) + (tc >> 1);
-  const int tfh = trow & 3;
-  const int tr_b0 = trow * kRowBytes + 512 * lh + ((tx ^ ((trow >> 2) & 3)) << 4) + ((tc & 1) << 3);
-  const int tr_b1 = (trow + 8) * kRowBytes + 512 * lh + ((tx ^ (((trow >> 2) + 2) & 3)) << 4) + ((tc & 1) << 3);
-
-  // partial scores of tile t over this wave's 256 latents: sixteen k-steps in pairs (the
-  // other wave on the SIMD covers the read latency)
-  // With ks = 8u + v, the chunk offset ((2v + hf) ^ psw) << 4 equals ((v ^ p7) << 5) + x16,
-  // p7 = psw >> 1, x16 = (hf ^ (psw & 1)) << 4: one xor and one shift-add per v on top of a
-  // per-tile base, the 256-byte step of u folded into the instruction offset.
-  const int qk_p7 = psw >> 1;
-  const int qk_lane = qk_base + ((hf ^ (psw & 1)) << 4);
-  // dma >= 0: also copy this wave's eight rows of tile `dma`, one row per two MFMAs; the
-  // reads run three MFMAs ahead
-  auto scores = [&](const uint8_t* tile, f32x16& sc, int dma) {
-    const int p7 = opaque(qk_p7);
-    const uint8_t* rb = tile + qk_lane;
-    auto rd = [&](int ks) { return *(const bf16x8*)(rb + 256 * (ks >> 3) + (((ks & 7) ^ p7) << 5)); };
+      // lane holds positions 16 blk + 4jj + G of head c; mask those past the visible set
+      float v[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) sc[k] = 0.f;
-    bf16x8 av[4];
-    av[0] = rd(0);
-    av[1] = rd(1);
-    av[2] = rd(2);
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      if (ks + 3 < 16) av[(ks + 3) % 4] = rd(ks + 3);
-      if ((ks & 1) == 0 && dma >= 0) issue_row(dma, ks >> 1);
-      __builtin_amdgcn_sched_barrier(0);
-      sc = mfma32(av[ks % 4], qf[ks], sc);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // add the partner's partial (same heads, other latents) and mask rows past the visible set
-  auto complete_scores = [&](f32x16& sc, uint32_t valid) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const f32x4 x = xbuf[sg][w4 ^ 2][k][lane];
-      sc[4 * k] += x[0];
-      sc[4 * k + 1] += x[1];
-      sc[4 * k + 2] += x[2];
-      sc[4 * k + 3] += x[3];
-    }
-    if (valid != 0xffffffffu) {
-      const uint32_t vb = valid >> (4 * hf);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (!((vb >> (8 * ii + j)) & 1u)) sc[4 * ii + j] = -INFINITY;
-    }
-  };
-  // online softmax of one tile's scores (lane column = head h0+hl; rows 8ii + 4hf + j are
-  // tile positions); returns P^T as the B operand of the value MFMAs: k-slot e < 4 is
-  // position 16ks + 4hf + e, e >= 4 is 16ks + 8 + 4hf + e - 4
-  auto softmax = [&](const f32x16& sc, bf16x8 (&pf)[2]) {
-    // reductions as trees: four dependent steps instead of fifteen
-    float mx[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) mx[k] = fmaxf(sc[k], sc[k + 8]);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) mx[k] = fmaxf(mx[k], mx[k + 4]);
-    float tmax = fmaxf(fmaxf(mx[0], mx[2]), fmaxf(mx[1], mx[3]));
-    tmax = half_swap_max(tmax) * c2;  // scale > 0 keeps the order
-    const float m_new = fmaxf(m_run, tmax);
-    const bool need = m_new > m_run + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_use = need ? m_new : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
-      l_run *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
-      m_run = m_use;
-    }
-    const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
-    float p[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[k], c2, -msafe));
-    float ps[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ps[k] = p[k] + p[k + 8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ps[k] = ps[k] + ps[k + 4];
-    l_run += half_swap_sum((ps[0] + ps[2]) + (ps[1] + ps[3]));
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)p[4 * (2 * ks + (e >> 2)) + (e & 3)];
-  };
-  // values: O^T += C^T . P^T, A from the transpose read of the tile; MFMA n covers latent
-  // block mb = n & 7 and k-step ks = n >> 3, its reads issued two MFMAs ahead
-  auto values = [&](const uint8_t* tile, const bf16x8 (&pf)[2]) {
-    const int fh = opaque(tfh);
-    const uint8_t* t0 = tile + tr_b0;
-    const uint8_t* t1 = tile + tr_b1;
-    s16x4 tv[2][2];
-    auto load = [&](int n, int slot) {
-      const int ks = n >> 3, mb = n & 7;
-      const int sh = 256 * (mb >> 2) + 64 * ((mb & 3) ^ fh) + (16 * ks) * kRowBytes;
-      tv[slot][0] = lds_read_tr16(t0 + sh);
-      tv[slot][1] = lds_read_tr16(t1 + sh);
-    };
-    load(0, 0);
-#pragma unroll
-    for (int n = 0; n < 16; ++n) {
-      if (n + 1 < 16) load(n + 1, (n + 1) % 2);
-      __builtin_amdgcn_sched_barrier(0);
-      o[n & 7] = mfma32(concat_bf16(tv[n % 2][0], tv[n % 2][1]), pf[n >> 3], o[n & 7]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // ---- the interval loop.  One barrier opens every interval.  Subgroup sg runs phase A of
-  // its j-th tile in interval 2j + sg and phase B in the next one; its j-th tile is tile j
-  // (PAIR) or tile 2j + sg.  Tile t is first used in interval t (alternating tiles) or 2t
-  // (PAIR).  The waves in phase A copy the tile two ahead of theirs, into the stage whose
-  // last use ended with the previous interval: alternating, subgroup k&1 copies tile k+2 in
-  // interval k; PAIR, subgroup 0 copies tile m+2 in interval 2m.  A copying wave waits for
-  // its own rows of a tile just before the interval that first uses it opens.
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    if (t < ntiles)
-#pragma unroll
-      for (int rr = 0; rr < kRowsPerWave / 2; ++rr) {
-        // both subgroups share the first two copies: wave w takes rows 4w .. 4w+3
-        const int r = wave * (kRowsPerWave / 2) + rr;
-        const int slot = s_begin + t * kTile + r;
-        int p;
+      for (int k = 0; k < 8; ++k) v[k] = sc[k >> 2][k & 3];
+      {
+        const int base = s_begin + t * kTile;
+        const int nvalid = s_end - base;
+        uint32_t valid = nvalid >= kTile ? 0xffffffffu : ((1u << nvalid) - 1u);
         if constexpr (INDEXED) {
-          p = idx_row[min(slot, s_end - 1)];
-          p = (p >= 0 && p < L) ? p : 0;
-        } else {
-          p = min(slot, s_end - 1);
+#pragma unroll
+          for (int r = 0; r < kTile; ++r) {
+            const int p = idx_row[min(base + r, s_end - 1)];
+            if (!(p >= 0 && p < L)) valid &= ~(1u << r);
+          }
         }
-        row_to_lds(seq + (size_t)p * kRowBytes, lds0 + t * kTileBytes + r * kRowBytes, lane16,
-                   (uint32_t)(swz(r) << 4));
+        if (valid != 0xffffffffu) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (!((valid >> (16 * (k >> 2) + 4 * (k & 3) + G)) & 1u)) v[k] = -INFINITY;
+        }
       }
-  // waiting for the query loads and the first copies here leaves the loop's waits counting
-  // tile copies only (the compiler's own wait for the query registers is then satisfied)
-  wait_vmcnt<0>();
-  auto open_interval = [&](int k) {
-    if constexpr (PAIR) {
-      const int m = k >> 1;  // tile first used now (k even); subgroup 0 copied it in interval k-4
-      if (sg == 0 && (k & 1) == 0 && m < ntiles) {
-        if (m + 1 < ntiles) wait_vmcnt<kRowsPerWave>();  // tile m+1 (interval k-2) may stay in flight
+      // online softmax (scale > 0 keeps the order of the maxima)
+      float tmax = fmaxf(fmaxf(fmaxf(v[0], v[4]), fmaxf(v[1], v[5])), fmaxf(fmaxf(v[2], v[6]), fmaxf(v[3], v[7])));
+      tmax = quad_max(tmax) * c2;
+      const float m_new = fmaxf(m_run, tmax);
+      const bool need = m_new > m_run + kRescaleLog2;
+      float alpha = 1.f;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_use = need ? m_new : m_run;
+        alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
+        l_run *= alpha;
+        m_run = m_use;
+      }
+      const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
+      float p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -msafe));
+      l_run += quad_sum(((p[0] + p[4]) + (p[1] + p[5])) + ((p[2] + p[6]) + (p[3] + p[7])));
+      // P in bf16: head row 16s + c, positions 16 blk + 4jj + G
+      __bf16* prow = (__bf16*)(pbuf[t & 1] + (16 * s + c) * kPStride) + G;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) prow[16 * (k >> 2) + 4 * (k & 3)] = (__bf16)p[k];
+      if (G == 0) abuf[t & 1][16 * s + c] = alpha;
+    }
+    if (G == 0) {
+      mlbuf[0][16 * s + c] = m_run;
+      mlbuf[1][16 * s + c] = l_run;
+    }
+    __syncthreads();  // (m, l) are posted
+  } else {
+    // ======================= value waves =======================
+    const int v = wave - 4;
+    const int vh = v >> 2, lq = v & 3;  // heads 32vh .., latents 128lq ..
+    const int hl = lane & 31, hf = lane >> 5;
+    // tile copies: rows 4v .. 4v+3 of a tile
+    auto issue_row = [&](int t, int rr) {
+      const int r = kRowsPerVWave * v + rr;
+      const int slot = s_begin + t * kTile + r;
+      const uint32_t dst = lds0 + (t % kRing) * kTileBytes + r * kRowBytes;
+      if constexpr (INDEXED) {
+        int p = idx_row[min(slot, s_end - 1)];
+        p = (p >= 0 && p < L) ? p : 0;
+        row_to_lds(seq + (size_t)p * kRowBytes, dst, lane16, (uint32_t)(swz(r) << 4));
+      } else {
+        const int first = s_begin + t * kTile;
+        const int row = min(r, s_end - 1 - first);
+        row_to_lds_at(seq + (size_t)first * kRowBytes, (uint32_t)(row * kRowBytes), dst, lane16,
+                      (uint32_t)(swz(r) << 4));
+      }
+    };
+    // Every row read is a visible row: rows past the split repeat its last row and indexed
+    // slots naming a position outside the cache read row 0; the score waves mask both out.
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (t < ntiles)
+#pragma unroll
+        for (int rr = 0; rr < kRowsPerVWave; ++rr) issue_row(t, rr);
+
+    // transpose reads for the A operand (lane l: latent l % 32 of a 32-latent block, positions
+    // 8(l/32) .. +7 of a 16-position k-step): in each 16-lane group g, lane 4e + q names tile
+    // row base + e, latents 16(g&1) + 4q .. +3, and receives latent 16(g&1) + (lane & 15) of
+    // rows base .. base+3; rows 8(g>>1) + e (k-slots 0-3) and +4 (k-slots 4-7).  With the
+    // swizzle swz(r) = 4(r & 3) + ((r >> 2) & 3), latent block mb of quarter lq sits at byte
+    // 256lq + 64(mb ^ e) + 16(x ^ f) + 8(q & 1), x = 2(g&1) + (q >> 1), f = (row >> 2) & 3.
+    const int g = lane >> 4, ip = lane & 15, te = ip >> 2, tq = ip & 3;
+    const int x = 2 * (g & 1) + (tq >> 1);
+    const int row0 = 8 * (g >> 1) + te, row1 = row0 + 4;
+    const int tb0 = row0 * kRowBytes + 256 * lq + ((x ^ ((row0 >> 2) & 3)) << 4) + ((tq & 1) << 3);
+    const int tb1 = row1 * kRowBytes + 256 * lq + ((x ^ ((row1 >> 2) & 3)) << 4) + ((tq & 1) << 3);
+    const int hv = hg * 64 + 32 * vh + hl;  // this lane's head (output column)
+
+    f32x16 o[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) o[mb][k] = 0.f;
+    wait_vmcnt<0>();
+    __syncthreads();  // the first two tiles have landed
+
+    for (int t = 0; t <= ntiles; ++t) {
+      // tile t (copied in step t-2) must have landed before step t opens; tile t+1 may stay in flight
+      if (t < ntiles) {
+        if (t + 1 < ntiles) wait_vmcnt<kRowsPerVWave>();
         else wait_vmcnt<0>();
       }
-    } else {
-      // tile k, copied in interval k-2 by subgroup k&1, which has copied nothing since
-      if (sg == (k & 1) && k < ntiles) wait_vmcnt<0>();
-    }
-    __syncthreads();  // the copies are visible to all; the previous interval is done
-  };
-  // both subgroups pass the same number of barriers: J iterations of two, plus one
-  const int J = PAIR ? ntiles : (ntiles + 1) / 2;
-  if (sg == 1) open_interval(0);
-  for (int j = 0; j < J; ++j) {
-    const int t = PAIR ? j : 2 * j + sg;
-    const bool have = active && t < ntiles;
-    const uint8_t* tile = smem[t % kRing];
-    open_interval(2 * j + sg);
-    f32x16 s;
-    if (have) {
-      const bool copies = PAIR ? sg == 0 : true;
-      scores(tile, s, (copies && t + 2 < ntiles) ? t + 2 : -1);
+      __syncthreads();  // step t opens
+      const int cp = t + 2;  // tile copied in this step, into the stage of tile t-2
+      if (t == 0) {
+        if (cp < ntiles)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        xbuf[sg][w4][q][lane] = (f32x4){s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
-    }
-    open_interval(2 * j + sg + 1);
-    if (have) {
-      complete_scores(s, valid_rows(t));
+          for (int rr = 0; rr < kRowsPerVWave; ++rr) issue_row(cp, rr);
+        continue;
+      }
+      const int tv_ = t - 1;  // tile whose values this step accumulates
+      const float alpha = abuf[tv_ & 1][32 * vh + hl];
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) o[mb] *= alpha;
+      }
       bf16x8 pf[2];
-      softmax(s, pf);
-      values(tile, pf);
-    }
-  }
-  if (sg == 0) open_interval(2 * J);
-
-  // ---- results: lane holds head h0+hl, latents 256lh + 32mb + 8ii + 4hf + j
-  const int h = h0 + hl;
-  // MBLO: first latent block written (a compile-time constant: the accumulator array must be
-  // indexed by constants to stay in registers)
-  auto write_out = [&](auto mblo_c, bool write_ml) {
-    constexpr int mb_lo = decltype(mblo_c)::value;
-    if (a.num_splits == 1) {
-      const float inv_l = 1.0f / l_run;
-      float* orow = a.o_lat + ((size_t)bq * a.H + h) * kLatent + 256 * lh + 4 * hf;
 #pragma unroll
-      for (int mb = mb_lo; mb < mb_lo + (PAIR ? 8 : 4); ++mb)
+      for (int ks = 0; ks < 2; ++ks)
+        pf[ks] = *(const bf16x8*)(pbuf[tv_ & 1] + (32 * vh + hl) * kPStride + 32 * ks + 16 * hf);
+      const uint8_t* tile = smem[tv_ % kRing];
+      const int fh = opaque(te);
+      const uint8_t* t0 = tile + tb0;
+      const uint8_t* t1 = tile + tb1;
+      constexpr int kAhead = 3;  // MFMAs whose reads are in flight ahead of the current one
+      s16x4 tv[kAhead + 1][2];
+      auto load = [&](int n, int slot) {  // n = 4 ks + mb
+        const int sh = 64 * ((n & 3) ^ fh) + 16 * kRowBytes * (n >> 2);
+        tv[slot][0] = lds_read_tr16(t0 + sh);
+        tv[slot][1] = lds_read_tr16(t1 + sh);
+      };
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          f32x4 v = {o[mb][4 * ii] * inv_l, o[mb][4 * ii + 1] * inv_l, o[mb][4 * ii + 2] * inv_l,
-                     o[mb][4 * ii + 3] * inv_l};
-          *(f32x4*)(orow + 32 * mb + 8 * ii) = v;
-        }
-      // __builtin_amdgcn_logf is the hardware base-2 logarithm
-      if (write_ml && a.lse != nullptr && hf == 0 && lh == 0)
-        a.lse[(size_t)bq * a.H + h] = (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f;
-    } else {
-      const size_t prow_idx = ((size_t)split * a.B * a.Q + bq) * a.H + h;
-      float* orow = a.part_o + prow_idx * kLatent + 256 * lh + 4 * hf;
+      for (int n = 0; n < kAhead; ++n) load(n, n);
 #pragma unroll
-      for (int mb = mb_lo; mb < mb_lo + (PAIR ? 8 : 4); ++mb)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          f32x4 v = {o[mb][4 * ii], o[mb][4 * ii + 1], o[mb][4 * ii + 2], o[mb][4 * ii + 3]};
-          *(f32x4*)(orow + 32 * mb + 8 * ii) = v;
-        }
-      if (write_ml && hf == 0 && lh == 0) {
-        a.part_ml[2 * prow_idx] = m_run;
-        a.part_ml[2 * prow_idx + 1] = l_run;
+      for (int n = 0; n < 8; ++n) {
+        if (n + kAhead < 8) load(n + kAhead, (n + kAhead) % (kAhead + 1));
+        if ((n & 1) == 0 && cp < ntiles) issue_row(cp, n >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+        o[n & 3] = mfma32(concat_bf16(tv[n % (kAhead + 1)][0], tv[n % (kAhead + 1)][1]), pf[n >> 2], o[n & 3]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-  };
-  if constexpr (PAIR) {
-    if (active) write_out(std::integral_constant<int, 0>{}, true);
-  } else {
-    // merge the two subgroups' partial softmaxes (same query, heads and latents, disjoint
-    // tiles): subgroup 0 finishes latent blocks mb 0-3, subgroup 1 blocks 4-7; each hands the
-    // other its half through the (now free) tile ring, and (m, l) through the exchange buffer
-    __syncthreads();
-    f32x4* xo = (f32x4*)&smem[0][0];  // [w4][subgroup][16][64] f32x4 = 128 KiB
-    float* xml = (float*)&xbuf[0][0][0][0];
-    const int other = sg ^ 1;
-    // GIVE: the blocks handed over; TAKE: the blocks finished here
-    auto merge = [&](auto give_c) {
-      constexpr int give = decltype(give_c)::value, take = 4 - give;
+    __syncthreads();  // (m, l) are posted
+    const float m_fin = mlbuf[0][32 * vh + hl];
+    const float l_fin = mlbuf[1][32 * vh + hl];
+    // lane holds head hv, latents 128lq + 32mb + 8ii + 4hf + j
+    if (a.num_splits == 1) {
+      const float inv_l = 1.0f / l_fin;
+      float* orow = a.o_lat + ((size_t)bq * a.H + hv) * kLatent + 128 * lq + 4 * hf;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          xo[((w4 * 2 + sg) * 16 + 4 * mb + q) * 64 + lane] =
-              (f32x4){o[give + mb][4 * q], o[give + mb][4 * q + 1], o[give + mb][4 * q + 2], o[give + mb][4 * q + 3]};
-      xml[wave * 64 + lane] = m_run;
-      xml[512 + wave * 64 + lane] = l_run;
-      __syncthreads();
-      const float m_o = xml[(other * 4 + w4) * 64 + lane];
-      const float l_o = xml[512 + (other * 4 + w4) * 64 + lane];
-      const float M = fmaxf(m_run, m_o);
-      const float ws = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-      const float wo = m_o == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_o - M);
+        for (int ii = 0; ii < 4; ++ii)
+          *(f32x4*)(orow + 32 * mb + 8 * ii) = (f32x4){o[mb][4 * ii] * inv_l, o[mb][4 * ii + 1] * inv_l,
+                                                      o[mb][4 * ii + 2] * inv_l, o[mb][4 * ii + 3] * inv_l};
+      // __builtin_amdgcn_logf is the hardware base-2 logarithm
+      if (a.lse != nullptr && hf == 0 && lq == 0)
+        a.lse[(size_t)bq * a.H + hv] = (m_fin + __builtin_amdgcn_logf(l_fin)) * 0.69314718055994531f;
+    } else {
+      const size_t prow_idx = ((size_t)split * a.B * a.Q + bq) * a.H + hv;
+      float* orow = a.part_o + prow_idx * kLatent + 128 * lq + 4 * hf;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 x = xo[((w4 * 2 + other) * 16 + 4 * mb + q) * 64 + lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[take + mb][4 * q + e] = o[take + mb][4 * q + e] * ws + x[e] * wo;
-        }
-      l_run = l_run * ws + l_o * wo;
-      m_run = M;
-      write_out(std::integral_constant<int, take>{}, give == 4);
-    };
-    if (sg == 0)
-      merge(std::integral_constant<int, 4>{});
-    else
-      merge(std::integral_constant<int, 0>{});
+        for (int ii = 0; ii < 4; ++ii)
+          *(f32x4*)(orow + 32 * mb + 8 * ii) =
+              (f32x4){o[mb][4 * ii], o[mb][4 * ii + 1], o[mb][4 * ii + 2], o[mb][4 * ii + 3]};
+      if (hf == 0 && lq == 0) {
+        a.part_ml[2 * prow_idx] = m_fin;
+        a.part_ml[2 * prow_idx + 1] = l_fin;
+      }
+    }
   }
 }
 
@@ -469,13 +365,7 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) { merge_row(a,
 hipError_t launch_latent_attn(const AttnArgs& a, bool indexed, hipStream_t stream) {
   void* args[] = {const_cast<AttnArgs*>(&a)};
   const dim3 grid(a.total_wg), block(kThreads);
-  const void* k;
-  if (indexed)
-    k = (const void*)&latent_attn_kernel<true, false>;
-  else if (a.q_units < a.Q)
-    k = (const void*)&latent_attn_kernel<false, true>;
-  else
-    k = (const void*)&latent_attn_kernel<false, false>;
+  const void* k = indexed ? (const void*)&latent_attn_kernel<true> : (const void*)&latent_attn_kernel<false>;
   return hipLaunchKernel(k, grid, block, args, 0, stream);
 }
 

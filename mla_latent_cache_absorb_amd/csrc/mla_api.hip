@@ -69,7 +69,7 @@ int32_t split_length(int32_t max_positions, int32_t s) {
 bool supported(int32_t H, int32_t D, int32_t R) { return R == 512 && D == 256 && H > 0 && H % 64 == 0; }
 
 // queries handled by one workgroup: two for dense multi-query calls, else one
-int32_t queries_per_unit(int32_t Q, bool indexed) { return (!indexed && Q > 1) ? 2 : 1; }
+int32_t queries_per_unit(int32_t, bool) { return 1; }
 
 int resolve_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions, int32_t num_splits, int cus,
                    bool indexed) {
