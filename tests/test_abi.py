@@ -87,10 +87,10 @@ def test_split_sizing(L):
 
 
 def test_split_choice_without_device(L):
-    # with no GPU visible the choice assumes 256 CUs: bandwidth-bound calls (one query, or
-    # index lists) get one workgroup per CU, dense multi-query calls two
+    # with no GPU visible the choice assumes 256 CUs, one workgroup per CU: whole rounds of
+    # workgroups, as few splits (partials) as that allows
     assert binding.mla_latent_attn_num_splits(32, 1, 64, 8192, 0) == 8          # 256 workgroups
     assert binding.mla_latent_attn_num_splits(4, 1, 64, 131072, 0) == 64        # 256 workgroups
-    assert binding.mla_latent_attn_num_splits(16, 6, 64, 32768, 0) == 5         # 480 workgroups
+    assert binding.mla_latent_attn_num_splits(16, 6, 64, 32768, 0) == 8         # 768 = 3 rounds
     assert binding.mla_latent_attn_num_splits(32, 4, 64, 2052, 0, indexed=True) == 2
     assert binding.mla_latent_attn_workspace_size(32, 4, 64, 512, 2052, 0, indexed=True) == 2 * 128 * 64 * 514 * 4
