@@ -217,10 +217,26 @@ void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -msafe));
       l_run += quad_sum(((p[0] + p[4]) + (p[1] + p[5])) + ((p[2] + p[6]) + (p[3] + p[7])));
-      // P in bf16: head row 16s + c, positions 16 blk + 4jj + G
-      __bf16* prow = (__bf16*)(pbuf[t & 1] + (16 * s + c) * kPStride) + G;
+      // P in bf16: head row 16s + c.  Lane G holds positions 16 blk + 4jj + G; a 4 x 4
+      // transpose across the lanes G = 0..3 of head c (pairs G^1 swapped first, then G^2) gives
+      // it positions 16 blk + 4G + jj, four consecutive entries of the row
+      uint8_t* prow = pbuf[t & 1] + (16 * s + c) * kPStride + 8 * G;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) prow[16 * (k >> 2) + 4 * (k & 3)] = (__bf16)p[k];
+      for (int blk = 0; blk < 2; ++blk) {
+        unsigned u[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) u[jj] = __builtin_bit_cast(unsigned, p[4 * blk + jj]);
+        auto r01 = __builtin_amdgcn_permlane16_swap(u[0], u[1], false, false);
+        auto r23 = __builtin_amdgcn_permlane16_swap(u[2], u[3], false, false);
+        auto r02 = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
+        auto r13 = __builtin_amdgcn_permlane32_swap(r01[1], r23[1], false, false);
+        s16x4 pv;
+        pv[0] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[0]));
+        pv[1] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[0]));
+        pv[2] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[1]));
+        pv[3] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[1]));
+        *(s16x4*)(prow + 32 * blk) = pv;
+      }
       if (G == 0) abuf[t & 1][16 * s + c] = alpha;
     }
     if (G == 0) {
