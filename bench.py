@@ -160,6 +160,67 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
     return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, splits=splits, workload=w0)
 
 
+def time_indexer(name: str, steps: int, warmup: int):
+    """The k-pooled indexer on the sequences of `name`: pooled keys (full build), pool scores for
+    all queries, top-k selection into position lists; per-kernel times from HIP events on the
+    launch stream."""
+    import numpy as np
+    import torch
+    from mla_latent_cache_absorb_amd import binding, workloads as wl
+
+    dev = torch.device("cuda:0")
+    spec = wl.WORKLOADS[name]
+    lens = wl.cache_lengths(spec)
+    ix = wl.make_indexer_inputs(spec, lens)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, g = bf(ix.q), bf(ix.k), bf(ix.g)
+    cl = torch.from_numpy(lens).to(dev)
+    Lmax = int(spec.cache_len)
+    B, Q, d = ix.q.shape
+    max_pools = Lmax // ix.pool
+    pooled = torch.empty((B, max_pools, d), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, Q, max_pools), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Q, ix.topk + ix.pool - 1), dtype=torch.int32, device=dev)
+    idx_len = torch.empty((B, Q), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        binding.mla_kpool_keys(k, g, cl, Lmax, ix.pool, pooled=pooled)
+        if ev is not None:
+            ev[1].record(stream)
+        binding.mla_indexer_scores(q, pooled, cl, Lmax, ix.pool, scores=scores)
+        if ev is not None:
+            ev[2].record(stream)
+        binding.mla_indexer_select(scores, cl, Lmax, ix.pool, ix.topk, True, idx=idx, idx_len=idx_len)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    stage = {kname: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+             for j, kname in enumerate(("kpool_keys", "scores", "select"))}
+    npools = (lens // ix.pool).astype(np.int64)
+    # algorithmic bytes of the score kernel: every pooled key read once per sequence, one score
+    # written per (query, pool)
+    score_bytes = int(npools.sum()) * d * 4 + int(npools.sum()) * Q * 4
+    achieved = score_bytes / (stage["scores"] * 1e-3) / 1e9
+    return {
+        "workload": name, "pool": ix.pool, "topk": ix.topk, "dim": d, "queries": B * Q,
+        "stages_ms": {kname: round(v, 6) for kname, v in stage.items()},
+        "ms_per_step": round(sum(stage.values()), 6),
+        "roofline": {"kernel": "score_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": score_bytes, "avg_launch_ms": round(stage["scores"], 6)},
+    }
+
+
 def cpu_baseline(name: str, budget_s: float = 12.0):
     """The fp64 oracle (expanded form) on whole sequences of the same workload, until about
     budget_s of CPU time has been spent."""
@@ -193,6 +254,9 @@ def main():
     ap.add_argument("--workload", default="decode_b32_l8192")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-indexer", action="store_true")
+    ap.add_argument("--indexer-only", action="store_true",
+                    help="time only the k-pooled indexer (for profiling it on its own)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device three times (a plain copy of known size, "
                          "so that hardware byte counters can be scaled)")
@@ -221,6 +285,10 @@ def main():
         log(f"[bench] copied {args.calibrate_copy} MiB three times")
         del src, dst
         torch.cuda.empty_cache()
+    if args.indexer_only:
+        print(json.dumps({"indexer": time_indexer("indexed_verify_b32_q4_ragged", args.steps, args.warmup)}),
+              flush=True)
+        return
     r = time_path(args.workload, args.steps, args.warmup, NSETS)
     w = r["workload"]
     B, Q, H, D = w.q.shape
@@ -267,6 +335,10 @@ def main():
             "frac": round(tf / BF16_PEAK_TFLOPS, 4), "attn_flops": flops,
             "ms_per_step": round(s["ms_step"], 6), "stages_ms": {k: round(v, 6) for k, v in s["stage_ms"].items()},
             "splits": s["splits"]}
+    if not args.no_indexer:
+        torch.cuda.empty_cache()
+        log("[bench] timing the k-pooled indexer")
+        result["indexer"] = time_indexer("indexed_verify_b32_q4_ragged", max(5, args.steps // 5), 3)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(args.workload)

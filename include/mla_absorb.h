@@ -148,6 +148,62 @@ int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* cache, int64_
                             float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * k-pooled sparse-attention indexer: the three steps that turn indexer keys into the position
+ * lists mla_latent_attn_indexed consumes (colibri "GLM-5.3-Flash engine", "Architecture notes",
+ * "DSA with k-pooling": keys are grouped into pools, a pool's key is a per-channel softmax
+ * mixture of its members, only complete and causally visible pools are selectable, the
+ * incomplete tail is appended, ties go to the lower index; page "Module 08", section 3: after a
+ * rollback the selection is rebuilt under the same pool-completion rule, which a smaller
+ * cache_len gives).  Pool p holds positions p*pool .. p*pool + pool - 1 of its sequence.
+ *
+ * mla_kpool_keys: pooled[b][p][c] = sum_s w[s][c] * k[b][p*pool + s][c] with
+ * w[.][c] = softmax over s of g[b][p*pool + s][c] (fp32), for every complete pool
+ * p < min(cache_len[b], max_cache_len) / pool at or after pool_begin[b].
+ *   k, g         bf16 rows of d values; row j of sequence b at (k|g) + b*batch_stride + j*d;
+ *                batch_stride (elements) >= max_cache_len * d; rows past cache_len are never read
+ *   cache_len    [B] int32 (device)
+ *   pool_begin   [B] int32 (device) first pool to build (pools before it are left as they are,
+ *                so an append after new positions only builds the pools they complete), or
+ *                NULL for 0
+ *   d            64, 128 or 256;  pool >= 1;  max_pools >= max_cache_len / pool
+ *   pooled       [B][max_pools][d] fp32 output (caller-owned)
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ARG, MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_kpool_keys(const uint16_t* k, const uint16_t* g, int64_t batch_stride, const int32_t* cache_len,
+                   const int32_t* pool_begin, int32_t B, int32_t max_cache_len, int32_t d, int32_t pool,
+                   float* pooled, int32_t max_pools, void* stream);
+
+/*
+ * mla_indexer_scores: scores[b][i][p] = q[b][i] . pooled[b][p] (fp32, channels summed in
+ * order), for every complete pool of sequence b.
+ *   q        [B][Q][d] bf16 indexer queries; 1 <= Q <= 8
+ *   pooled   [B][max_pools][d] fp32 from mla_kpool_keys
+ *   scores   [B][Q][max_pools] fp32 output; entries of incomplete pools are not written
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (Q or d out of range), MLA_ERR_ARG, MLA_ERR_DEVICE,
+ * MLA_ERR_HIP.
+ */
+int mla_indexer_scores(const uint16_t* q, const float* pooled, const int32_t* cache_len, int32_t B, int32_t Q,
+                       int32_t d, int32_t pool, int32_t max_pools, int32_t max_cache_len, float* scores,
+                       void* stream);
+
+/*
+ * mla_indexer_select: for query i of sequence b, at position t = cache_len[b] - Q + i, the
+ * topk / pool highest-scoring pools whose last position is <= t (ties: the lower pool first;
+ * all of them when there are fewer), in ascending order and expanded to their positions, then
+ * (tail != 0) the positions floor((t+1)/pool)*pool .. t of the incomplete pool.
+ *   scores   [B][Q][max_pools] fp32 (mla_indexer_scores); max_pools <= 16384
+ *   topk     positions selected before the tail: a positive multiple of pool
+ *   idx      [B][Q][K_max] int32 output, ascending positions, unused slots -1;
+ *            K_max >= topk + pool - 1 with the tail (topk without)
+ *   idx_len  [B][Q] int32 output: entries used
+ * The selection is exact integer work on the fp32 scores and deterministic.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ARG, MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_indexer_select(const float* scores, const int32_t* cache_len, int32_t B, int32_t Q, int32_t pool,
+                       int32_t max_pools, int32_t max_cache_len, int32_t topk, int32_t tail, int32_t* idx,
+                       int32_t* idx_len, int32_t K_max, void* stream);
+
+/*
  * Value up-projection (page "Module 05", section 3: U_h^V factors out of the sum over
  * history, so the accumulated latent is expanded once, at the end).
  *   o_lat  [rows][H][R] fp32   accumulated latents (mla_latent_attn)

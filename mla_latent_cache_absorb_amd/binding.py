@@ -24,7 +24,8 @@ MLA_ERR_HIP = -5
 MLA_ERR_DEVICE = -6
 
 EXPORTS = ("mla_status_string", "mla_absorb_q", "mla_latent_attn_num_splits", "mla_latent_attn_workspace_size",
-           "mla_latent_attn", "mla_latent_attn_indexed", "mla_up_v")
+           "mla_latent_attn", "mla_latent_attn_indexed", "mla_up_v", "mla_kpool_keys", "mla_indexer_scores",
+           "mla_indexer_select")
 
 
 class MlaError(RuntimeError):
@@ -59,6 +60,12 @@ def lib() -> ctypes.CDLL:
         L.mla_latent_attn_indexed.restype = ctypes.c_int
         L.mla_up_v.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
         L.mla_up_v.restype = ctypes.c_int
+        L.mla_kpool_keys.argtypes = [vp, vp, i64, vp, vp, i32, i32, i32, i32, vp, i32, vp]
+        L.mla_kpool_keys.restype = ctypes.c_int
+        L.mla_indexer_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+        L.mla_indexer_scores.restype = ctypes.c_int
+        L.mla_indexer_select.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
+        L.mla_indexer_select.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -198,6 +205,78 @@ def mla_up_v(o_lat: torch.Tensor, w_v: torch.Tensor, out: Optional[torch.Tensor]
     _need(out, torch.float32, "out")
     _check(lib().mla_up_v(_ptr(o_lat), _ptr(w_v), _ptr(out), rows, H, D, R, _stream(stream)), "mla_up_v")
     return out
+
+
+# ---------------------------------------------------------------------------- k-pooled indexer
+def _rows(t: torch.Tensor, name: str):
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [B, L, d] with contiguous rows")
+    return int(t.stride(0))
+
+
+def mla_kpool_keys(k: torch.Tensor, g: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int, pool: int,
+                   pooled: Optional[torch.Tensor] = None, max_pools: Optional[int] = None, pool_begin=None,
+                   stream=None) -> torch.Tensor:
+    """k, g [B, L, d] bf16 (indexer keys, gate logits) -> pooled [B, max_pools, d] fp32."""
+    _need(k, torch.bfloat16, "k", contiguous=False)
+    _need(g, torch.bfloat16, "g", contiguous=False)
+    _need(cache_len, torch.int32, "cache_len")
+    B, _, d = k.shape
+    stride = _rows(k, "k")
+    if _rows(g, "g") != stride or g.shape != k.shape:
+        raise ValueError("g must have the layout of k")
+    if max_pools is None:
+        max_pools = max(1, max_cache_len // pool)
+    if pooled is None:
+        pooled = torch.empty((B, max_pools, d), dtype=torch.float32, device=k.device)
+    _need(pooled, torch.float32, "pooled")
+    if pool_begin is not None:
+        _need(pool_begin, torch.int32, "pool_begin")
+    _check(lib().mla_kpool_keys(_ptr(k), _ptr(g), stride, _ptr(cache_len), _ptr(pool_begin), B, int(max_cache_len),
+                                d, int(pool), _ptr(pooled), int(max_pools), _stream(stream)), "mla_kpool_keys")
+    return pooled
+
+
+def mla_indexer_scores(q: torch.Tensor, pooled: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int,
+                       pool: int, scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q [B, Q, d] bf16, pooled [B, max_pools, d] fp32 -> scores [B, Q, max_pools] fp32."""
+    _need(q, torch.bfloat16, "q")
+    _need(pooled, torch.float32, "pooled")
+    B, Q, d = q.shape
+    max_pools = pooled.shape[1]
+    if scores is None:
+        scores = torch.empty((B, Q, max_pools), dtype=torch.float32, device=q.device)
+    _need(scores, torch.float32, "scores")
+    _check(lib().mla_indexer_scores(_ptr(q), _ptr(pooled), _ptr(cache_len), B, Q, d, int(pool), max_pools,
+                                    int(max_cache_len), _ptr(scores), _stream(stream)), "mla_indexer_scores")
+    return scores
+
+
+def mla_indexer_select(scores: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int, pool: int, topk: int,
+                       tail: bool = True, idx: Optional[torch.Tensor] = None, idx_len: Optional[torch.Tensor] = None,
+                       stream=None):
+    """scores [B, Q, max_pools] fp32 -> (idx [B, Q, topk + pool - 1] int32, idx_len [B, Q] int32)."""
+    _need(scores, torch.float32, "scores")
+    B, Q, max_pools = scores.shape
+    K_max = topk + (pool - 1 if tail else 0)
+    if idx is None:
+        idx = torch.empty((B, Q, K_max), dtype=torch.int32, device=scores.device)
+    if idx_len is None:
+        idx_len = torch.empty((B, Q), dtype=torch.int32, device=scores.device)
+    _need(idx, torch.int32, "idx")
+    _need(idx_len, torch.int32, "idx_len")
+    _check(lib().mla_indexer_select(_ptr(scores), _ptr(cache_len), B, Q, int(pool), max_pools, int(max_cache_len),
+                                    int(topk), int(bool(tail)), _ptr(idx), _ptr(idx_len), idx.shape[2],
+                                    _stream(stream)), "mla_indexer_select")
+    return idx, idx_len
+
+
+def mla_indexer(q: torch.Tensor, k: torch.Tensor, g: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int,
+                pool: int, topk: int, tail: bool = True, stream=None):
+    """The three indexer steps: pooled keys -> pool scores -> position lists (idx, idx_len)."""
+    pooled = mla_kpool_keys(k, g, cache_len, max_cache_len, pool, stream=stream)
+    scores = mla_indexer_scores(q, pooled, cache_len, max_cache_len, pool, stream=stream)
+    return mla_indexer_select(scores, cache_len, max_cache_len, pool, topk, tail, stream=stream)
 
 
 def mla_forward(q, w_k, w_v, cache, cache_len, max_cache_len, scale, idx=None, idx_len=None, num_splits=0,

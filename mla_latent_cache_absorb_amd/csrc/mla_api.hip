@@ -217,6 +217,49 @@ int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* cache, int64_
                      max_cache_len, scale, num_splits, o_lat, lse, workspace, workspace_bytes, stream);
 }
 
+int mla_kpool_keys(const uint16_t* k, const uint16_t* g, int64_t batch_stride, const int32_t* cache_len,
+                   const int32_t* pool_begin, int32_t B, int32_t max_cache_len, int32_t d, int32_t pool,
+                   float* pooled, int32_t max_pools, void* stream) {
+  if (!k || !g || !cache_len || !pooled) return MLA_ERR_NULL;
+  if (B < 1 || max_cache_len < 1 || pool < 1 || max_pools < 1) return MLA_ERR_SHAPE;
+  if (!(d == 64 || d == 128 || d == 256)) return MLA_ERR_SHAPE;
+  if (batch_stride < (int64_t)max_cache_len * d) return MLA_ERR_ARG;
+  if (max_pools < max_cache_len / pool) return MLA_ERR_ARG;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  mla::KpoolArgs a{k, g, batch_stride, cache_len, pool_begin, B, max_cache_len, d, pool, max_pools, pooled};
+  return mla::launch_kpool(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_indexer_scores(const uint16_t* q, const float* pooled, const int32_t* cache_len, int32_t B, int32_t Q,
+                       int32_t d, int32_t pool, int32_t max_pools, int32_t max_cache_len, float* scores,
+                       void* stream) {
+  if (!q || !pooled || !cache_len || !scores) return MLA_ERR_NULL;
+  if (B < 1 || Q < 1 || Q > mla::kMaxIndexerQ || pool < 1 || max_pools < 1 || max_cache_len < 1)
+    return MLA_ERR_SHAPE;
+  if (!(d == 64 || d == 128 || d == 256)) return MLA_ERR_SHAPE;
+  if (max_pools < max_cache_len / pool) return MLA_ERR_ARG;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  mla::ScoreArgs a{q, pooled, cache_len, B, Q, d, pool, max_pools, max_cache_len, scores};
+  return mla::launch_scores(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_indexer_select(const float* scores, const int32_t* cache_len, int32_t B, int32_t Q, int32_t pool,
+                       int32_t max_pools, int32_t max_cache_len, int32_t topk, int32_t tail, int32_t* idx,
+                       int32_t* idx_len, int32_t K_max, void* stream) {
+  if (!scores || !cache_len || !idx || !idx_len) return MLA_ERR_NULL;
+  if (B < 1 || Q < 1 || pool < 1 || max_pools < 1 || max_cache_len < 1) return MLA_ERR_SHAPE;
+  if (max_pools > mla::kMaxIndexerPools || max_pools < max_cache_len / pool) return MLA_ERR_ARG;
+  if (topk < pool || topk % pool != 0) return MLA_ERR_ARG;
+  if (K_max < topk + (tail ? pool - 1 : 0)) return MLA_ERR_ARG;
+  if ((int64_t)B * Q > 0x7fffffff) return MLA_ERR_SHAPE;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  mla::SelectArgs a{scores, cache_len, B, Q, pool, max_pools, max_cache_len, topk, tail ? 1 : 0, K_max, idx, idx_len};
+  return mla::launch_select(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, int32_t H, int32_t D, int32_t R,
              void* stream) {
   if (!o_lat || !w_v || !out) return MLA_ERR_NULL;

@@ -32,6 +32,41 @@ struct AttnArgs {
 // q_units < Q selects the query-pair variant (dense only)
 hipError_t launch_latent_attn(const AttnArgs& a, bool indexed, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
+// ---- k-pooled indexer
+constexpr int kMaxIndexerPools = 16384;  // selectable pools per query (one LDS key each)
+constexpr int kMaxIndexerQ = 8;          // queries per sequence scored together
+constexpr int kMaxIndexerDim = 256;      // indexer key width
+
+struct KpoolArgs {
+  const uint16_t* k;          // [B][.][d] bf16 indexer keys, batch_stride elements apart
+  const uint16_t* g;          // [B][.][d] bf16 gate logits, same layout
+  int64_t batch_stride;
+  const int32_t* cache_len;   // [B]
+  const int32_t* pool_begin;  // [B] first pool to (re)build, or null for 0
+  int32_t B, max_cache_len, d, pool, max_pools;
+  float* pooled;              // [B][max_pools][d]
+};
+
+struct ScoreArgs {
+  const uint16_t* q;          // [B][Q][d] bf16
+  const float* pooled;        // [B][max_pools][d]
+  const int32_t* cache_len;
+  int32_t B, Q, d, pool, max_pools, max_cache_len;
+  float* scores;              // [B][Q][max_pools]
+};
+
+struct SelectArgs {
+  const float* scores;        // [B][Q][max_pools]
+  const int32_t* cache_len;
+  int32_t B, Q, pool, max_pools, max_cache_len, topk, tail, K_max;
+  int32_t* idx;               // [B][Q][K_max]
+  int32_t* idx_len;           // [B][Q]
+};
+
+hipError_t launch_kpool(const KpoolArgs& a, hipStream_t stream);
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream);
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
 hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int rows, int H,
                            float prescale, hipStream_t stream);
 hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H,

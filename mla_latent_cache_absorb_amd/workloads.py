@@ -161,6 +161,20 @@ def make_spec(batch, q_len, cache_len, *, heads=HEADS, head_dim=HEAD_DIM, latent
                         head_dim=head_dim, latent=latent)
 
 
+def _draw_lengths(spec: WorkloadSpec, s_len: np.random.SeedSequence) -> np.ndarray:
+    if spec.min_cache_len is not None:
+        g = np.random.Generator(np.random.PCG64(s_len))
+        return g.integers(spec.min_cache_len, spec.cache_len, size=spec.batch, endpoint=True).astype(np.int32)
+    return np.full(spec.batch, spec.cache_len, np.int32)
+
+
+def cache_lengths(spec, set_index: int = 0) -> np.ndarray:
+    """The cache_len array make_workload(spec, set_index) draws, without drawing the rest."""
+    if isinstance(spec, str):
+        spec = WORKLOADS[spec]
+    return _draw_lengths(spec, np.random.SeedSequence([SEED_ROOT, spec.workload_id, set_index]).spawn(7)[0])
+
+
 def make_workload(spec, set_index: int = 0, *, pad_bits: int = BF16_NAN, pad_index: int = -1,
                   l_max: Optional[int] = None) -> Workload:
     """Draw one batch of inputs for `spec` (a WorkloadSpec or a key of WORKLOADS).
@@ -176,12 +190,7 @@ def make_workload(spec, set_index: int = 0, *, pad_bits: int = BF16_NAN, pad_ind
     streams = np.random.SeedSequence([SEED_ROOT, spec.workload_id, set_index]).spawn(7)
     s_len, s_q, s_c, s_wk, s_wv, s_spk, s_idx = streams
 
-    # lengths
-    if spec.min_cache_len is not None:
-        g = np.random.Generator(np.random.PCG64(s_len))
-        cache_len = g.integers(spec.min_cache_len, spec.cache_len, size=B, endpoint=True).astype(np.int32)
-    else:
-        cache_len = np.full(B, spec.cache_len, np.int32)
+    cache_len = _draw_lengths(spec, s_len)
     L_max = int(l_max if l_max is not None else spec.cache_len)
     if L_max < int(cache_len.max()):
         raise ValueError("l_max smaller than the longest cache")
@@ -238,3 +247,46 @@ def latent_query_bits(spec, set_index: int = 0) -> np.ndarray:
     s = np.random.SeedSequence([SEED_ROOT, spec.workload_id, set_index, 0x51]).spawn(1)[0]
     n = spec.batch * spec.q_len * spec.heads * spec.latent
     return normal_bf16(s, n, float(np.sqrt(0.5))).reshape(spec.batch, spec.q_len, spec.heads, spec.latent)
+
+
+# ---------------------------------------------------------------- k-pooled indexer inputs
+INDEXER_DIM = 128   # indexer key / query width (a reading: the pages give none)
+INDEXER_POOL = 4    # positions per pool (`index_kpool`; a reading: the pages give no value)
+INDEXER_TOPK = 2048  # positions selected per query (a multiple of the pool)
+
+
+@dataclass
+class IndexerInputs:
+    """Inputs of the k-pooled indexer for one batch.  Shapes:
+    q [B, Q, d], k and g [B, L_max, d]  uint16 (bf16 bits): indexer queries, keys, gate logits;
+    rows at or past cache_len[b] hold pad_bits.  cache_len [B] int32 (the same lengths as the
+    attention workload's)."""
+    q: np.ndarray
+    k: np.ndarray
+    g: np.ndarray
+    cache_len: np.ndarray
+    pool: int
+    topk: int
+
+
+def make_indexer_inputs(spec, cache_len: np.ndarray, set_index: int = 0, *, d: int = INDEXER_DIM,
+                        pool: int = INDEXER_POOL, topk: int = INDEXER_TOPK, pad_bits: int = BF16_NAN,
+                        l_max: Optional[int] = None) -> IndexerInputs:
+    """N(0, 1) indexer queries, keys and gate logits (bf16) for the sequences of `spec`, seeded
+    from SeedSequence([SEED_ROOT, workload_id, set_index, 0x1D]) spawned into q, k, g."""
+    if isinstance(spec, str):
+        spec = WORKLOADS[spec]
+    B, Q = spec.batch, spec.q_len
+    L_max = int(l_max if l_max is not None else spec.cache_len)
+    s_q, s_k, s_g = np.random.SeedSequence([SEED_ROOT, spec.workload_id, set_index, 0x1D]).spawn(3)
+    q = normal_bf16(s_q, B * Q * d).reshape(B, Q, d)
+    k = np.empty((B, L_max, d), np.uint16)
+    g = np.empty((B, L_max, d), np.uint16)
+    k_kids, g_kids = s_k.spawn(B), s_g.spawn(B)
+    for b in range(B):
+        n = int(cache_len[b])
+        k[b, :n] = normal_bf16(k_kids[b], n * d).reshape(n, d)
+        g[b, :n] = normal_bf16(g_kids[b], n * d).reshape(n, d)
+        k[b, n:] = pad_bits
+        g[b, n:] = pad_bits
+    return IndexerInputs(q, k, g, np.asarray(cache_len, np.int32), pool, topk)

@@ -8,3 +8,4 @@ from .mla_oracle import *  # noqa: F401,F403
 from .mla_oracle import (absorbed_query, bf16_bits_to_f64, cache_bytes_per_token, dense_visible_positions,
                          expanded_scores, indexed_visible_positions, latent_attention, mla_reference,
                          query_position, softmax_attention, up_project, visible_sets)
+from . import kpool_indexer  # noqa: F401  (the k-pooled indexer that produces position lists)

@@ -94,3 +94,19 @@ def test_split_choice_without_device(L):
     assert binding.mla_latent_attn_num_splits(16, 6, 64, 32768, 0) == 8         # 768 = 3 rounds
     assert binding.mla_latent_attn_num_splits(32, 4, 64, 2052, 0, indexed=True) == 2
     assert binding.mla_latent_attn_workspace_size(32, 4, 64, 512, 2052, 0, indexed=True) == 2 * 128 * 64 * 514 * 4
+
+
+def test_indexer_host_validation(L):
+    fake = ctypes.c_void_p(0x1000)
+    # null pointers, bad widths, and sizes the kernels cannot hold are refused before any launch
+    assert L.mla_kpool_keys(None, fake, 128 * 64, fake, None, 1, 64, 128, 4, fake, 16, None) == binding.MLA_ERR_NULL
+    assert L.mla_kpool_keys(fake, fake, 96 * 64, fake, None, 1, 64, 96, 4, fake, 16, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_kpool_keys(fake, fake, 128 * 63, fake, None, 1, 64, 128, 4, fake, 16, None) == binding.MLA_ERR_ARG
+    assert L.mla_kpool_keys(fake, fake, 128 * 64, fake, None, 1, 64, 128, 4, fake, 15, None) == binding.MLA_ERR_ARG
+    assert L.mla_indexer_scores(fake, fake, fake, 1, 9, 128, 4, 16, 64, fake, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_indexer_scores(fake, None, fake, 1, 4, 128, 4, 16, 64, fake, None) == binding.MLA_ERR_NULL
+    # topk must be a multiple of the pool, rows must hold topk + pool - 1 with the tail
+    assert L.mla_indexer_select(fake, fake, 1, 1, 4, 16, 64, 6, 1, fake, fake, 9, None) == binding.MLA_ERR_ARG
+    assert L.mla_indexer_select(fake, fake, 1, 1, 4, 16, 64, 8, 1, fake, fake, 10, None) == binding.MLA_ERR_ARG
+    assert L.mla_indexer_select(fake, fake, 1, 1, 4, 16384 * 2, 65536 * 2, 8, 1, fake, fake, 11, None) \
+        == binding.MLA_ERR_ARG

@@ -81,3 +81,8 @@ def test_named_workloads_cover_the_five_cases():
     assert (s.batch, s.cache_len, s.spike_frac, s.spike_scale) == (4, 131072, 0.01, 8.0)
     s = W["indexed_verify_b32_q4_ragged"]
     assert (s.batch, s.q_len, s.min_cache_len, s.cache_len, s.n_index) == (32, 4, 4096, 65536, 2048)
+
+
+def test_cache_lengths_match_the_workload():
+    w = wl.make_workload(wl.make_spec(5, 2, 300, min_cache_len=10, workload_id=77))
+    np.testing.assert_array_equal(wl.cache_lengths(w.spec), w.cache_len)
