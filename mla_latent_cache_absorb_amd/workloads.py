@@ -290,3 +290,33 @@ def make_indexer_inputs(spec, cache_len: np.ndarray, set_index: int = 0, *, d: i
         k[b, n:] = pad_bits
         g[b, n:] = pad_bits
     return IndexerInputs(q, k, g, np.asarray(cache_len, np.int32), pool, topk)
+
+
+# --------------------------------------------------------------------------
+# down-projection inputs: hidden states of the new tokens and the latent projection
+# --------------------------------------------------------------------------
+HIDDEN = 4096                        # the language model's hidden width
+W_DKV_STD = float(np.sqrt(1.0 / HIDDEN))  # keeps the projected latents near N(0, 1), like the caches
+
+
+@dataclass
+class AppendInputs:
+    """Inputs of the latent down-projection for one pass: h [B, Q, hidden] (bf16 bits), the new
+    tokens' hidden states; w_dkv [R, hidden] (bf16 bits), row r = the weights of latent channel r."""
+    h: np.ndarray
+    w_dkv: np.ndarray
+
+
+def make_append_inputs(spec, set_index: int = 0, *, hidden: int = HIDDEN, rows: Optional[int] = None,
+                       w_seed: int = 0) -> AppendInputs:
+    """N(0, 1) hidden states for the spec's B x Q new tokens (or `rows` x 1) and an N(0, 1/hidden)
+    projection, bf16, seeded from SeedSequence([SEED_ROOT, workload_id, set_index, 0xD0]) (h) and
+    SeedSequence([SEED_ROOT, 0xD1, w_seed]) (the projection, shared by every workload)."""
+    if isinstance(spec, str):
+        spec = WORKLOADS[spec]
+    B, Q = (spec.batch, spec.q_len) if rows is None else (rows, 1)
+    s_h = np.random.SeedSequence([SEED_ROOT, spec.workload_id, set_index, 0xD0])
+    s_w = np.random.SeedSequence([SEED_ROOT, 0xD1, w_seed])
+    h = normal_bf16(s_h, B * Q * hidden).reshape(B, Q, hidden)
+    w = normal_bf16(s_w, spec.latent * hidden, W_DKV_STD if hidden == HIDDEN else float(np.sqrt(1.0 / hidden)))
+    return AppendInputs(h, w.reshape(spec.latent, hidden))

@@ -9,3 +9,4 @@ from .mla_oracle import (absorbed_query, bf16_bits_to_f64, cache_bytes_per_token
                          expanded_scores, indexed_visible_positions, latent_attention, mla_reference,
                          query_position, softmax_attention, up_project, visible_sets)
 from . import kpool_indexer  # noqa: F401  (the k-pooled indexer that produces position lists)
+from . import latent_append  # noqa: F401  (down-projection of new tokens into the cache)
