@@ -221,6 +221,66 @@ def time_indexer(name: str, steps: int, warmup: int):
     }
 
 
+def time_append(steps: int, warmup: int):
+    """The latent down-projection with cache append at three pass shapes: the decode batch
+    (32 sequences x 1 token), the verification batch (16 x 6) and a 4096-token prefill chunk of
+    one sequence.  Per-call time from HIP events around a graph replay of `steps` calls.  The two small passes are
+    bound by reading the projection (4 MiB) and the hidden states; the chunk by the matrix cores
+    (2 * 4096 * 512 flops per token)."""
+    import numpy as np
+    import torch
+    from mla_latent_cache_absorb_amd import binding, workloads as wl
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    out = {}
+    for label, wname, rows in (("decode_b32_q1", "decode_b32_l8192", None),
+                               ("verify_b16_q6", "verify_b16_q6_l32768", None),
+                               ("prefill_chunk_4096", "decode_b32_l8192", 4096)):
+        spec = wl.WORKLOADS[wname]
+        inp = wl.make_append_inputs(spec, rows=rows)
+        B, Q, hidden = inp.h.shape if rows is None else (1, rows, wl.HIDDEN)
+        h = bf(inp.h.reshape(B, Q, hidden))
+        w = bf(inp.w_dkv)
+        L = 8192 if rows is None else rows
+        cache = torch.zeros((B, L, wl.LATENT), dtype=torch.bfloat16, device=dev)
+        cl = torch.full((B,), L, dtype=torch.int32, device=dev)
+        for _ in range(warmup):
+            binding.mla_latent_append(h, w, cache, cl, L)
+        torch.cuda.synchronize()
+        # a call takes a few microseconds on the GPU, less than the Python call that launches it:
+        # the timed calls are captured in a HIP graph and replayed, so the events see GPU time
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                binding.mla_latent_append(h, w, cache, cl, L)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        del graph
+        n = B * Q
+        nbytes = wl.LATENT * hidden * 2 + n * hidden * 2 + n * wl.LATENT * 2
+        flops = 2 * n * hidden * wl.LATENT
+        entry = {"tokens": n, "ms": round(ms, 6)}
+        if rows is None:
+            ach = nbytes / (ms * 1e-3) / 1e9
+            entry["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": nbytes}
+        else:
+            ach = flops / (ms * 1e-3) / 1e12
+            entry["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops}
+        out[label] = entry
+        del cache
+    return out
+
+
 def cpu_baseline(name: str, budget_s: float = 12.0):
     """The fp64 oracle (expanded form) on whole sequences of the same workload, until about
     budget_s of CPU time has been spent."""
@@ -255,6 +315,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-indexer", action="store_true")
+    ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--append-only", action="store_true",
+                    help="time only the down-projection with cache append (for profiling it on its own)")
     ap.add_argument("--indexer-only", action="store_true",
                     help="time only the k-pooled indexer (for profiling it on its own)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -285,6 +348,9 @@ def main():
         log(f"[bench] copied {args.calibrate_copy} MiB three times")
         del src, dst
         torch.cuda.empty_cache()
+    if args.append_only:
+        print(json.dumps({"append": time_append(args.steps, args.warmup)}), flush=True)
+        return
     if args.indexer_only:
         print(json.dumps({"indexer": time_indexer("indexed_verify_b32_q4_ragged", args.steps, args.warmup)}),
               flush=True)
@@ -339,6 +405,9 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] timing the k-pooled indexer")
         result["indexer"] = time_indexer("indexed_verify_b32_q4_ragged", max(5, args.steps // 5), 3)
+    if not args.no_append:
+        log("[bench] timing the down-projection with cache append")
+        result["append"] = time_append(max(10, args.steps // 2), 3)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(args.workload)

@@ -204,6 +204,30 @@ int mla_indexer_select(const float* scores, const int32_t* cache_len, int32_t B,
                        int32_t* idx_len, int32_t K_max, void* stream);
 
 /*
+ * Latent down-projection with cache append (page "Module 05", section 1: every token is
+ * projected down to one shared latent c_t, and c_t is what the cache keeps; page "Module 08",
+ * section 1: hidden width 4096; section 3: the latent cache is truncatable by position).
+ *   h          [B][Q][hidden] bf16  hidden states of the pass's Q new tokens per sequence
+ *   w_dkv      [R][hidden]    bf16  the projection; row r holds the weights of latent channel r
+ *   cache      latent cache (as in mla_latent_attn); row j of sequence b at
+ *              cache + b*cache_batch_stride + j*R; cache_batch_stride >= max_cache_len * R
+ *   cache_len  [B] int32 (device): lengths AFTER the pass.  Token i of sequence b is written at
+ *              position cache_len[b] - Q + i, where its query sits in the attention call, as
+ *              bf16(sum_k w_dkv[r][k] h[b][i][k]) (fp32 accumulation, nearest-even rounding).
+ *              Nothing else is written.  Device-side precondition: Q <= cache_len[b] <=
+ *              max_cache_len (positions that would fall outside the cache are skipped).
+ * Each row depends only on its own hidden state and w_dkv (a fixed summation order), so a token
+ * projected in a verification pass and the same token projected alone give identical bits.
+ * Rolling back rejected tokens is a smaller cache_len; their stale rows are never read.
+ * Supported: hidden == 4096, R == 512.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ARG (stride or max_cache_len < Q),
+ * MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_latent_append(const uint16_t* h, const uint16_t* w_dkv, uint16_t* cache, int64_t cache_batch_stride,
+                      const int32_t* cache_len, int32_t B, int32_t Q, int32_t hidden, int32_t R,
+                      int32_t max_cache_len, void* stream);
+
+/*
  * Value up-projection (page "Module 05", section 3: U_h^V factors out of the sum over
  * history, so the accumulated latent is expanded once, at the end).
  *   o_lat  [rows][H][R] fp32   accumulated latents (mla_latent_attn)

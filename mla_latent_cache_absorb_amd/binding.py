@@ -25,7 +25,7 @@ MLA_ERR_DEVICE = -6
 
 EXPORTS = ("mla_status_string", "mla_absorb_q", "mla_latent_attn_num_splits", "mla_latent_attn_workspace_size",
            "mla_latent_attn", "mla_latent_attn_indexed", "mla_up_v", "mla_kpool_keys", "mla_indexer_scores",
-           "mla_indexer_select")
+           "mla_indexer_select", "mla_latent_append")
 
 
 class MlaError(RuntimeError):
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.mla_indexer_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
         L.mla_indexer_scores.restype = ctypes.c_int
         L.mla_indexer_select.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
+        L.mla_latent_append.restype = ctypes.c_int
+        L.mla_latent_append.argtypes = [vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, vp]
         L.mla_indexer_select.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -205,6 +207,27 @@ def mla_up_v(o_lat: torch.Tensor, w_v: torch.Tensor, out: Optional[torch.Tensor]
     _need(out, torch.float32, "out")
     _check(lib().mla_up_v(_ptr(o_lat), _ptr(w_v), _ptr(out), rows, H, D, R, _stream(stream)), "mla_up_v")
     return out
+
+
+# ------------------------------------------------------------------ down-projection and append
+def mla_latent_append(h: torch.Tensor, w_dkv: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor,
+                      max_cache_len: int, stream=None) -> torch.Tensor:
+    """h [B, Q, hidden] bf16, w_dkv [R, hidden] bf16: writes bf16(W h) of token i of sequence b
+    into cache[b, cache_len[b] - Q + i] (cache_len: lengths after the pass).  Returns cache."""
+    _need(h, torch.bfloat16, "h")
+    _need(w_dkv, torch.bfloat16, "w_dkv")
+    _need(cache_len, torch.int32, "cache_len")
+    if cache.dtype != torch.bfloat16:
+        raise TypeError("cache must be bfloat16")
+    if h.dim() != 3:
+        raise ValueError("h must be [B, Q, hidden]")
+    B, Q, hidden = h.shape
+    R = w_dkv.shape[0]
+    if w_dkv.shape != (R, hidden) or cache.shape[0] != B or cache.shape[2] != R or cache_len.numel() != B:
+        raise ValueError("shape mismatch between h, w_dkv, cache and cache_len")
+    _check(lib().mla_latent_append(_ptr(h), _ptr(w_dkv), _ptr(cache), _cache_stride(cache), _ptr(cache_len), B, Q,
+                                   hidden, R, int(max_cache_len), _stream(stream)), "mla_latent_append")
+    return cache
 
 
 # ---------------------------------------------------------------------------- k-pooled indexer

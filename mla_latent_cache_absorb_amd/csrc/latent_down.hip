@@ -1,0 +1,131 @@
+// Latent down-projection with cache append for gfx950 (page "Module 05 -- MLA: Compressing
+// Per-Token History", section 1: each token is projected down to one shared latent and that
+// latent is what the cache keeps; page "Module 08 -- Vision, MTP, and Hybrid Serving State",
+// section 1: hidden width 4096).
+//
+//   c[n][r] = sum_k W[r][k] h[n][k]   (fp32), stored as bf16 (nearest, ties to even) at
+//   cache[b][cache_len[b] - Q + i][r] for token n = b*Q + i.
+//
+// A workgroup owns 16 latent channels (one 16 x 4096 slab of W, 128 KiB) and sixteen waves; wave
+// w holds the slab's K-slice 256w .. 256w+255 in 32 VGPRs for the whole kernel, so W is read from
+// memory once per workgroup however many tokens it projects.  For each tile of 16 tokens every
+// wave multiplies its K-slice (8 MFMA 16x16x32, k in natural order) and the sixteen partial tiles
+// are summed through LDS in wave order: the result of a token depends only on its own hidden
+// state and W, never on the batch it came in.
+//
+// Operands reach registers through a private 8 KiB LDS stage per wave: each copy instruction
+// moves two 512-byte row slices (1 KiB, whole 128-byte lines) straight from memory into LDS, with
+// 16-byte chunk c of row r stored at slot c ^ r, so that the MFMA-layout reads (16 rows at one
+// chunk) fall in sixteen different bank groups.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kDownCols = 16;              // latent channels per workgroup
+constexpr int kDownWaves = 16;
+constexpr int kDownThreads = 64 * kDownWaves;
+constexpr int kSlice = kHidden / kDownWaves;  // K per wave
+constexpr int kSteps = kSlice / 32;           // MFMA 16x16x32 per tile
+constexpr int kSliceBytes = kSlice * 2;       // one row's slice: 32 chunks of 16 bytes
+constexpr int kStageBytes = 16 * kSliceBytes;
+
+static_assert(kSlice == 256 && kSteps == 8, "lane k-ranges assume a 256-wide slice");
+
+__device__ __forceinline__ f32x4 mfma16x16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// lane-addressed copy of 16 bytes from `src` to lds + 16 * lane (lds wave-uniform); the caller
+// waits (vmcnt) before reading the copy
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+  const uint32_t ls = __builtin_amdgcn_readfirstlane(lds);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(ls), "v"(src) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Stage 16 rows' K-slices (row r at `rows + r * kHidden` elements) into this wave's LDS stage.
+// Copy j moves rows 2j and 2j+1: lane l takes row 2j + (l >> 5) and fills slot l & 31 with chunk
+// (l & 31) ^ row.  Rows at or past nrows_valid are read from the last valid row.
+__device__ __forceinline__ void stage_rows(const uint16_t* rows, int nrows_valid, uint32_t st, int lane) {
+  const int slot = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 2 * j + half;
+    const int rc = r < nrows_valid ? r : nrows_valid - 1;
+    const uint8_t* src = (const uint8_t*)(rows + (size_t)rc * kHidden) + 16 * (slot ^ r);
+    copy16_to_lds(src, st + 1024 * j);
+  }
+}
+
+// operand fragment for MFMA step s: row m, chunk 4s + g (k = 32s + 8g .. +7 of the slice)
+__device__ __forceinline__ bf16x8 stage_read(const uint8_t* stage, int m, int g, int s) {
+  return *(const bf16x8*)(stage + m * kSliceBytes + 16 * ((4 * s + g) ^ m));
+}
+
+__global__ __launch_bounds__(kDownThreads) void latent_down_kernel(DownArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[kDownWaves][kStageBytes];  // 128 KiB
+  __shared__ f32x4 red[kDownWaves][kDownCols][4];  // [wave][channel][tokens / 4]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int r0 = blockIdx.x * kDownCols;
+  const uint8_t* my = stage[wave];
+  const uint32_t st = lds_addr(my);
+
+  bf16x8 wb[kSteps];
+  stage_rows(a.w + (size_t)r0 * kHidden + wave * kSlice, 16, st, lane);
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) wb[s] = stage_read(my, m, g, s);
+
+  const int rows = a.B * a.Q;
+  const int ntiles = (rows + 15) / 16;
+  for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
+    wait_lds_reads();  // the stage is rewritten below
+    stage_rows(a.h + (size_t)tile * 16 * kHidden + wave * kSlice, min(16, rows - tile * 16), st, lane);
+    wait_vmcnt<0>();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) acc = mfma16x16(stage_read(my, m, g, s), wb[s], acc);
+    // lane holds channel r0 + m of tokens 16 tile + 4g + j
+    red[wave][m][g] = acc;
+    __syncthreads();
+    if (threadIdx.x < 16 * kDownCols) {
+      const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
+      const float* part = (const float*)&red[0][col][0] + row;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDownWaves; ++w) sum += part[w * kDownCols * 16];
+      const int nn = tile * 16 + row;
+      if (nn < rows) {
+        const int b = nn / a.Q, i = nn - b * a.Q;
+        const int pos = min(a.cache_len[b], a.max_cache_len) - a.Q + i;
+        if (pos >= 0) a.cache[(size_t)b * a.cache_bstride + (size_t)pos * kLatent + r0 + col] = f32_to_bf16_bits(sum);
+      }
+    }
+    __syncthreads();  // red is rewritten by the next tile
+  }
+}
+
+}  // namespace
+
+int down_row_groups(int rows) {
+  const int ntiles = (rows + 15) / 16;
+  return ntiles < 32 ? ntiles : 32;
+}
+
+hipError_t launch_latent_down(const DownArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<DownArgs*>(&a)};
+  const dim3 grid(kLatent / kDownCols, down_row_groups(a.B * a.Q)), block(kDownThreads);
+  return hipLaunchKernel((const void*)&latent_down_kernel, grid, block, args, 0, stream);
+}
+
+}  // namespace mla

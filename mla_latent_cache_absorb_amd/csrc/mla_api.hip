@@ -260,6 +260,20 @@ int mla_indexer_select(const float* scores, const int32_t* cache_len, int32_t B,
   return mla::launch_select(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_latent_append(const uint16_t* h, const uint16_t* w_dkv, uint16_t* cache, int64_t cache_batch_stride,
+                      const int32_t* cache_len, int32_t B, int32_t Q, int32_t hidden, int32_t R,
+                      int32_t max_cache_len, void* stream) {
+  if (!h || !w_dkv || !cache || !cache_len) return MLA_ERR_NULL;
+  if (hidden != mla::kHidden || R != 512 || B < 1 || Q < 1 || (int64_t)B * Q > 0x7fffffff)
+    return MLA_ERR_SHAPE;
+  if (max_cache_len < Q || cache_batch_stride < (int64_t)max_cache_len * R) return MLA_ERR_ARG;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  mla::DownArgs a{h, w_dkv, cache, cache_batch_stride, cache_len, B, Q, max_cache_len};
+  if (mla::launch_latent_down(a, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, int32_t H, int32_t D, int32_t R,
              void* stream) {
   if (!o_lat || !w_v || !out) return MLA_ERR_NULL;

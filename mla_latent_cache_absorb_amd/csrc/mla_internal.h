@@ -67,6 +67,19 @@ hipError_t launch_kpool(const KpoolArgs& a, hipStream_t stream);
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
+// ---- latent down-projection with cache append
+constexpr int kHidden = 4096;   // hidden width projected down to the latent
+struct DownArgs {
+  const uint16_t* h;          // [B*Q][kHidden] bf16 hidden states of the new tokens
+  const uint16_t* w;          // [kLatent][kHidden] bf16 projection
+  uint16_t* cache;            // latent rows, cache_bstride elements between sequences
+  int64_t cache_bstride;
+  const int32_t* cache_len;   // [B] lengths after the append
+  int32_t B, Q, max_cache_len;
+};
+int down_row_groups(int rows);
+hipError_t launch_latent_down(const DownArgs& a, hipStream_t stream);
+
 hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int rows, int H,
                            float prescale, hipStream_t stream);
 hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H,

@@ -110,3 +110,15 @@ def test_indexer_host_validation(L):
     assert L.mla_indexer_select(fake, fake, 1, 1, 4, 16, 64, 8, 1, fake, fake, 10, None) == binding.MLA_ERR_ARG
     assert L.mla_indexer_select(fake, fake, 1, 1, 4, 16384 * 2, 65536 * 2, 8, 1, fake, fake, 11, None) \
         == binding.MLA_ERR_ARG
+
+
+def test_append_host_validation(L):
+    fake = ctypes.c_void_p(0x1000)
+    # null pointers, widths other than 4096 -> 512, and a stride or cache too small for the pass
+    assert L.mla_latent_append(None, fake, fake, 512 * 64, fake, 1, 1, 4096, 512, 64, None) == binding.MLA_ERR_NULL
+    assert L.mla_latent_append(fake, fake, fake, 512 * 64, None, 1, 1, 4096, 512, 64, None) == binding.MLA_ERR_NULL
+    assert L.mla_latent_append(fake, fake, fake, 512 * 64, fake, 1, 1, 2048, 512, 64, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_latent_append(fake, fake, fake, 512 * 64, fake, 1, 1, 4096, 256, 64, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_latent_append(fake, fake, fake, 512 * 64, fake, 0, 1, 4096, 512, 64, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_latent_append(fake, fake, fake, 512 * 63, fake, 1, 1, 4096, 512, 64, None) == binding.MLA_ERR_ARG
+    assert L.mla_latent_append(fake, fake, fake, 512 * 64, fake, 1, 6, 4096, 512, 5, None) == binding.MLA_ERR_ARG
