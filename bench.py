@@ -161,9 +161,9 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
 
 
 def time_indexer(name: str, steps: int, warmup: int):
-    """The k-pooled indexer on the sequences of `name`: pooled keys (full build), pool scores for
-    all queries, top-k selection into position lists; per-kernel times from HIP events on the
-    launch stream."""
+    """The k-pooled indexer on the sequences of `name`: pooled keys (a full build, and a decode
+    step's build of each sequence's newest pool), pool scores for all queries, top-k selection
+    into position lists; per-kernel times from HIP events on the launch stream."""
     import numpy as np
     import torch
     from mla_latent_cache_absorb_amd import binding, workloads as wl
@@ -183,6 +183,8 @@ def time_indexer(name: str, steps: int, warmup: int):
     idx = torch.empty((B, Q, ix.topk + ix.pool - 1), dtype=torch.int32, device=dev)
     idx_len = torch.empty((B, Q), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    # a decode step only pools what its new positions complete: the last pool of each sequence
+    last_pool = torch.from_numpy(np.maximum(lens // ix.pool - 1, 0).astype(np.int32)).to(dev)
 
     def step(ev=None):
         if ev is not None:
@@ -190,31 +192,43 @@ def time_indexer(name: str, steps: int, warmup: int):
         binding.mla_kpool_keys(k, g, cl, Lmax, ix.pool, pooled=pooled)
         if ev is not None:
             ev[1].record(stream)
-        binding.mla_indexer_scores(q, pooled, cl, Lmax, ix.pool, scores=scores)
+        binding.mla_kpool_keys(k, g, cl, Lmax, ix.pool, pooled=pooled, pool_begin=last_pool)
         if ev is not None:
             ev[2].record(stream)
-        binding.mla_indexer_select(scores, cl, Lmax, ix.pool, ix.topk, True, idx=idx, idx_len=idx_len)
+        binding.mla_indexer_scores(q, pooled, cl, Lmax, ix.pool, scores=scores)
         if ev is not None:
             ev[3].record(stream)
+        binding.mla_indexer_select(scores, cl, Lmax, ix.pool, ix.topk, True, idx=idx, idx_len=idx_len)
+        if ev is not None:
+            ev[4].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for s in range(steps):
         step(evs[s])
     torch.cuda.synchronize()
     stage = {kname: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
-             for j, kname in enumerate(("kpool_keys", "scores", "select"))}
+             for j, kname in enumerate(("kpool_keys_full", "kpool_keys_step", "scores", "select"))}
     npools = (lens // ix.pool).astype(np.int64)
     # algorithmic bytes of the score kernel: every pooled key read once per sequence, one score
     # written per (query, pool)
     score_bytes = int(npools.sum()) * d * 4 + int(npools.sum()) * Q * 4
+    # the full pooled-key build: keys and gate logits of every complete pool read, keys written
+    kpool_bytes = int(npools.sum()) * (2 * ix.pool * d * 2 + d * 4)
     achieved = score_bytes / (stage["scores"] * 1e-3) / 1e9
     return {
         "workload": name, "pool": ix.pool, "topk": ix.topk, "dim": d, "queries": B * Q,
         "stages_ms": {kname: round(v, 6) for kname, v in stage.items()},
-        "ms_per_step": round(sum(stage.values()), 6),
+        # one decode step: pool the newly completed pools, score, select (the full build is a
+        # prefill-time cost, reported on its own)
+        "ms_per_step": round(stage["kpool_keys_step"] + stage["scores"] + stage["select"], 6),
+        "kpool_full_roofline": {"kernel": "kpool_kernel", "bound": "hbm",
+                                "achieved": round(kpool_bytes / (stage["kpool_keys_full"] * 1e-3) / 1e9, 2),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(kpool_bytes / (stage["kpool_keys_full"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "algorithmic_bytes_per_launch": kpool_bytes},
         "roofline": {"kernel": "score_kernel", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": score_bytes, "avg_launch_ms": round(stage["scores"], 6)},

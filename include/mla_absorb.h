@@ -160,7 +160,8 @@ int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* cache, int64_
  * w[.][c] = softmax over s of g[b][p*pool + s][c] (fp32), for every complete pool
  * p < min(cache_len[b], max_cache_len) / pool at or after pool_begin[b].
  *   k, g         bf16 rows of d values; row j of sequence b at (k|g) + b*batch_stride + j*d;
- *                batch_stride (elements) >= max_cache_len * d; rows past cache_len are never read
+ *                batch_stride (elements) >= max_cache_len * d and a multiple of 8 (rows are read as
+ *                16-byte vectors); rows past cache_len are never read
  *   cache_len    [B] int32 (device)
  *   pool_begin   [B] int32 (device) first pool to build (pools before it are left as they are,
  *                so an append after new positions only builds the pools they complete), or
@@ -174,8 +175,8 @@ int mla_kpool_keys(const uint16_t* k, const uint16_t* g, int64_t batch_stride, c
                    float* pooled, int32_t max_pools, void* stream);
 
 /*
- * mla_indexer_scores: scores[b][i][p] = q[b][i] . pooled[b][p] (fp32, channels summed in
- * order), for every complete pool of sequence b.
+ * mla_indexer_scores: scores[b][i][p] = q[b][i] . pooled[b][p] (fp32, the channels summed in
+ * one fixed order), for every complete pool of sequence b.
  *   q        [B][Q][d] bf16 indexer queries; 1 <= Q <= 8
  *   pooled   [B][max_pools][d] fp32 from mla_kpool_keys
  *   scores   [B][Q][max_pools] fp32 output; entries of incomplete pools are not written

@@ -5,13 +5,15 @@
 //
 //   kpool_kernel   pooled[b][p][c] = sum_s w[s][c] k[b][p*pool + s][c], w[.][c] = softmax over the
 //                  pool's positions of the gate logits g[b][p*pool + s][c] (fp32)
-//   score_kernel   scores[b][i][p] = q[b][i] . pooled[b][p] (fp32, channels in order)
+//   score_kernel   scores[b][i][p] = q[b][i] . pooled[b][p] (fp32, a fixed order of the channels)
 //   select_kernel  per query at t = cache_len - Q + i: the topk / pool best pools among the
 //                  complete ones (last position <= t), ties to the lower pool, in ascending order,
 //                  expanded to positions, then the incomplete tail floor((t+1)/pool)*pool .. t;
 //                  unused slots -1
 // The selection is integer work decided on the fp32 scores: a radix select over order-preserving
 // 32-bit keys finds the k-th largest score, equal keys are taken lowest pool first.
+// Keys and gate logits are read as 16-byte vectors: rows start 16-byte aligned (d is a multiple
+// of 8, batch_stride a multiple of 8 elements).
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -20,62 +22,157 @@ namespace mla {
 namespace {
 
 constexpr int kSelThreads = 256;
+constexpr int kSelPerThread = kMaxIndexerPools / kSelThreads;  // pools owned by one thread
+constexpr int kHistBins = 2048;
+constexpr int kScoreLanes = 8;        // lanes that share one pool's key
+constexpr int kScoreBatch = 4;        // pools per lane group in flight together
+constexpr int kScorePoolsPerBlock = 256;
 
+static_assert(kSelPerThread == 64, "the selection keeps one 64-bit mask per thread");
+
+// Eight channels per thread (16-byte loads of keys and gate logits): d / 8 threads per pool.
+// Per channel: gm = max_s g, e_s = exp(g_s - gm), pooled = (sum_s e_s k_s) / (sum_s e_s).
+// Pools of up to PR positions (PR = 4 or 8) keep their gate logits in registers between the two
+// passes and issue every load of the pool at once; longer pools (PR = 0) read the logits twice.
+
+__device__ __forceinline__ void kpool_store(float* dst, const float (&acc)[8], const float (&sum)[8]) {
+  const f32x4 lo = {acc[0] / sum[0], acc[1] / sum[1], acc[2] / sum[2], acc[3] / sum[3]};
+  const f32x4 hi = {acc[4] / sum[4], acc[5] / sum[5], acc[6] / sum[6], acc[7] / sum[7]};
+  *(f32x4*)dst = lo;
+  *(f32x4*)(dst + 4) = hi;
+}
+
+template <int PR>
 __global__ __launch_bounds__(256) void kpool_kernel(KpoolArgs a) {
   const int b = blockIdx.y;
   const int L = min(a.cache_len[b], a.max_cache_len);
   const int np = min(L / a.pool, a.max_pools);
   const int p0 = a.pool_begin ? max(a.pool_begin[b], 0) : 0;
-  const int per_block = 256 / a.d;  // pools handled at once (d threads each)
-  const int c = threadIdx.x % a.d;
-  const uint16_t* kb = a.k + (size_t)b * a.batch_stride;
-  const uint16_t* gb = a.g + (size_t)b * a.batch_stride;
-  for (int p = p0 + blockIdx.x * per_block + (int)threadIdx.x / a.d; p < np; p += gridDim.x * per_block) {
-    const size_t base = (size_t)p * a.pool * a.d + c;
-    float gm = -INFINITY;
-    for (int s = 0; s < a.pool; ++s) gm = fmaxf(gm, bf16_bits_to_f32(gb[base + (size_t)s * a.d]));
-    float sum = 0.f, acc = 0.f;
-    for (int s = 0; s < a.pool; ++s) {
-      const float e = __expf(bf16_bits_to_f32(gb[base + (size_t)s * a.d]) - gm);
-      sum += e;
-      acc = __builtin_fmaf(e, bf16_bits_to_f32(kb[base + (size_t)s * a.d]), acc);
+  const int tpp = a.d >> 3;                 // threads per pool
+  const int per_block = 256 / tpp;
+  const int c0 = 8 * ((int)threadIdx.x % tpp);
+  const uint16_t* kb = a.k + (size_t)b * a.batch_stride + c0;
+  const uint16_t* gb = a.g + (size_t)b * a.batch_stride + c0;
+  for (int p = p0 + blockIdx.x * per_block + (int)threadIdx.x / tpp; p < np; p += gridDim.x * per_block) {
+    const size_t base = (size_t)p * a.pool * a.d;
+    float* dst = a.pooled + ((size_t)b * a.max_pools + p) * a.d + c0;
+    float gm[8], sum[8], acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gm[e] = -INFINITY;
+      sum[e] = acc[e] = 0.f;
     }
-    a.pooled[((size_t)b * a.max_pools + p) * a.d + c] = acc / sum;
+    if constexpr (PR > 0) {
+      s16x8 gv[PR], kv[PR];
+#pragma unroll
+      for (int s = 0; s < PR; ++s) {
+        if (s < a.pool) {
+          gv[s] = *(const s16x8*)(gb + base + (size_t)s * a.d);
+          kv[s] = *(const s16x8*)(kb + base + (size_t)s * a.d);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < PR; ++s)
+        if (s < a.pool)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gm[e] = fmaxf(gm[e], bf16_bits_to_f32((uint16_t)gv[s][e]));
+#pragma unroll
+      for (int s = 0; s < PR; ++s) {
+        if (s < a.pool) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float w = __expf(bf16_bits_to_f32((uint16_t)gv[s][e]) - gm[e]);
+            sum[e] += w;
+            acc[e] = __builtin_fmaf(w, bf16_bits_to_f32((uint16_t)kv[s][e]), acc[e]);
+          }
+        }
+      }
+    } else {
+      for (int s = 0; s < a.pool; ++s) {
+        const s16x8 g1 = *(const s16x8*)(gb + base + (size_t)s * a.d);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gm[e] = fmaxf(gm[e], bf16_bits_to_f32((uint16_t)g1[e]));
+      }
+      for (int s = 0; s < a.pool; ++s) {
+        const s16x8 g1 = *(const s16x8*)(gb + base + (size_t)s * a.d);
+        const s16x8 k1 = *(const s16x8*)(kb + base + (size_t)s * a.d);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float w = __expf(bf16_bits_to_f32((uint16_t)g1[e]) - gm[e]);
+          sum[e] += w;
+          acc[e] = __builtin_fmaf(w, bf16_bits_to_f32((uint16_t)k1[e]), acc[e]);
+        }
+      }
+    }
+    kpool_store(dst, acc, sum);
   }
 }
 
-// One thread per pool, all queries of the sequence at once (Q <= kMaxIndexerQ); the queries
-// sit in LDS as fp32, the pool's key is read once as 16-byte vectors.
+// Eight lanes per pool: lane i of a pool's group reads 16-byte chunks 8j + i of the fp32 key,
+// so each load instruction reads whole 128-byte lines of eight consecutive pools.  The lane
+// sums its channels for every query (queries in LDS as fp32), the group adds its eight
+// partial sums (butterfly over lanes xor 1, 2, 4), and lane i < Q writes query i's score.
+template <int NCH>  // 16-byte chunks per lane: d / 32
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  __shared__ float qs[kMaxIndexerQ * kMaxIndexerDim];
+  __shared__ f32x4 qs[kMaxIndexerQ * kMaxIndexerDim / 4];
   const int b = blockIdx.y;
-  for (int e = threadIdx.x; e < a.Q * a.d; e += 256)
-    qs[e] = bf16_bits_to_f32(a.q[(size_t)b * a.Q * a.d + e]);
-  __syncthreads();
   const int L = min(a.cache_len[b], a.max_cache_len);
   const int np = min(L / a.pool, a.max_pools);
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= np) return;
-  const f32x4* row = (const f32x4*)(a.pooled + ((size_t)b * a.max_pools + p) * a.d);
-  float acc[kMaxIndexerQ];
+  const int pb = blockIdx.x * kScorePoolsPerBlock;
+  if (pb >= np) return;  // uniform over the block
+  const int d4 = a.d >> 2;
+  for (int e = threadIdx.x; e < a.Q * d4; e += 256) {
+    const uint16_t* src = a.q + ((size_t)b * a.Q * a.d) + 4 * e;
+    qs[e] = f32x4{bf16_bits_to_f32(src[0]), bf16_bits_to_f32(src[1]), bf16_bits_to_f32(src[2]),
+                  bf16_bits_to_f32(src[3])};
+  }
+  __syncthreads();
+  const int i = threadIdx.x & (kScoreLanes - 1);
+  const int pend = min(pb + kScorePoolsPerBlock, np);
+  // a lane group takes kScoreBatch pools 32 apart at once, so all their loads are in flight together
+  for (int p0 = pb + (int)threadIdx.x / kScoreLanes; p0 < pend; p0 += kScoreBatch * (256 / kScoreLanes)) {
+    f32x4 v[kScoreBatch][NCH];
 #pragma unroll
-  for (int i = 0; i < kMaxIndexerQ; ++i) acc[i] = 0.f;
-  for (int c4 = 0; c4 < a.d / 4; ++c4) {
-    const f32x4 v = row[c4];
+    for (int u = 0; u < kScoreBatch; ++u) {
+      const int p = min(p0 + u * (256 / kScoreLanes), pend - 1);
+      const f32x4* row = (const f32x4*)(a.pooled + ((size_t)b * a.max_pools + p) * a.d);
 #pragma unroll
-    for (int i = 0; i < kMaxIndexerQ; ++i) {
-      if (i < a.Q) {
-        const float* qq = qs + i * a.d + 4 * c4;
-        acc[i] = __builtin_fmaf(qq[0], v[0], acc[i]);
-        acc[i] = __builtin_fmaf(qq[1], v[1], acc[i]);
-        acc[i] = __builtin_fmaf(qq[2], v[2], acc[i]);
-        acc[i] = __builtin_fmaf(qq[3], v[3], acc[i]);
+      for (int j = 0; j < NCH; ++j) v[u][j] = row[kScoreLanes * j + i];
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreBatch; ++u) {
+      const int p = p0 + u * (256 / kScoreLanes);
+      float acc[kMaxIndexerQ];
+#pragma unroll
+      for (int q = 0; q < kMaxIndexerQ; ++q) acc[q] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = kScoreLanes * j + i;
+#pragma unroll
+        for (int q = 0; q < kMaxIndexerQ; ++q) {
+          if (q < a.Q) {
+            const f32x4 w = qs[q * d4 + c];
+            acc[q] = __builtin_fmaf(w[0], v[u][j][0], acc[q]);
+            acc[q] = __builtin_fmaf(w[1], v[u][j][1], acc[q]);
+            acc[q] = __builtin_fmaf(w[2], v[u][j][2], acc[q]);
+            acc[q] = __builtin_fmaf(w[3], v[u][j][3], acc[q]);
+          }
+        }
       }
+      float mine = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxIndexerQ; ++q) {
+        if (q < a.Q) {
+          float x = acc[q];
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 4);
+          if (q == i) mine = x;
+        }
+      }
+      if (i < a.Q && p < pend) a.scores[((size_t)b * a.Q + i) * a.max_pools + p] = mine;
     }
   }
-#pragma unroll
-  for (int i = 0; i < kMaxIndexerQ; ++i)
-    if (i < a.Q) a.scores[((size_t)b * a.Q + i) * a.max_pools + p] = acc[i];
 }
 
 // order-preserving unsigned key of an fp32 value (larger float, larger key)
@@ -84,98 +181,149 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// number of set bits of a wave ballot below this lane
-__device__ __forceinline__ int rank_in_wave(uint64_t ballot, int lane) {
-  return __builtin_popcountll(ballot & ((1ull << lane) - 1ull));
+// Exclusive prefix sum of v over the block's 256 threads; `total` receives the block sum.
+// Every thread of the block must call it (it holds two barriers).
+__device__ int block_exclusive_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    const int s = wsum[w];
+    if (w < wave) before += s;
+    total += s;
+  }
+  __syncthreads();  // wsum is rewritten by the next scan
+  return before + x - v;
 }
 
+// One workgroup per (sequence, query).  The selectable pools' scores become order keys in LDS;
+// thread t owns pools 64t .. 64t+63 and visits them rotated by t (slot j -> pool 64t + ((j + t)
+// & 63)), which puts the 64 lanes of a wave in 64 different banks.
+//   1. A radix select over the keys, 11 + 11 + 10 bits from the top, finds the n_sel-th largest
+//      key kth and how many keys equal to it are taken (need_eq).
+//   2. Each thread marks its pools above kth and its keys equal to kth; a block scan over the
+//      equal counts gives the lowest-index-first share of need_eq to each thread, a second scan
+//      over the selected counts gives each thread its place in the output, and the thread writes
+//      its selected pools' positions in ascending order.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ uint32_t keys[kMaxIndexerPools];
-  __shared__ int hist[256];
-  __shared__ int wsum[kSelThreads / 64][2];
-  __shared__ uint32_t s_prefix, s_mask;
-  __shared__ int s_remaining;
+  __shared__ int hist[kHistBins];
+  __shared__ int wsum[kSelThreads / 64];
+  __shared__ int s_digit, s_remaining;
 
   const int bq = blockIdx.x;
   const int b = bq / a.Q, i = bq % a.Q;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int L = min(a.cache_len[b], a.max_cache_len);
   const int t = L - a.Q + i;  // this query's position
   const int np = t >= 0 ? min((t + 1) / a.pool, min(L / a.pool, a.max_pools)) : 0;
   const int n_sel = a.topk / a.pool;
   const float* sc = a.scores + (size_t)bq * a.max_pools;
-  for (int p = tid; p < np; p += kSelThreads) keys[p] = order_key(sc[p]);
-
-  // the threshold key: the n_sel-th largest, found eight bits at a time from the top
-  uint32_t kth = 0;
-  int need_eq = 0;  // keys equal to kth that are taken (lowest pools first)
-  const bool all = np <= n_sel;
-  if (!all) {
-    if (tid == 0) {
-      s_prefix = 0;
-      s_mask = 0;
-      s_remaining = n_sel;
+  // sixteen loads in flight per thread, then sixteen LDS stores
+  for (int base = 0; base < np; base += 16 * kSelThreads) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int p = base + u * kSelThreads + tid;
+      v[u] = p < np ? sc[p] : 0.f;
     }
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int p = base + u * kSelThreads + tid;
+      if (p < np) keys[p] = order_key(v[u]);
+    }
+  }
+  __syncthreads();
+
+  const bool all = np <= n_sel;
+  const int own = kSelPerThread * tid;
+  uint32_t kth = 0;
+  int need_eq = 0;
+  if (!all) {
+    uint32_t prefix = 0, mask = 0;
+    int rem = n_sel;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int nb = pass == 2 ? 1024 : 2048;
+      for (int e = tid; e < nb; e += kSelThreads) hist[e] = 0;
       __syncthreads();
-      const uint32_t prefix = s_prefix, mask = s_mask;
-      for (int p = tid; p < np; p += kSelThreads) {
-        const uint32_t k = keys[p];
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+      for (int j = 0; j < kSelPerThread; ++j) {
+        const int p = own + ((j + tid) & (kSelPerThread - 1));
+        if (p < np) {
+          const uint32_t k = keys[p];
+          if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1);
+        }
       }
       __syncthreads();
-      if (tid == 0) {
-        int rem = s_remaining, cum = 0, digit = 0;
-        for (int dgt = 255; dgt >= 0; --dgt) {
-          if (cum + hist[dgt] >= rem) {
-            digit = dgt;
+      // thread t sums bins nb-1-(per*t) .. nb-per-(per*t) (the top bins first)
+      const int per = nb / kSelThreads;
+      int c = 0;
+      for (int e = 0; e < per; ++e) c += hist[nb - 1 - (per * tid + e)];
+      int total;
+      const int before = block_exclusive_scan(c, wsum, total);
+      if (before < rem && rem <= before + c) {
+        int cum = before;
+        for (int e = 0; e < per; ++e) {
+          const int bin = nb - 1 - (per * tid + e);
+          const int h = hist[bin];
+          if (cum + h >= rem) {
+            s_digit = bin;
+            s_remaining = rem - cum;
             break;
           }
-          cum += hist[dgt];
+          cum += h;
         }
-        s_remaining = rem - cum;
-        s_prefix = prefix | ((uint32_t)digit << shift);
-        s_mask = mask | (255u << shift);
       }
       __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      mask |= (uint32_t)(nb - 1) << shift;
+      rem = s_remaining;
+      __syncthreads();  // s_digit and hist are rewritten by the next pass
     }
-    kth = s_prefix;
-    need_eq = s_remaining;
+    kth = prefix;
+    need_eq = rem;
   }
 
-  // walk the pools in index order, 256 at a time: selected = above the threshold, or equal to
-  // it within the first need_eq equal ones; each selected pool's rank places its positions
+  uint64_t above = 0, eq = 0;
+  for (int j = 0; j < kSelPerThread; ++j) {
+    const int jj = (j + tid) & (kSelPerThread - 1);
+    const int p = own + jj;
+    if (p < np) {
+      const uint32_t k = keys[p];
+      if (all || k > kth)
+        above |= 1ull << jj;
+      else if (k == kth)
+        eq |= 1ull << jj;
+    }
+  }
+  int total;
+  const int n_eq = __builtin_popcountll(eq);
+  const int eq_before = block_exclusive_scan(n_eq, wsum, total);
+  const int take = min(max(need_eq - eq_before, 0), n_eq);
+  uint64_t kept = 0, rest = eq;
+  for (int e = 0; e < take; ++e) {
+    kept |= rest & (~rest + 1ull);  // lowest set bit
+    rest &= rest - 1ull;
+  }
+  uint64_t sel = above | kept;
+  int taken;
+  int r = block_exclusive_scan(__builtin_popcountll(sel), wsum, taken);
   int32_t* out = a.idx + (size_t)bq * a.K_max;
-  int eq_seen = 0, taken = 0;
-  for (int base = 0; base < np; base += kSelThreads) {
-    const int p = base + tid;
-    const bool valid = p < np;
-    const uint32_t k = valid ? keys[p] : 0u;
-    const bool eq = valid && !all && k == kth;
-    const uint64_t beq = __builtin_amdgcn_ballot_w64(eq);
-    if (lane == 0) wsum[wave][0] = __builtin_popcountll(beq);
-    __syncthreads();
-    int eq_off = eq_seen;
-    for (int w = 0; w < wave; ++w) eq_off += wsum[w][0];
-    const int eq_rank = eq_off + rank_in_wave(beq, lane);
-    const bool sel = valid && (all || k > kth || (eq && eq_rank < need_eq));
-    const uint64_t bsel = __builtin_amdgcn_ballot_w64(sel);
-    if (lane == 0) wsum[wave][1] = __builtin_popcountll(bsel);
-    __syncthreads();
-    int sel_off = taken, eq_tot = 0, sel_tot = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-      if (w < wave) sel_off += wsum[w][1];
-      eq_tot += wsum[w][0];
-      sel_tot += wsum[w][1];
-    }
-    if (sel) {
-      const int r = sel_off + rank_in_wave(bsel, lane);
-      for (int u = 0; u < a.pool; ++u) out[r * a.pool + u] = p * a.pool + u;
-    }
-    eq_seen += eq_tot;
-    taken += sel_tot;
-    __syncthreads();  // wsum is rewritten by the next chunk
+  while (sel) {
+    const int jj = __builtin_ctzll(sel);
+    sel &= sel - 1ull;
+    const int p = own + jj;
+    for (int u = 0; u < a.pool; ++u) out[r * a.pool + u] = p * a.pool + u;
+    ++r;
   }
   // the incomplete tail pool, then padding
   const int n_tail = (a.tail && t >= 0) ? t + 1 - np * a.pool : 0;
@@ -189,16 +337,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 
 hipError_t launch_kpool(const KpoolArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<KpoolArgs*>(&a)};
-  const int per_block = 256 / a.d;
+  // about 8192 workgroups in all (32 per CU), each striding over its sequence's pools: enough
+  // to stream a full build, and few enough that an incremental build of a handful of new pools
+  // is not dominated by launching empty workgroups
+  const int per_block = 256 / (a.d / 8);
   const int blocks = (a.max_pools + per_block - 1) / per_block;
-  const dim3 grid(blocks < 4096 ? blocks : 4096, a.B), block(256);
-  return hipLaunchKernel((const void*)&kpool_kernel, grid, block, args, 0, stream);
+  const int per_seq = a.B >= 8192 ? 1 : 8192 / a.B;
+  const dim3 grid(blocks < per_seq ? blocks : per_seq, a.B), block(256);
+  const void* fn = a.pool <= 4 ? (const void*)&kpool_kernel<4>
+                   : a.pool <= 8 ? (const void*)&kpool_kernel<8> : (const void*)&kpool_kernel<0>;
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<ScoreArgs*>(&a)};
-  const dim3 grid((a.max_pools + 255) / 256, a.B), block(256);
-  return hipLaunchKernel((const void*)&score_kernel, grid, block, args, 0, stream);
+  const dim3 grid((a.max_pools + kScorePoolsPerBlock - 1) / kScorePoolsPerBlock, a.B), block(256);
+  const void* fn = a.d == 64 ? (const void*)&score_kernel<2>
+                   : a.d == 128 ? (const void*)&score_kernel<4> : (const void*)&score_kernel<8>;
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {

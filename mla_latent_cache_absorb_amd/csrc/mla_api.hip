@@ -223,7 +223,7 @@ int mla_kpool_keys(const uint16_t* k, const uint16_t* g, int64_t batch_stride, c
   if (!k || !g || !cache_len || !pooled) return MLA_ERR_NULL;
   if (B < 1 || max_cache_len < 1 || pool < 1 || max_pools < 1) return MLA_ERR_SHAPE;
   if (!(d == 64 || d == 128 || d == 256)) return MLA_ERR_SHAPE;
-  if (batch_stride < (int64_t)max_cache_len * d) return MLA_ERR_ARG;
+  if (batch_stride < (int64_t)max_cache_len * d || batch_stride % 8 != 0) return MLA_ERR_ARG;
   if (max_pools < max_cache_len / pool) return MLA_ERR_ARG;
   const int dst = check_device(nullptr);
   if (dst != MLA_OK) return dst;

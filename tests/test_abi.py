@@ -102,6 +102,7 @@ def test_indexer_host_validation(L):
     assert L.mla_kpool_keys(None, fake, 128 * 64, fake, None, 1, 64, 128, 4, fake, 16, None) == binding.MLA_ERR_NULL
     assert L.mla_kpool_keys(fake, fake, 96 * 64, fake, None, 1, 64, 96, 4, fake, 16, None) == binding.MLA_ERR_SHAPE
     assert L.mla_kpool_keys(fake, fake, 128 * 63, fake, None, 1, 64, 128, 4, fake, 16, None) == binding.MLA_ERR_ARG
+    assert L.mla_kpool_keys(fake, fake, 128 * 64 + 4, fake, None, 1, 64, 128, 4, fake, 16, None) == binding.MLA_ERR_ARG
     assert L.mla_kpool_keys(fake, fake, 128 * 64, fake, None, 1, 64, 128, 4, fake, 15, None) == binding.MLA_ERR_ARG
     assert L.mla_indexer_scores(fake, fake, fake, 1, 9, 128, 4, 16, 64, fake, None) == binding.MLA_ERR_SHAPE
     assert L.mla_indexer_scores(fake, None, fake, 1, 4, 128, 4, 16, 64, fake, None) == binding.MLA_ERR_NULL

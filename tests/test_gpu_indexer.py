@@ -46,7 +46,7 @@ def oracle_select_on(scores, lens, Q, pool, topk, tail, width):
     return idx, n
 
 
-@pytest.mark.parametrize("pool,topk,tail", [(4, 16, True), (4, 16, False), (2, 6, True), (8, 64, True)])
+@pytest.mark.parametrize("pool,topk,tail", [(4, 16, True), (4, 16, False), (2, 6, True), (8, 64, True), (16, 64, True)])
 def test_exact_inputs_bit_exact(pool, topk, tail):
     # small integers and equal gates: pooling is an exact mean, scores exact integers with
     # many ties, so the whole indexer must match the oracle bit for bit
@@ -150,3 +150,25 @@ def test_full_size_sampled():
         rs = np.stack([kp.pool_scores(ix.q[b, i], ref) for i in range(spec.q_len)])
         bound = 1e-5 * (np.abs(F(ix.q[b])) @ np.abs(ref).T).max() + 1e-5
         assert np.abs(scores[b, :, :npb] - rs).max() <= bound
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "three_levels", "ties_at_threshold"])
+def test_selection_ties_across_the_whole_row(kind):
+    # up to 16384 selectable pools: the tie group at the threshold spans many threads' pool
+    # ranges, and the lowest-index-first rule must still hold exactly
+    rng = np.random.default_rng(21)
+    B, Q, pool, topk = 2, 2, 4, 2048
+    L = np.array([65536, 40001], np.int32)
+    n_pools = 65536 // pool
+    if kind == "all_equal":
+        s = np.zeros((B, Q, n_pools), np.float32)
+    elif kind == "three_levels":
+        s = rng.integers(0, 3, (B, Q, n_pools)).astype(np.float32) - 1.0
+    else:
+        s = rng.standard_normal((B, Q, n_pools)).astype(np.float32)
+        s[s > 2.2] = 2.2  # a large tie group right at the 512th-largest value
+    idx, n = binding.mla_indexer_select(torch.from_numpy(s).to(DEV), i32(L), 65536, pool, topk, True)
+    torch.cuda.synchronize()
+    ridx, rn = oracle_select_on(s, L, Q, pool, topk, True, topk + pool - 1)
+    np.testing.assert_array_equal(n.cpu().numpy(), rn)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
