@@ -10,3 +10,4 @@ from .mla_oracle import (absorbed_query, bf16_bits_to_f64, cache_bytes_per_token
                          query_position, softmax_attention, up_project, visible_sets)
 from . import kpool_indexer  # noqa: F401  (the k-pooled indexer that produces position lists)
 from . import latent_append  # noqa: F401  (down-projection of new tokens into the cache)
+from . import naive_form  # noqa: F401  (the expanded form, stage by stage)
