@@ -295,6 +295,67 @@ def time_append(steps: int, warmup: int):
     return out
 
 
+CROSSOVER_SHAPES = (("decode", 1, 4096), ("decode", 1, 32768), ("prefill", 1024, 1024), ("prefill", 4096, 4096),
+                    ("prefill", 8192, 8192))
+
+
+def time_crossover(reps: int = 3):
+    """Module 05 section 5's comparison: the absorbed path (absorb_q, latent attention, up_v) and
+    the naive path (expand every cached key and value, then multi-head attention) on one sequence,
+    decode-shaped (one query against a cache of L) and prefill-shaped (L queries, each over its
+    own prefix).  Each form is captured in a HIP graph of `reps` calls and replayed; per-call time
+    from HIP events.  Inputs: torch.randn on the GPU with the workloads' distributions (timing
+    only)."""
+    import torch
+    from mla_latent_cache_absorb_amd import binding, workloads as wl
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0x5C)
+    H, D, R = wl.HEADS, wl.HEAD_DIM, wl.LATENT
+    bf = lambda *shape, std=1.0: (torch.randn(*shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+    w_k, w_v = bf(H, D, R, std=wl.W_STD), bf(H, D, R, std=wl.W_STD)
+    rows = []
+    for kind, Q, L in CROSSOVER_SHAPES:
+        q, cache = bf(1, Q, H, D), bf(1, L, R)
+        cl = torch.full((1,), L, dtype=torch.int32, device=dev)
+        visible = Q * (L - Q) + Q * (Q + 1) // 2        # sum over queries of the positions each sees
+        forms = {
+            "absorbed": lambda: binding.mla_forward(q, w_k, w_v, cache, cl, L, wl.SCALE),
+            "naive": lambda: binding.mla_naive_forward(q, w_k, w_v, cache, cl, L, wl.SCALE),
+        }
+        entry = {"shape": kind, "queries": Q, "cache_len": L}
+        for name, fn in forms.items():
+            fn()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(reps):
+                    fn()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            entry[name + "_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+            del graph
+            torch.cuda.empty_cache()
+        wbytes = 2 * H * D * R * 2                        # U^K and U^V, read once
+        io = Q * H * D * 2 + Q * H * D * 4                # queries in, outputs out
+        entry["absorbed_flops"] = 2 * 2 * Q * H * D * R + 4 * H * R * visible
+        entry["naive_flops"] = 2 * 2 * L * H * D * R + 4 * H * D * visible
+        entry["absorbed_bytes"] = L * R * 2 + wbytes + io
+        # the expanded keys and values are written once and read back once
+        entry["naive_bytes"] = L * R * 2 + wbytes + io + 2 * L * H * D * 2 * 2
+        entry["winner"] = "absorbed" if entry["absorbed_ms"] <= entry["naive_ms"] else "naive"
+        rows.append(entry)
+        del q, cache
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(name: str, budget_s: float = 12.0):
     """The fp64 oracle (expanded form) on whole sequences of the same workload, until about
     budget_s of CPU time has been spent."""
@@ -330,6 +391,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-indexer", action="store_true")
     ap.add_argument("--no-append", action="store_true")
+    ap.add_argument("--no-crossover", action="store_true")
+    ap.add_argument("--crossover-only", action="store_true",
+                    help="time only the absorbed / naive comparison (for profiling it on its own)")
     ap.add_argument("--append-only", action="store_true",
                     help="time only the down-projection with cache append (for profiling it on its own)")
     ap.add_argument("--indexer-only", action="store_true",
@@ -362,6 +426,9 @@ def main():
         log(f"[bench] copied {args.calibrate_copy} MiB three times")
         del src, dst
         torch.cuda.empty_cache()
+    if args.crossover_only:
+        print(json.dumps({"crossover": time_crossover()}), flush=True)
+        return
     if args.append_only:
         print(json.dumps({"append": time_append(args.steps, args.warmup)}), flush=True)
         return
@@ -422,6 +489,9 @@ def main():
     if not args.no_append:
         log("[bench] timing the down-projection with cache append")
         result["append"] = time_append(max(10, args.steps // 2), 3)
+    if not args.no_crossover:
+        log("[bench] timing the absorbed and naive forms at decode and prefill shapes")
+        result["crossover"] = time_crossover()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(args.workload)

@@ -229,6 +229,43 @@ int mla_latent_append(const uint16_t* h, const uint16_t* w_dkv, uint16_t* cache,
                       int32_t max_cache_len, void* stream);
 
 /*
+ * The naive (expanded) form, for comparison with the absorbed one (page "Module 05", section 5:
+ * prefill and decode may prefer different algebra; the naive form expands k_{j,h} and v_{j,h}
+ * for every cached token and runs ordinary multi-head attention).  The two calls below compute
+ * the same attention as mla_absorb_q + mla_latent_attn + mla_up_v, up to rounding: keys and values
+ * are rounded to bf16 after expansion.
+ *
+ * mla_expand_kv: k_{j,h} = U_h^K c_j and v_{j,h} = U_h^V c_j for every position j < cache_len[b]
+ * (fp32 accumulation, nearest-even bf16 out).
+ *   cache, cache_batch_stride, cache_len, max_cache_len   as in mla_latent_attn
+ *   w_k, w_v  [H][D][R] bf16, as in mla_absorb_q / mla_up_v
+ *   k_out     [B][max_cache_len][H][D] bf16 output, position-major (rows past cache_len untouched)
+ *   vt_out    [B][H][D][vt_len] bf16 output: values transposed, each (head, dim) row running over
+ *             positions; vt_len >= max_cache_len and a multiple of 64.  Positions from cache_len[b]
+ *             to the next multiple of 64 are written as zeros (mla_naive_attn reads whole
+ *             64-position spans); later ones are untouched.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ARG (stride or vt_len), MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_expand_kv(const uint16_t* cache, int64_t cache_batch_stride, const int32_t* cache_len, const uint16_t* w_k,
+                  const uint16_t* w_v, int32_t B, int32_t H, int32_t D, int32_t R, int32_t max_cache_len,
+                  uint16_t* k_out, uint16_t* vt_out, int32_t vt_len, void* stream);
+
+/*
+ * mla_naive_attn: causal multi-head attention on the expanded keys and values of mla_expand_kv:
+ * query i of sequence b (position t = cache_len[b] - Q + i) and head h sees k_{j,h}, v_{j,h} for
+ * j <= t; s_j = scale * q . k_j, out = sum_j softmax(s)_j v_j (fp32), lse = ln sum_j exp(s_j).
+ *   q      [B][Q][H][D] bf16 queries (not absorbed)
+ *   k, vt  the outputs of mla_expand_kv for the same cache_len, max_cache_len and vt_len
+ *   out    [B][Q][H][D] fp32;  lse  [B][Q][H] fp32 or NULL
+ * Device-side precondition: Q <= cache_len[b] <= max_cache_len.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ARG (scale, vt_len, max_cache_len < Q),
+ * MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_naive_attn(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int32_t vt_len, const int32_t* cache_len,
+                   int32_t B, int32_t Q, int32_t H, int32_t D, int32_t max_cache_len, float scale, float* out,
+                   float* lse, void* stream);
+
+/*
  * Value up-projection (page "Module 05", section 3: U_h^V factors out of the sum over
  * history, so the accumulated latent is expanded once, at the end).
  *   o_lat  [rows][H][R] fp32   accumulated latents (mla_latent_attn)

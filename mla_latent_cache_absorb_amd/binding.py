@@ -25,7 +25,7 @@ MLA_ERR_DEVICE = -6
 
 EXPORTS = ("mla_status_string", "mla_absorb_q", "mla_latent_attn_num_splits", "mla_latent_attn_workspace_size",
            "mla_latent_attn", "mla_latent_attn_indexed", "mla_up_v", "mla_kpool_keys", "mla_indexer_scores",
-           "mla_indexer_select", "mla_latent_append")
+           "mla_indexer_select", "mla_latent_append", "mla_expand_kv", "mla_naive_attn")
 
 
 class MlaError(RuntimeError):
@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.mla_indexer_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
         L.mla_indexer_scores.restype = ctypes.c_int
         L.mla_indexer_select.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
+        L.mla_expand_kv.restype = ctypes.c_int
+        L.mla_expand_kv.argtypes = [vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, vp]
+        L.mla_naive_attn.restype = ctypes.c_int
+        L.mla_naive_attn.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
         L.mla_latent_append.restype = ctypes.c_int
         L.mla_latent_append.argtypes = [vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, vp]
         L.mla_indexer_select.restype = ctypes.c_int
@@ -228,6 +232,66 @@ def mla_latent_append(h: torch.Tensor, w_dkv: torch.Tensor, cache: torch.Tensor,
     _check(lib().mla_latent_append(_ptr(h), _ptr(w_dkv), _ptr(cache), _cache_stride(cache), _ptr(cache_len), B, Q,
                                    hidden, R, int(max_cache_len), _stream(stream)), "mla_latent_append")
     return cache
+
+
+# ------------------------------------------------------------------------------ the naive form
+def vt_length(max_cache_len: int) -> int:
+    """Positions per row of the transposed value buffer: max_cache_len rounded up to 64."""
+    return (int(max_cache_len) + 63) // 64 * 64
+
+
+def mla_expand_kv(cache: torch.Tensor, cache_len: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
+                  max_cache_len: int, k_out: Optional[torch.Tensor] = None, vt_out: Optional[torch.Tensor] = None,
+                  stream=None):
+    """The naive form's expansion.  cache [B, L, R] bf16, w_k / w_v [H, D, R] bf16 ->
+    (k [B, max_cache_len, H, D] bf16, vt [B, H, D, vt_len] bf16, values transposed)."""
+    _need(cache, torch.bfloat16, "cache", contiguous=False)
+    _need(cache_len, torch.int32, "cache_len")
+    _need(w_k, torch.bfloat16, "w_k")
+    _need(w_v, torch.bfloat16, "w_v")
+    H, D, R = w_k.shape
+    B = cache.shape[0]
+    L = int(max_cache_len)
+    vt_len = vt_length(L)
+    if k_out is None:
+        k_out = torch.empty((B, L, H, D), dtype=torch.bfloat16, device=cache.device)
+    if vt_out is None:
+        vt_out = torch.empty((B, H, D, vt_len), dtype=torch.bfloat16, device=cache.device)
+    _need(k_out, torch.bfloat16, "k_out")
+    _need(vt_out, torch.bfloat16, "vt_out")
+    if k_out.shape != (B, L, H, D) or vt_out.shape != (B, H, D, vt_len):
+        raise ValueError("k_out must be [B, max_cache_len, H, D] and vt_out [B, H, D, vt_length(max_cache_len)]")
+    _check(lib().mla_expand_kv(_ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(w_k), _ptr(w_v), B, H, D, R,
+                               L, _ptr(k_out), _ptr(vt_out), vt_len, _stream(stream)), "mla_expand_kv")
+    return k_out, vt_out
+
+
+def mla_naive_attn(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int,
+                   scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   want_lse: bool = True, stream=None):
+    """Causal multi-head attention on expanded keys and values.  q [B, Q, H, D] bf16; k, vt from
+    mla_expand_kv.  Returns (out [B, Q, H, D] fp32, lse [B, Q, H] fp32 or None)."""
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    _need(vt, torch.bfloat16, "vt")
+    _need(cache_len, torch.int32, "cache_len")
+    B, Q, H, D = q.shape
+    if k.shape != (B, int(max_cache_len), H, D) or vt.shape[:3] != (B, H, D):
+        raise ValueError("k / vt do not match q and max_cache_len")
+    if out is None:
+        out = torch.empty((B, Q, H, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device)
+    _check(lib().mla_naive_attn(_ptr(q), _ptr(k), _ptr(vt), vt.shape[3], _ptr(cache_len), B, Q, H, D,
+                                int(max_cache_len), float(scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "mla_naive_attn")
+    return out, lse
+
+
+def mla_naive_forward(q, w_k, w_v, cache, cache_len, max_cache_len, scale, stream=None):
+    """The whole naive path: expand keys and values, then attention.  Returns (out, lse)."""
+    k, vt = mla_expand_kv(cache, cache_len, w_k, w_v, max_cache_len, stream=stream)
+    return mla_naive_attn(q, k, vt, cache_len, max_cache_len, scale, stream=stream)
 
 
 # ---------------------------------------------------------------------------- k-pooled indexer

@@ -38,19 +38,6 @@ __device__ __forceinline__ f32x4 mfma16x16(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// lane-addressed copy of 16 bytes from `src` to lds + 16 * lane (lds wave-uniform); the caller
-// waits (vmcnt) before reading the copy
-__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
-  const uint32_t ls = __builtin_amdgcn_readfirstlane(lds);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(ls), "v"(src) : "memory", "m0");
-#pragma clang diagnostic pop
-}
-
-// s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned
-__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
 // Stage 16 rows' K-slices (row r at `rows + r * kHidden` elements) into this wave's LDS stage.
 // Copy j moves rows 2j and 2j+1: lane l takes row 2j + (l >> 5) and fills slot l & 31 with chunk
 // (l & 31) ^ row.  Rows at or past nrows_valid are read from the last valid row.

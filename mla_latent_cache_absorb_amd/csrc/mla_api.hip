@@ -274,6 +274,39 @@ int mla_latent_append(const uint16_t* h, const uint16_t* w_dkv, uint16_t* cache,
   return MLA_OK;
 }
 
+int mla_expand_kv(const uint16_t* cache, int64_t cache_batch_stride, const int32_t* cache_len, const uint16_t* w_k,
+                  const uint16_t* w_v, int32_t B, int32_t H, int32_t D, int32_t R, int32_t max_cache_len,
+                  uint16_t* k_out, uint16_t* vt_out, int32_t vt_len, void* stream) {
+  if (!cache || !cache_len || !w_k || !w_v || !k_out || !vt_out) return MLA_ERR_NULL;
+  if (!supported(H, D, R) || B < 1 || max_cache_len < 1) return MLA_ERR_SHAPE;
+  if (cache_batch_stride < (int64_t)max_cache_len * R || vt_len < max_cache_len || vt_len % 64 != 0)
+    return MLA_ERR_ARG;
+  if ((max_cache_len + 127) / 128 > 65535 || B > 65535) return MLA_ERR_SHAPE;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  const int32_t HD = H * D;
+  mla::ExpandArgs a{(const uint8_t*)cache, cache_batch_stride * 2, cache_len, w_k, w_v,
+                    k_out, (int64_t)max_cache_len * HD, vt_out, (int64_t)HD * vt_len, vt_len,
+                    B, HD, max_cache_len};
+  return mla::launch_expand_kv(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_naive_attn(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int32_t vt_len, const int32_t* cache_len,
+                   int32_t B, int32_t Q, int32_t H, int32_t D, int32_t max_cache_len, float scale, float* out,
+                   float* lse, void* stream) {
+  if (!q || !k || !vt || !cache_len || !out) return MLA_ERR_NULL;
+  if (!supported(H, D, 512) || B < 1 || Q < 1 || max_cache_len < 1) return MLA_ERR_SHAPE;
+  if ((int64_t)B * Q * H > 0x7fffffff || B > 65535 || H > 65535) return MLA_ERR_SHAPE;
+  if (max_cache_len < Q || vt_len < max_cache_len || vt_len % 64 != 0) return MLA_ERR_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return MLA_ERR_ARG;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  const int32_t HD = H * D;
+  mla::NaiveArgs a{q, k, (int64_t)max_cache_len * HD, vt, (int64_t)HD * vt_len, vt_len, cache_len,
+                   B, Q, H, HD, max_cache_len, scale * 1.4426950408889634f, out, lse};
+  return mla::launch_naive_attn(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, int32_t H, int32_t D, int32_t R,
              void* stream) {
   if (!o_lat || !w_v || !out) return MLA_ERR_NULL;

@@ -123,6 +123,21 @@ __device__ __forceinline__ void row_to_lds_at(const uint8_t* base, uint32_t off,
 #pragma clang diagnostic pop
 }
 
+// Lane-addressed copy of 16 bytes from `src` (any per-lane address) to lds + 16 * lane, `lds`
+// wave-uniform, without passing through registers.  Issued from asm so that the compiler does not
+// wait for it before unrelated LDS reads: the caller waits (vmcnt) before reading the copy.  M0 is
+// clobbered, as in row_to_lds.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+  const uint32_t ls = __builtin_amdgcn_readfirstlane(lds);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(ls), "v"(src) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // acc *= alpha for an MFMA accumulator that lives in AGPRs, done in place (read, multiply,
 // write back one register at a time).  Written in asm so that the only other uses of the
 // accumulator are matrix-core operands and the compiler keeps it in AGPRs instead of copying

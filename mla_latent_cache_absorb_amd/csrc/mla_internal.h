@@ -80,6 +80,36 @@ struct DownArgs {
 int down_row_groups(int rows);
 hipError_t launch_latent_down(const DownArgs& a, hipStream_t stream);
 
+// ---- the naive (expanded) form
+struct ExpandArgs {
+  const uint8_t* cache;          // latent rows (bytes)
+  int64_t cache_bstride_bytes;
+  const int32_t* cache_len;      // [B]
+  const uint16_t* w_k;           // [H*D][R]
+  const uint16_t* w_v;           // [H*D][R]
+  uint16_t* k_out;               // [B][max_cache_len][H*D]
+  int64_t k_bstride;             // elements
+  uint16_t* v_out;               // [B][H*D][vt_len] (values transposed)
+  int64_t vt_bstride;            // elements
+  int32_t vt_len;                // positions per transposed row, a multiple of 64
+  int32_t B, HD, max_cache_len;
+};
+struct NaiveArgs {
+  const uint16_t* q;             // [B][Q][H][D] bf16
+  const uint16_t* k;             // as ExpandArgs::k_out
+  int64_t k_bstride;
+  const uint16_t* vt;            // as ExpandArgs::v_out
+  int64_t vt_bstride;
+  int32_t vt_len;
+  const int32_t* cache_len;
+  int32_t B, Q, H, HD, max_cache_len;
+  float scale_log2;              // softmax scale * log2(e)
+  float* out;                    // [B][Q][H][D] fp32
+  float* lse;                    // [B][Q][H] or null
+};
+hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t stream);
+hipError_t launch_naive_attn(const NaiveArgs& a, hipStream_t stream);
+
 hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int rows, int H,
                            float prescale, hipStream_t stream);
 hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H,

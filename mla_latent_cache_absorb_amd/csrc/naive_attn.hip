@@ -1,0 +1,317 @@
+// The naive (expanded) form of MLA attention for gfx950, the other side of the prefill / decode
+// comparison of page "Module 05 -- MLA: Compressing Per-Token History", section 5: expand every
+// cached token's per-head key and value, k_{j,h} = U_h^K c_j and v_{j,h} = U_h^V c_j (section 1),
+// then run ordinary causal multi-head attention on them (section 4: a query sees j <= t).
+//
+// expand_kv_kernel   one GEMM per operand: [positions x 512] latents times the [H*D x 512]
+//                    weights (U_h stored [D][R] per head, so row h*D + d is U_h[d][:]), fp32
+//                    accumulation, nearest-even bf16 out.  Keys are written position-major,
+//                    K[b][j][h][d]; values head-major and transposed, V^T[b][h][d][j], so that the
+//                    attention's value product reads them along positions.
+// naive_attn_kernel  flash attention with head dimension 256: per (sequence, head, 128 queries),
+//                    eight waves of 16 queries each over 64-key tiles staged in LDS.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+// ---------------------------------------------------------------------------------- expansion
+constexpr int kExpTile = 128;                    // positions and channels per workgroup
+constexpr int kExpK = 64;                        // latents per stage
+constexpr int kExpStages = kLatent / kExpK;      // 8
+constexpr int kExpRowBytes = kExpK * 2;          // 128 bytes: 8 chunks of 16
+constexpr int kExpTileBytes = kExpTile * kExpRowBytes;
+
+// chunk c of tile row r sits at slot c ^ ((r >> 1) & 7): sixteen consecutive rows at one chunk
+// (an MFMA operand read) then fall in sixteen different 16-byte bank groups
+__device__ __forceinline__ int row128_swz(int r) { return (r >> 1) & 7; }
+
+// VT = false: D[channel][position], each lane holds 4 consecutive channels of one position (keys,
+// position-major rows).  VT = true: D[position][channel], 4 consecutive positions of one channel
+// (values, transposed).
+template <bool VT>
+__global__ __launch_bounds__(256) void expand_kv_kernel(ExpandArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kExpTileBytes];  // [buffer][W, latents]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kExpTile;          // weight rows (h*D + d)
+  const int m0 = blockIdx.y * kExpTile;          // positions
+  const int b = blockIdx.z;
+  const int L = min(a.cache_len[b], a.max_cache_len);
+  if (m0 >= L) return;  // uniform over the block
+  const uint16_t* w = (VT ? a.w_v : a.w_k) + (size_t)n0 * kLatent;
+  const uint8_t* c = a.cache + (size_t)b * a.cache_bstride_bytes;
+
+  // each copy instruction moves 8 rows x 128 bytes; wave w moves rows 32w .. 32w+31 of both tiles
+  auto issue = [&](int st, int buf) {
+    const int kb = st * kExpRowBytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = wave * 4 + u;
+      const int r = 8 * j + (lane >> 3);
+      const int chunk = (lane & 7) ^ row128_swz(r);
+      copy16_to_lds((const uint8_t*)(w + (size_t)r * kLatent) + kb + 16 * chunk, lds_addr(&lds[buf][0][1024 * j]));
+      const int pr = min(m0 + r, L - 1);
+      copy16_to_lds(c + (size_t)pr * kRowBytes + kb + 16 * chunk, lds_addr(&lds[buf][1][1024 * j]));
+    }
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;       // this wave: positions 64wm.., channels 64wn..
+  const int r32 = lane & 31, kg = lane >> 5;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
+
+  issue(0, 0);
+  for (int st = 0; st < kExpStages; ++st) {
+    const int buf = st & 1;
+    wait_vmcnt<0>();
+    __syncthreads();  // stage st landed for every wave; every wave is done reading the other buffer
+    if (st + 1 < kExpStages) issue(st + 1, buf ^ 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {  // k-steps of 16 latents: chunk 2s + kg
+      const int chunk = 2 * s + kg;
+      bf16x8 fw[2], fc[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int rw = 64 * wn + 32 * x + r32;
+        const int rc = 64 * wm + 32 * x + r32;
+        fw[x] = *(const bf16x8*)&lds[buf][0][rw * kExpRowBytes + 16 * (chunk ^ row128_swz(rw))];
+        fc[x] = *(const bf16x8*)&lds[buf][1][rc * kExpRowBytes + 16 * (chunk ^ row128_swz(rc))];
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          if constexpr (VT)
+            acc[x][y] = mfma32(fc[x], fw[y], acc[x][y]);  // [positions x][channels y]
+          else
+            acc[x][y] = mfma32(fw[x], fc[y], acc[x][y]);  // [channels x][positions y]
+        }
+    }
+  }
+
+  // D lane layout: column lane & 31, rows 8i + 4kg + j
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc[x][y][4 * i]) |
+                            ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * i + 1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc[x][y][4 * i + 2]) |
+                            ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * i + 3]) << 16);
+        const uint2 v = {lo, hi};
+        if constexpr (VT) {
+          // rows: positions 64wm + 32x + 8i + 4kg + j; column: channel 64wn + 32y + r32
+          const int m = m0 + 64 * wm + 32 * x + 8 * i + 4 * kg;
+          const int n = n0 + 64 * wn + 32 * y + r32;
+          const int h = n / kHeadDim, d = n % kHeadDim;
+          uint16_t* dst = a.v_out + (size_t)b * a.vt_bstride + ((size_t)h * kHeadDim + d) * a.vt_len + m;
+          // positions from L up to the next multiple of 64 get zeros: the attention reads whole
+          // 64-position spans and multiplies them by zero weights, which must not meet a NaN
+          const int pad_end = min((L + 63) & ~63, a.vt_len);
+          if (m + 3 < L) {
+            *(uint2*)dst = v;
+          } else if (m < pad_end) {
+            const uint64_t keep = m >= L ? 0ull : (~0ull >> (16 * (4 - (L - m))));
+            const uint64_t w64 = ((uint64_t)hi << 32 | lo) & keep;
+            *(uint2*)dst = uint2{(uint32_t)w64, (uint32_t)(w64 >> 32)};
+          }
+        } else {
+          const int n = n0 + 64 * wn + 32 * x + 8 * i + 4 * kg;
+          const int m = m0 + 64 * wm + 32 * y + r32;
+          if (m < L) *(uint2*)(a.k_out + (size_t)b * a.k_bstride + (size_t)m * a.HD + n) = v;
+        }
+      }
+}
+
+// ------------------------------------------------------------------------------ attention
+constexpr int kNaWaves = 8;
+constexpr int kNaQ = 16 * kNaWaves;        // queries per workgroup
+constexpr int kNaKeys = 64;                // keys per tile
+constexpr int kNaKRow = kHeadDim * 2;      // 512-byte key rows
+constexpr int kNaVRow = kNaKeys * 2;       // 128-byte rows of the transposed value tile
+constexpr int kNaStage = kNaKeys * kNaKRow;  // 32 KiB, and the same for the value tile
+constexpr int kNaPStride = 72;             // bf16 per P row (64 + 8 pad: conflict-free)
+constexpr float kNaRescale = 8.f;          // lazy rescale threshold, log2 units
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 (one query column of a 16x16 result)
+__device__ __forceinline__ float col_max(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  u = __builtin_bit_cast(unsigned, x);
+  auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)t[0]), __builtin_bit_cast(float, (unsigned)t[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  u = __builtin_bit_cast(unsigned, x);
+  auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)t[0]) + __builtin_bit_cast(float, (unsigned)t[1]);
+}
+
+__global__ __launch_bounds__(64 * kNaWaves) void naive_attn_kernel(NaiveArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[2][kNaStage];   // keys [64][256], swizzled
+  __shared__ __attribute__((aligned(1024))) uint8_t vt[2][kNaStage];   // values^T [256][64], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t pb[kNaWaves][16 * kNaPStride];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i0 = blockIdx.x * kNaQ;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int L = min(a.cache_len[b], a.max_cache_len);
+  const int ql = lane & 15, g = lane >> 4;
+  const int qi = i0 + 16 * wave + ql;              // this lane's query column
+  const int t = L - a.Q + qi;                      // its position
+  const int t_last = L - a.Q + min(i0 + kNaQ - 1, a.Q - 1);
+  const int ntiles = t_last >= 0 ? t_last / kNaKeys + 1 : 0;
+
+  const uint8_t* kbase = (const uint8_t*)(a.k + (size_t)b * a.k_bstride + (size_t)h * kHeadDim);
+  const uint8_t* vbase = (const uint8_t*)(a.vt + (size_t)b * a.vt_bstride + (size_t)h * kHeadDim * a.vt_len);
+  // copies: key tile = 32 instructions of two 512-byte rows, value tile = 32 of eight 128-byte
+  // rows; wave w issues instructions 4w .. 4w+3 of each
+  auto issue = [&](int tile, int buf) {
+    const int key0 = tile * kNaKeys;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = wave * 4 + u;
+      {
+        const int r = 2 * j + (lane >> 5);
+        const int key = min(key0 + r, L - 1);
+        const int chunk = (lane & 31) ^ (r & 15);
+        copy16_to_lds(kbase + (size_t)key * a.HD * 2 + 16 * chunk, lds_addr(&kt[buf][1024 * j]));
+      }
+      {
+        const int r = 8 * j + (lane >> 3);  // head dimension row of V^T
+        const int chunk = (lane & 7) ^ row128_swz(r);
+        // positions key0 .. key0+63 (vt_len is a multiple of 64, so the span is inside the row;
+        // positions from the length to the next multiple of 64 hold zeros, written by the expansion)
+        copy16_to_lds(vbase + ((size_t)r * a.vt_len + key0) * 2 + 16 * chunk, lds_addr(&vt[buf][1024 * j]));
+      }
+    }
+  };
+
+  // queries as the B operand of S^T = K Q^T: lane (column q, group g) holds d = 32s + 8g .. +7
+  bf16x8 qf[8];
+  {
+    const int qc = min(qi, a.Q - 1);
+    const uint16_t* src = a.q + (((size_t)b * a.Q + qc) * a.H + h) * kHeadDim + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *(const bf16x8*)(src + 32 * s);
+  }
+  f32x4 o[16];
+#pragma unroll
+  for (int db = 0; db < 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  uint16_t* pw = pb[wave];
+
+  if (ntiles > 0) issue(0, 0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tile + 1 < ntiles) issue(tile + 1, buf ^ 1);
+    const int key0 = tile * kNaKeys;
+    // S^T[64 keys x 16 queries]: lane holds keys 16kb + 4g + j of column q
+    f32x4 sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * kb + ql;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 kf = *(const bf16x8*)&kt[buf][r * kNaKRow + 16 * ((4 * s + g) ^ (r & 15))];
+        sc[kb] = mfma16(kf, qf[s], sc[kb]);
+      }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = key0 + 16 * kb + 4 * g + j;
+        const float v = (key <= t && key < L) ? sc[kb][j] * a.scale_log2 : -INFINITY;
+        sc[kb][j] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = col_max(mt);
+    // lazy rescale: move the running maximum only when the tile's exceeds it by 2^8
+    const bool grow = mt > m_run + kNaRescale;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = grow ? exp2f(m_run - m_new) : 1.f;  // 0 on the first tile (m_run = -inf)
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    // P = exp2(s - m), bf16, to this wave's LDS rows (query q, keys 16kb + 4g .. +3)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = exp2f(sc[kb][j] - m_run);
+        l_run += p[j];
+      }
+      const uint32_t lo = (uint32_t)f32_to_bf16_bits(p[0]) | ((uint32_t)f32_to_bf16_bits(p[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_bits(p[2]) | ((uint32_t)f32_to_bf16_bits(p[3]) << 16);
+      *(uint2*)&pw[ql * kNaPStride + 16 * kb + 4 * g] = uint2{lo, hi};
+    }
+    // P^T as the B operand: lane (q, g) holds keys 32ks + 8g .. +7 of its query
+    bf16x8 pf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pf[ks] = *(const bf16x8*)&pw[ql * kNaPStride + 32 * ks + 8 * g];
+    // O^T[256 d x 16 q] += V^T[256 x 64] P^T[64 x 16]; A operand: row d = 16db + ql, keys 32ks + 8g
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+      const int r = 16 * db + ql;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 vf = *(const bf16x8*)&vt[buf][r * kNaVRow + 16 * ((4 * ks + g) ^ row128_swz(r))];
+        o[db] = mfma16(vf, pf[ks], o[db]);
+      }
+    }
+  }
+
+  const float l_all = col_sum(l_run);
+  if (qi < a.Q) {
+    const float inv = 1.f / l_all;
+    float* dst = a.out + (((size_t)b * a.Q + qi) * a.H + h) * kHeadDim + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) *(f32x4*)(dst + 16 * db) = o[db] * inv;
+    if (a.lse && g == 0) a.lse[((size_t)b * a.Q + qi) * a.H + h] = (m_run + __log2f(l_all)) * 0.69314718055994531f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<ExpandArgs*>(&a)};
+  const dim3 grid(a.HD / kExpTile, (a.max_cache_len + kExpTile - 1) / kExpTile, a.B), block(256);
+  hipError_t e = hipLaunchKernel((const void*)&expand_kv_kernel<false>, grid, block, args, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)&expand_kv_kernel<true>, grid, block, args, 0, stream);
+}
+
+hipError_t launch_naive_attn(const NaiveArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<NaiveArgs*>(&a)};
+  const dim3 grid((a.Q + kNaQ - 1) / kNaQ, a.H, a.B), block(64 * kNaWaves);
+  return hipLaunchKernel((const void*)&naive_attn_kernel, grid, block, args, 0, stream);
+}
+
+}  // namespace mla
