@@ -2,10 +2,12 @@
 // Per-Token History", section 3: U_h^V does not depend on the position, so it factors out of
 // the weighted sum and the accumulated latent is expanded once).
 //
-// Per head, out^T[D x rows] = U_h^V[D x R] . o_lat^T[R x rows].  U^V, stored [D][R] per head,
-// is the A operand as it lies in memory (16-byte loads along R); the fp32 latents are the B
-// operand, each split into two bf16 terms (hi = bf16(x), lo = bf16(x - hi)) and multiplied
-// twice, so the result keeps about 16 bits of o_lat.  Bound by reading U^V (16 MiB).
+// Per head, out^T[D x rows] = U_h^V[D x R] . o_lat^T[R x rows].  A workgroup owns one head and 64
+// output dims, four waves of 16.  U^V rows are the A operand, loaded straight into registers (16
+// dims x 512 latents per wave, 64 VGPRs) and kept for every row.  The fp32 latents of 32 rows are
+// staged once per workgroup in LDS, each split into two bf16 terms (hi = bf16(x), lo = bf16(x -
+// hi)), and read as the B operand of two MFMA 16x16x32 per k-step, so the result keeps about 16
+// bits of o_lat.  Bound by reading U^V (16 MiB) at decode sizes.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -13,56 +15,82 @@ namespace mla {
 
 namespace {
 
-constexpr int kDBlock = 64;   // output dims per workgroup (32 per wave)
-constexpr int kThreads = 128;
+constexpr int kDBlock = 64;           // output dims per workgroup (16 per wave)
+constexpr int kUpWaves = 4;
+constexpr int kThreads = 64 * kUpWaves;
+constexpr int kUpRows = 32;           // o_lat rows staged per pass
+constexpr int kMaxRowGroups = 32;
+
+__device__ __forceinline__ f32x4 mfma16x16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS rows of 512 bf16 (64 chunks of 16 bytes); chunk c of row r at slot c ^ (r & 15), so the
+// B-operand reads (16 consecutive rows at one chunk) fall in sixteen different bank groups
+__device__ __forceinline__ int up_slot(int r, int c) { return c ^ (r & 15); }
 
 __global__ __launch_bounds__(kThreads) void up_v_kernel(const float* __restrict__ o_lat,
                                                         const uint16_t* __restrict__ w_v,
                                                         float* __restrict__ out, int rows, int H) {
+  __shared__ __attribute__((aligned(1024))) uint8_t hi_t[kUpRows * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lo_t[kUpRows * kRowBytes];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ndb = kHeadDim / kDBlock;
   const int h = blockIdx.x / ndb;
-  const int d0 = (blockIdx.x % ndb) * kDBlock + 32 * wave;
-  const int hl = lane & 31, hf = lane >> 5;
+  const int d0 = (blockIdx.x % ndb) * kDBlock + 16 * wave;
+  const int ql = lane & 15, g = lane >> 4;
 
-  // A operand: U_h^V row d0 + hl, latents 16ks + 8hf .. +7
-  bf16x8 wa[32];
-  const uint16_t* wrow = w_v + ((size_t)h * kHeadDim + d0 + hl) * kLatent + 8 * hf;
+  // A operand: U_h^V row d0 + ql, latents 32s + 8g .. +7
+  bf16x8 wa[16];
+  {
+    const uint16_t* wrow = w_v + ((size_t)h * kHeadDim + d0 + ql) * kLatent + 8 * g;
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks) wa[ks] = *(const bf16x8*)(wrow + 16 * ks);
+    for (int s = 0; s < 16; ++s) wa[s] = *(const bf16x8*)(wrow + 32 * s);
+  }
 
-  const int nblocks = (rows + 31) / 32;
-  for (int nb = 0; nb < nblocks; ++nb) {
-    const int row = nb * 32 + hl;
-    const bool rvalid = row < rows;
-    const float* src = o_lat + ((size_t)(rvalid ? row : 0) * H + h) * kLatent + 8 * hf;
-    f32x16 acc;
+  const int npass = (rows + kUpRows - 1) / kUpRows;
+  for (int pass = blockIdx.y; pass < npass; pass += gridDim.y) {
+    const int row0 = pass * kUpRows;
+    __syncthreads();  // the previous pass's reads are done
+    // stage rows row0 .. row0+31: task t = 8 consecutive latents (chunk t % 64) of row t / 64
 #pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = 0.f;
-#pragma unroll 8
-    for (int ks = 0; ks < 32; ++ks) {
-      const f32x4 x0 = *(const f32x4*)(src + 16 * ks);
-      const f32x4 x1 = *(const f32x4*)(src + 16 * ks + 4);
-      bf16x8 hi, lo;
+    for (int k = 0; k < kUpRows * 64 / kThreads; ++k) {
+      const int task = threadIdx.x + kThreads * k;
+      const int r = task >> 6, c = task & 63;
+      const int row = row0 + r;
+      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+      if (row < rows) {
+        const float* src = o_lat + ((size_t)row * H + h) * kLatent + 8 * c;
+        x0 = *(const f32x4*)src;
+        x1 = *(const f32x4*)(src + 4);
+      }
+      bf16x8 vh, vl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = rvalid ? (e < 4 ? x0[e] : x1[e - 4]) : 0.f;
+        const float x = e < 4 ? x0[e] : x1[e - 4];
         const __bf16 bh = (__bf16)x;
-        hi[e] = bh;
-        lo[e] = (__bf16)(x - (float)bh);
+        vh[e] = bh;
+        vl[e] = (__bf16)(x - (float)bh);
       }
-      acc = mfma32(wa[ks], hi, acc);
-      acc = mfma32(wa[ks], lo, acc);
+      const int off = r * kRowBytes + 16 * up_slot(r, c);
+      *(bf16x8*)(hi_t + off) = vh;
+      *(bf16x8*)(lo_t + off) = vl;
     }
-    if (rvalid) {
-      // lane holds query row `row`, output dims d0 + 8ii + 4hf + j
-      float* dst = out + ((size_t)row * H + h) * kHeadDim + d0 + 4 * hf;
+    __syncthreads();
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        f32x4 v = {acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]};
-        *(f32x4*)(dst + 8 * ii) = v;
+    for (int rb = 0; rb < kUpRows / 16; ++rb) {
+      const int r = 16 * rb + ql;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int off = r * kRowBytes + 16 * up_slot(r, 4 * s + g);
+        acc = mfma16x16(wa[s], *(const bf16x8*)(hi_t + off), acc);
+        acc = mfma16x16(wa[s], *(const bf16x8*)(lo_t + off), acc);
       }
+      // lane holds row row0 + r, output dims d0 + 4g .. +3
+      const int row = row0 + r;
+      if (row < rows) *(f32x4*)(out + ((size_t)row * H + h) * kHeadDim + d0 + 4 * g) = acc;
     }
   }
 }
@@ -72,7 +100,8 @@ __global__ __launch_bounds__(kThreads) void up_v_kernel(const float* __restrict_
 hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H,
                        hipStream_t stream) {
   void* args[] = {(void*)&o_lat, (void*)&w_v, (void*)&out, (void*)&rows, (void*)&H};
-  const dim3 grid(H * (kHeadDim / kDBlock)), block(kThreads);
+  const int npass = (rows + kUpRows - 1) / kUpRows;
+  const dim3 grid(H * (kHeadDim / kDBlock), npass < kMaxRowGroups ? npass : kMaxRowGroups), block(kThreads);
   return hipLaunchKernel((const void*)&up_v_kernel, grid, block, args, 0, stream);
 }
 
