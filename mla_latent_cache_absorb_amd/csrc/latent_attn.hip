@@ -162,6 +162,10 @@ void latent_attn_kernel(AttnArgs a) {
     __syncthreads();  // the first two tiles have landed (copied by the value waves)
 
     for (int t = 0; t <= ntiles; ++t) {
+      // the previous step's P and rescale factors must be in LDS before the value waves pass
+      // this barrier: the compiler places no LDS wait before a barrier reached along the loop's
+      // back edge, so it is made explicit
+      wait_lds_reads();
       __syncthreads();  // step t opens: tile t is in LDS; the value waves read P of step t-1
       if (t == ntiles) break;
       const uint8_t* rb = smem[t % kRing] + qk_lane;
