@@ -30,6 +30,23 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
   const int h = blockIdx.x / nrb;
   const int r0 = (blockIdx.x % nrb) * kRBlock;
 
+  const int hl = lane & 31, hf = lane >> 5;
+  const int nblocks = (rows + 31) / 32;
+  // queries of row block nb as the B operand: lane (row hl, half hf) holds d = 16ks + 8hf .. +7
+  bf16x8 bq[16];
+  auto load_q = [&](int nb) {
+    const int row = nb * 32 + hl;
+    const bool rvalid = row < rows;
+    const uint16_t* qsrc = q + ((size_t)(rvalid ? row : 0) * H + h) * kHeadDim + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      bf16x8 v = *(const bf16x8*)(qsrc + 16 * ks);
+      if (!rvalid) v = (bf16x8)(s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      bq[ks] = v;
+    }
+  };
+  load_q(0);  // issued before the slab copies, so the two memory latencies overlap
+
   // stage U_h^K[0:256][r0:r0+128]: one instruction moves 4 d-rows (lane s: row 4k + s/16,
   // chunk slot s%16 holds global chunk (s%16) ^ swz(row))
   {
@@ -46,22 +63,13 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
   wait_vmcnt<0>();
   __syncthreads();
 
-  const int hl = lane & 31, hf = lane >> 5;
   // transpose-read addressing: group g = lane/16 supplies d-rows 16ks + 8(g/2) + 4r2 + e and
   // latent columns 32mb + 16(g&1) + 4c of the slab
   const int g = lane >> 4, ip = lane & 15, te = ip >> 2, tc = ip & 3;
-  const int nblocks = (rows + 31) / 32;
   for (int nb = 0; nb < nblocks; ++nb) {
     const int row = nb * 32 + hl;
     const bool rvalid = row < rows;
-    bf16x8 bq[16];
-    const uint16_t* qsrc = q + ((size_t)(rvalid ? row : 0) * H + h) * kHeadDim + 8 * hf;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      bf16x8 v = *(const bf16x8*)(qsrc + 16 * ks);
-      if (!rvalid) v = (bf16x8)(s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-      bq[ks] = v;
-    }
+    if (nb > 0) load_q(nb);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int mb = 2 * wave + m;
