@@ -111,7 +111,7 @@ void latent_attn_kernel(AttnArgs a) {
   const int wg = xcd_remap(blockIdx.x, a.total_wg);
   // logical order (b, head group, split, query): the queries of one split of one sequence are
   // adjacent, so they run on the same XCD and share the tile through its L2
-  const int i = wg % a.Q;
+  const int i = a.Q - 1 - wg % a.Q;  // later queries see more positions: they start first
   int rest = wg / a.Q;
   const int split = rest % a.num_splits;
   rest /= a.num_splits;
