@@ -21,14 +21,14 @@ namespace mla {
 
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 512;
 constexpr int kSelPerThread = kMaxIndexerPools / kSelThreads;  // pools owned by one thread
 constexpr int kHistBins = 2048;
 constexpr int kScoreLanes = 8;        // lanes that share one pool's key
 constexpr int kScoreBatch = 4;        // pools per lane group in flight together
 constexpr int kScorePoolsPerBlock = 256;
 
-static_assert(kSelPerThread == 64, "the selection keeps one 64-bit mask per thread");
+static_assert(kSelPerThread == 32, "the selection keeps one 32-bit mask per thread");
 
 // Eight channels per thread (16-byte loads of keys and gate logits): d / 8 threads per pool.
 // Per channel: gm = max_s g, e_s = exp(g_s - gm), pooled = (sum_s e_s k_s) / (sum_s e_s).
@@ -112,7 +112,9 @@ __global__ __launch_bounds__(256) void kpool_kernel(KpoolArgs a) {
 // so each load instruction reads whole 128-byte lines of eight consecutive pools.  The lane
 // sums its channels for every query (queries in LDS as fp32), the group adds its eight
 // partial sums (butterfly over lanes xor 1, 2, 4), and lane i < Q writes query i's score.
-template <int NCH>  // 16-byte chunks per lane: d / 32
+// NCH: 16-byte chunks per lane (d / 32).  QR > 0: every query (Q <= QR) is copied from LDS to
+// registers once, so the inner loop reads no LDS; QR = 0 reads the queries from LDS per pool.
+template <int NCH, int QR>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __shared__ f32x4 qs[kMaxIndexerQ * kMaxIndexerDim / 4];
   const int b = blockIdx.y;
@@ -129,6 +131,14 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __syncthreads();
   const int i = threadIdx.x & (kScoreLanes - 1);
   const int pend = min(pb + kScorePoolsPerBlock, np);
+  constexpr int kQ = QR > 0 ? QR : kMaxIndexerQ;  // queries the loops run over
+  f32x4 qreg[QR > 0 ? NCH : 1][QR > 0 ? QR : 1];
+  if constexpr (QR > 0) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int q = 0; q < QR; ++q) qreg[j][q] = q < a.Q ? qs[q * d4 + kScoreLanes * j + i] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   // a lane group takes kScoreBatch pools 32 apart at once, so all their loads are in flight together
   for (int p0 = pb + (int)threadIdx.x / kScoreLanes; p0 < pend; p0 += kScoreBatch * (256 / kScoreLanes)) {
     f32x4 v[kScoreBatch][NCH];
@@ -142,16 +152,20 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int u = 0; u < kScoreBatch; ++u) {
       const int p = p0 + u * (256 / kScoreLanes);
-      float acc[kMaxIndexerQ];
+      float acc[kQ];
 #pragma unroll
-      for (int q = 0; q < kMaxIndexerQ; ++q) acc[q] = 0.f;
+      for (int q = 0; q < kQ; ++q) acc[q] = 0.f;
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = kScoreLanes * j + i;
 #pragma unroll
-        for (int q = 0; q < kMaxIndexerQ; ++q) {
+        for (int q = 0; q < kQ; ++q) {
           if (q < a.Q) {
-            const f32x4 w = qs[q * d4 + c];
+            f32x4 w;
+            if constexpr (QR > 0)
+              w = qreg[j][q];
+            else
+              w = qs[q * d4 + c];
             acc[q] = __builtin_fmaf(w[0], v[u][j][0], acc[q]);
             acc[q] = __builtin_fmaf(w[1], v[u][j][1], acc[q]);
             acc[q] = __builtin_fmaf(w[2], v[u][j][2], acc[q]);
@@ -161,7 +175,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       }
       float mine = 0.f;
 #pragma unroll
-      for (int q = 0; q < kMaxIndexerQ; ++q) {
+      for (int q = 0; q < kQ; ++q) {
         if (q < a.Q) {
           float x = acc[q];
           x += __shfl_xor(x, 1);
@@ -181,7 +195,7 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of v over the block's 256 threads; `total` receives the block sum.
+// Exclusive prefix sum of v over the block's threads; `total` receives the block sum.
 // Every thread of the block must call it (it holds two barriers).
 __device__ int block_exclusive_scan(int v, int* wsum, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -206,8 +220,8 @@ __device__ int block_exclusive_scan(int v, int* wsum, int& total) {
 }
 
 // One workgroup per (sequence, query).  The selectable pools' scores become order keys in LDS;
-// thread t owns pools 64t .. 64t+63 and visits them rotated by t (slot j -> pool 64t + ((j + t)
-// & 63)), which puts the 64 lanes of a wave in 64 different banks.
+// thread t owns pools 32t .. 32t+31 and visits them rotated by t/2 (slot j -> pool 32t + ((j +
+// t/2) & 31)), which puts the 64 lanes of a wave in 64 different banks.
 //   1. A radix select over the keys, 11 + 11 + 10 bits from the top, finds the n_sel-th largest
 //      key kth and how many keys equal to it are taken (need_eq).
 //   2. Each thread marks its pools above kth and its keys equal to kth; a block scan over the
@@ -228,17 +242,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const int np = t >= 0 ? min((t + 1) / a.pool, min(L / a.pool, a.max_pools)) : 0;
   const int n_sel = a.topk / a.pool;
   const float* sc = a.scores + (size_t)bq * a.max_pools;
-  // sixteen loads in flight per thread, then sixteen LDS stores
-  for (int base = 0; base < np; base += 16 * kSelThreads) {
-    float v[16];
+  // every load of the row in flight at once (up to 64 per thread), then the LDS stores
+  {
+    float v[kSelPerThread];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int p = base + u * kSelThreads + tid;
+    for (int u = 0; u < kSelPerThread; ++u) {
+      const int p = u * kSelThreads + tid;
       v[u] = p < np ? sc[p] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int p = base + u * kSelThreads + tid;
+    for (int u = 0; u < kSelPerThread; ++u) {
+      const int p = u * kSelThreads + tid;
       if (p < np) keys[p] = order_key(v[u]);
     }
   }
@@ -257,7 +271,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       for (int e = tid; e < nb; e += kSelThreads) hist[e] = 0;
       __syncthreads();
       for (int j = 0; j < kSelPerThread; ++j) {
-        const int p = own + ((j + tid) & (kSelPerThread - 1));
+        const int p = own + ((j + (tid >> 1)) & (kSelPerThread - 1));
         if (p < np) {
           const uint32_t k = keys[p];
           if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1);
@@ -293,34 +307,34 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     need_eq = rem;
   }
 
-  uint64_t above = 0, eq = 0;
+  uint32_t above = 0, eq = 0;
   for (int j = 0; j < kSelPerThread; ++j) {
-    const int jj = (j + tid) & (kSelPerThread - 1);
+    const int jj = (j + (tid >> 1)) & (kSelPerThread - 1);
     const int p = own + jj;
     if (p < np) {
       const uint32_t k = keys[p];
       if (all || k > kth)
-        above |= 1ull << jj;
+        above |= 1u << jj;
       else if (k == kth)
-        eq |= 1ull << jj;
+        eq |= 1u << jj;
     }
   }
   int total;
-  const int n_eq = __builtin_popcountll(eq);
+  const int n_eq = __builtin_popcount(eq);
   const int eq_before = block_exclusive_scan(n_eq, wsum, total);
   const int take = min(max(need_eq - eq_before, 0), n_eq);
-  uint64_t kept = 0, rest = eq;
+  uint32_t kept = 0, rest = eq;
   for (int e = 0; e < take; ++e) {
-    kept |= rest & (~rest + 1ull);  // lowest set bit
-    rest &= rest - 1ull;
+    kept |= rest & (~rest + 1u);  // lowest set bit
+    rest &= rest - 1u;
   }
-  uint64_t sel = above | kept;
+  uint32_t sel = above | kept;
   int taken;
-  int r = block_exclusive_scan(__builtin_popcountll(sel), wsum, taken);
+  int r = block_exclusive_scan(__builtin_popcount(sel), wsum, taken);
   int32_t* out = a.idx + (size_t)bq * a.K_max;
   while (sel) {
-    const int jj = __builtin_ctzll(sel);
-    sel &= sel - 1ull;
+    const int jj = __builtin_ctz(sel);
+    sel &= sel - 1u;
     const int p = own + jj;
     for (int u = 0; u < a.pool; ++u) out[r * a.pool + u] = p * a.pool + u;
     ++r;
@@ -352,8 +366,10 @@ hipError_t launch_kpool(const KpoolArgs& a, hipStream_t stream) {
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<ScoreArgs*>(&a)};
   const dim3 grid((a.max_pools + kScorePoolsPerBlock - 1) / kScorePoolsPerBlock, a.B), block(256);
-  const void* fn = a.d == 64 ? (const void*)&score_kernel<2>
-                   : a.d == 128 ? (const void*)&score_kernel<4> : (const void*)&score_kernel<8>;
+  // queries in registers when they fit in 64 VGPRs (Q * d <= 512)
+  const void* fn = a.d == 64   ? (const void*)&score_kernel<2, 8>
+                   : a.d == 128 ? (a.Q <= 4 ? (const void*)&score_kernel<4, 4> : (const void*)&score_kernel<4, 0>)
+                                : (a.Q <= 2 ? (const void*)&score_kernel<8, 2> : (const void*)&score_kernel<8, 0>);
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

@@ -172,3 +172,22 @@ def test_selection_ties_across_the_whole_row(kind):
     ridx, rn = oracle_select_on(s, L, Q, pool, topk, True, topk + pool - 1)
     np.testing.assert_array_equal(n.cpu().numpy(), rn)
     np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+
+
+@pytest.mark.parametrize("d,Q", [(64, 3), (64, 8), (128, 6), (256, 2), (256, 5)])
+def test_exact_inputs_every_width(d, Q):
+    # every key width and query count the scores kernel specialises on (queries held in
+    # registers or read from LDS), bit for bit against the oracle on exact inputs
+    rng = np.random.default_rng(d * 10 + Q)
+    B, Lm, pool, topk = 2, 150, 4, 16
+    lens = np.array([150, 61], np.int32)
+    q = bits(rng.integers(-2, 3, (B, Q, d)))
+    k = bits(rng.integers(-4, 5, (B, Lm, d)) * pool)
+    g = bits(np.full((B, Lm, d), -0.75))
+    pooled, scores, idx, n = run_indexer(q, k, g, lens, pool, topk, True)
+    ridx, rn, rs = kp.indexer_reference(q, k, g, lens, pool, topk, True)
+    np.testing.assert_array_equal(n, rn)
+    np.testing.assert_array_equal(idx, ridx[:, :, : idx.shape[2]])
+    for b in range(B):
+        npb = lens[b] // pool
+        np.testing.assert_array_equal(scores[b, :, :npb], np.array(rs[b]))
