@@ -21,14 +21,14 @@ namespace mla {
 
 namespace {
 
-constexpr int kSelThreads = 512;
+constexpr int kSelThreads = 1024;
 constexpr int kSelPerThread = kMaxIndexerPools / kSelThreads;  // pools owned by one thread
 constexpr int kHistBins = 2048;
 constexpr int kScoreLanes = 8;        // lanes that share one pool's key
 constexpr int kScoreBatch = 4;        // pools per lane group in flight together
 constexpr int kScorePoolsPerBlock = 256;
 
-static_assert(kSelPerThread == 32, "the selection keeps one 32-bit mask per thread");
+static_assert(kSelPerThread <= 32 && 64 % kSelPerThread == 0, "the selection keeps one 32-bit mask per thread");
 
 // Eight channels per thread (16-byte loads of keys and gate logits): d / 8 threads per pool.
 // Per channel: gm = max_s g, e_s = exp(g_s - gm), pooled = (sum_s e_s k_s) / (sum_s e_s).
@@ -220,8 +220,8 @@ __device__ int block_exclusive_scan(int v, int* wsum, int& total) {
 }
 
 // One workgroup per (sequence, query).  The selectable pools' scores become order keys in LDS;
-// thread t owns pools 32t .. 32t+31 and visits them rotated by t/2 (slot j -> pool 32t + ((j +
-// t/2) & 31)), which puts the 64 lanes of a wave in 64 different banks.
+// thread t owns pools 16t .. 16t+15 and visits them rotated by t/4 (slot j -> pool 16t + ((j +
+// t/4) & 15)), which puts the 64 lanes of a wave in 64 different banks.
 //   1. A radix select over the keys, 11 + 11 + 10 bits from the top, finds the n_sel-th largest
 //      key kth and how many keys equal to it are taken (need_eq).
 //   2. Each thread marks its pools above kth and its keys equal to kth; a block scan over the
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       for (int e = tid; e < nb; e += kSelThreads) hist[e] = 0;
       __syncthreads();
       for (int j = 0; j < kSelPerThread; ++j) {
-        const int p = own + ((j + (tid >> 1)) & (kSelPerThread - 1));
+        const int p = own + ((j + ((tid * kSelPerThread) >> 6)) & (kSelPerThread - 1));
         if (p < np) {
           const uint32_t k = keys[p];
           if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1);
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 
   uint32_t above = 0, eq = 0;
   for (int j = 0; j < kSelPerThread; ++j) {
-    const int jj = (j + (tid >> 1)) & (kSelPerThread - 1);
+    const int jj = (j + ((tid * kSelPerThread) >> 6)) & (kSelPerThread - 1);
     const int p = own + jj;
     if (p < np) {
       const uint32_t k = keys[p];
