@@ -24,6 +24,7 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelPerThread = kMaxIndexerPools / kSelThreads;  // pools owned by one thread
 constexpr int kHistBins = 2048;
+constexpr int kKpoolBlocks = 4096;    // pooled-key workgroups in all, striding over the pools
 constexpr int kScoreLanes = 8;        // lanes that share one pool's key
 constexpr int kScoreBatch = 4;        // pools per lane group in flight together
 constexpr int kScorePoolsPerBlock = 256;
@@ -51,43 +52,62 @@ __global__ __launch_bounds__(256) void kpool_kernel(KpoolArgs a) {
   const int tpp = a.d >> 3;                 // threads per pool
   const int per_block = 256 / tpp;
   const int c0 = 8 * ((int)threadIdx.x % tpp);
+  const int stride = gridDim.x * per_block;
   const uint16_t* kb = a.k + (size_t)b * a.batch_stride + c0;
   const uint16_t* gb = a.g + (size_t)b * a.batch_stride + c0;
-  for (int p = p0 + blockIdx.x * per_block + (int)threadIdx.x / tpp; p < np; p += gridDim.x * per_block) {
-    const size_t base = (size_t)p * a.pool * a.d;
-    float* dst = a.pooled + ((size_t)b * a.max_pools + p) * a.d + c0;
-    float gm[8], sum[8], acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      gm[e] = -INFINITY;
-      sum[e] = acc[e] = 0.f;
-    }
+  // pools of up to four positions: two pools per thread per pass, every load of both in flight
+  constexpr int U = PR == 4 ? 2 : 1;
+  for (int p = p0 + blockIdx.x * per_block + (int)threadIdx.x / tpp; p < np; p += stride * U) {
     if constexpr (PR > 0) {
-      s16x8 gv[PR], kv[PR];
+      s16x8 gv[U][PR], kv[U][PR];
 #pragma unroll
-      for (int s = 0; s < PR; ++s) {
-        if (s < a.pool) {
-          gv[s] = *(const s16x8*)(gb + base + (size_t)s * a.d);
-          kv[s] = *(const s16x8*)(kb + base + (size_t)s * a.d);
-        }
-      }
+      for (int u = 0; u < U; ++u) {
+        const int pu = p + u * stride;
+        const size_t base = (size_t)pu * a.pool * a.d;
 #pragma unroll
-      for (int s = 0; s < PR; ++s)
-        if (s < a.pool)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) gm[e] = fmaxf(gm[e], bf16_bits_to_f32((uint16_t)gv[s][e]));
-#pragma unroll
-      for (int s = 0; s < PR; ++s) {
-        if (s < a.pool) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float w = __expf(bf16_bits_to_f32((uint16_t)gv[s][e]) - gm[e]);
-            sum[e] += w;
-            acc[e] = __builtin_fmaf(w, bf16_bits_to_f32((uint16_t)kv[s][e]), acc[e]);
+        for (int s = 0; s < PR; ++s) {
+          if (s < a.pool && pu < np) {
+            gv[u][s] = *(const s16x8*)(gb + base + (size_t)s * a.d);
+            kv[u][s] = *(const s16x8*)(kb + base + (size_t)s * a.d);
           }
         }
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pu = p + u * stride;
+        if (pu >= np) break;
+        float gm[8], sum[8], acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          gm[e] = -INFINITY;
+          sum[e] = acc[e] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < PR; ++s)
+          if (s < a.pool)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gm[e] = fmaxf(gm[e], bf16_bits_to_f32((uint16_t)gv[u][s][e]));
+#pragma unroll
+        for (int s = 0; s < PR; ++s) {
+          if (s < a.pool) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float w = __expf(bf16_bits_to_f32((uint16_t)gv[u][s][e]) - gm[e]);
+              sum[e] += w;
+              acc[e] = __builtin_fmaf(w, bf16_bits_to_f32((uint16_t)kv[u][s][e]), acc[e]);
+            }
+          }
+        }
+        kpool_store(a.pooled + ((size_t)b * a.max_pools + pu) * a.d + c0, acc, sum);
+      }
     } else {
+      const size_t base = (size_t)p * a.pool * a.d;
+      float gm[8], sum[8], acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        gm[e] = -INFINITY;
+        sum[e] = acc[e] = 0.f;
+      }
       for (int s = 0; s < a.pool; ++s) {
         const s16x8 g1 = *(const s16x8*)(gb + base + (size_t)s * a.d);
 #pragma unroll
@@ -103,8 +123,8 @@ __global__ __launch_bounds__(256) void kpool_kernel(KpoolArgs a) {
           acc[e] = __builtin_fmaf(w, bf16_bits_to_f32((uint16_t)k1[e]), acc[e]);
         }
       }
+      kpool_store(a.pooled + ((size_t)b * a.max_pools + p) * a.d + c0, acc, sum);
     }
-    kpool_store(dst, acc, sum);
   }
 }
 
@@ -351,12 +371,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 
 hipError_t launch_kpool(const KpoolArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<KpoolArgs*>(&a)};
-  // about 8192 workgroups in all (32 per CU), each striding over its sequence's pools: enough
+  // about 4096 workgroups in all (16 per CU), each striding over its sequence's pools: enough
   // to stream a full build, and few enough that an incremental build of a handful of new pools
   // is not dominated by launching empty workgroups
   const int per_block = 256 / (a.d / 8);
   const int blocks = (a.max_pools + per_block - 1) / per_block;
-  const int per_seq = a.B >= 8192 ? 1 : 8192 / a.B;
+  const int per_seq = a.B >= kKpoolBlocks ? 1 : kKpoolBlocks / a.B;
   const dim3 grid(blocks < per_seq ? blocks : per_seq, a.B), block(256);
   const void* fn = a.pool <= 4 ? (const void*)&kpool_kernel<4>
                    : a.pool <= 8 ? (const void*)&kpool_kernel<8> : (const void*)&kpool_kernel<0>;
