@@ -1,16 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the absorbed-MLA hot path on one MI355X.
 
-One step = the whole path over one batch: mla_absorb_q -> mla_latent_attn (split kernel +
-log-sum-exp merge) -> mla_up_v, on the single-token decode workload with batch 32, cache
-length 8192, 64 heads, 256-dim heads, latent 512 (bf16 inputs, fp32 outputs).  Inputs are
-resident in HBM before the timed region; three input sets rotate so the 256 MB Infinity Cache
-cannot hold the 256 MiB latent cache between steps.
+One step = the whole path over one batch: mla_absorb_q -> mla_latent_attn_up_v (split kernel,
+then the log-sum-exp merge of the splits fused into the value up-projection), on the
+single-token decode workload with batch 32, cache length 8192, 64 heads, 256-dim heads, latent
+512 (bf16 inputs, fp32 outputs).  Inputs are resident in HBM before the timed region; three
+input sets rotate so the 256 MB Infinity Cache cannot hold the 256 MiB latent cache between
+steps.
 
 Prints ONE JSON line: value = latent-cache GB/s over whole steps (bytes of latent rows the
-path reads per step / step time).  `roofline` is the dominant call, the latent attention,
-timed with HIP events on the stream it is launched on.  `secondary` is the 6-position
-verification pass (batch 16, cache 32768) in TFLOP/s against the bf16 matrix-core peak.
+path reads per step / step time).  `roofline` is the dominant call, mla_latent_attn_up_v, timed
+with HIP events on the stream it is launched on, against the bytes it must move (latent rows,
+U^V, absorbed queries, outputs).  `secondary` is the 6-position verification pass (batch 16,
+cache 32768) in TFLOP/s against the bf16 matrix-core peak.
 `cpu_baseline` is the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -36,7 +38,7 @@ def log(*a):
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("latent_attn.hip", "mla_device.h", "mla_internal.h", "mla_api.hip"):
+    for f in ("latent_attn.hip", "up_v.hip", "mla_device.h", "mla_internal.h", "mla_api.hip"):
         h.update(open(os.path.join(ROOT, "mla_latent_cache_absorb_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -79,6 +81,22 @@ def attended_positions(w) -> int:
     return int(sum(int(w.cache_len[b]) - Q + i + 1 for b in range(B) for i in range(Q)))
 
 
+def attn_up_v_bytes(w) -> int:
+    """Bytes mla_latent_attn_up_v must move: the latent rows, U^V once, the absorbed queries in,
+    the outputs and log-sum-exps out."""
+    B, Q, H, D = w.q.shape
+    R = w.cache.shape[2]
+    return visible_rows(w) * R * 2 + H * D * R * 2 + B * Q * H * (R * 2 + D * 4 + 4)
+
+
+def attn_up_v_flops(w) -> int:
+    """FLOPs of mla_latent_attn_up_v: 4 H R per (query, attended position) for the scores and the
+    value sum, and 2 H D R per query for the up-projection."""
+    B, Q, H, D = w.q.shape
+    R = w.cache.shape[2]
+    return 4 * H * R * attended_positions(w) + 2 * H * D * R * B * Q
+
+
 def to_device(w, dev):
     import numpy as np
     import torch
@@ -111,28 +129,19 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
     o_lat = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
     out = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev)
-    ws_bytes = binding.mla_latent_attn_workspace_size(B, Q, H, R, K_max, 0, indexed=indexed)
+    ws_bytes = max(binding.mla_latent_attn_workspace_size(B, Q, H, R, K_max, 0, indexed=indexed),
+                   binding.mla_latent_attn_up_v_workspace_size(B, Q, H, R, K_max, 0, indexed=indexed))
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(s, ev=None):
+    def attn_up_v(d):
+        binding.mla_latent_attn_up_v(q_abs, d["cache"], d["cache_len"], Lmax, w0.scale, d["w_v"], d.get("idx"),
+                                     d.get("idx_len"), 0, out=out, lse=lse, workspace=workspace)
+
+    def step(s):
         d = sets[s % nsets]
-        if ev is not None:
-            ev[0].record(stream)
         binding.mla_absorb_q(d["q"], d["w_k"], q_abs=q_abs)
-        if ev is not None:
-            ev[1].record(stream)
-        if indexed:
-            binding.mla_latent_attn_indexed(q_abs, d["cache"], d["cache_len"], d["idx"], d["idx_len"], Lmax,
-                                            w0.scale, 0, o_lat=o_lat, lse=lse, workspace=workspace)
-        else:
-            binding.mla_latent_attn(q_abs, d["cache"], d["cache_len"], Lmax, w0.scale, 0, o_lat=o_lat, lse=lse,
-                                    workspace=workspace)
-        if ev is not None:
-            ev[2].record(stream)
-        binding.mla_up_v(o_lat, d["w_v"], out=out)
-        if ev is not None:
-            ev[3].record(stream)
+        attn_up_v(d)
 
     for s in range(warmup):
         step(s)
@@ -149,32 +158,35 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / steps
     # per-stage durations, each stage's `steps` calls (input sets rotating as in the steps) between
-    # two events.  The attention call takes longer on the GPU than the Python call that launches
-    # it, so its calls are launched back to back; the short projections would measure the launch
-    # rate that way, so theirs are captured in a HIP graph and replayed
-    def one_stage(j, s):
+    # two events.  The attention calls take longer on the GPU than the Python call that launches
+    # them, so their calls are launched back to back; the short projections would measure the
+    # launch rate that way, so theirs are captured in a HIP graph and replayed.  The separate
+    # attention call (merge kernel writing o_lat) and up-projection are timed for comparison.
+    def one_stage(k, s):
         d = sets[s % nsets]
-        if j == 0:
+        if k == "absorb_q":
             binding.mla_absorb_q(d["q"], d["w_k"], q_abs=q_abs)
-        elif j == 1 and indexed:
+        elif k == "latent_attn_up_v":
+            attn_up_v(d)
+        elif k == "latent_attn" and indexed:
             binding.mla_latent_attn_indexed(q_abs, d["cache"], d["cache_len"], d["idx"], d["idx_len"], Lmax,
                                             w0.scale, 0, o_lat=o_lat, lse=lse, workspace=workspace)
-        elif j == 1:
+        elif k == "latent_attn":
             binding.mla_latent_attn(q_abs, d["cache"], d["cache_len"], Lmax, w0.scale, 0, o_lat=o_lat, lse=lse,
                                     workspace=workspace)
         else:
             binding.mla_up_v(o_lat, d["w_v"], out=out)
 
     stage = {}
-    for j, k in enumerate(("absorb_q", "latent_attn", "up_v")):
-        if k == "latent_attn":
+    for k in ("absorb_q", "latent_attn_up_v", "latent_attn", "up_v"):
+        if k.startswith("latent_attn"):
             for s in range(3):
-                one_stage(j, s)
+                one_stage(k, s)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for s in range(steps):
-                one_stage(j, s)
+                one_stage(k, s)
             e1.record(stream)
             torch.cuda.synchronize()
             stage[k] = e0.elapsed_time(e1) / steps
@@ -182,7 +194,7 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for s in range(steps):
-                one_stage(j, s)
+                one_stage(k, s)
         graph.replay()  # once untimed
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -481,8 +493,9 @@ def main():
     R = w.cache.shape[2]
     latent_bytes = visible_rows(w) * R * 2
     gbs = latent_bytes / (r["ms_step"] * 1e-3) / 1e9
-    attn_ms = r["stage_ms"]["latent_attn"]
-    achieved = latent_bytes / (attn_ms * 1e-3) / 1e9
+    attn_ms = r["stage_ms"]["latent_attn_up_v"]
+    call_bytes = attn_up_v_bytes(w)
+    achieved = call_bytes / (attn_ms * 1e-3) / 1e9
     traffic = read_traffic(args.workload)
     result = {
         "metric": "absorbed-MLA attn: latent-cache GB/s (q_len=1) + TFLOP/s (q_len=6) vs roofline",
@@ -500,11 +513,13 @@ def main():
         "config": {"workload": args.workload, "batch": B, "q_len": Q, "cache_len": int(w.cache.shape[1]),
                    "heads": H, "head_dim": D, "latent": R, "softmax_scale": w.scale, "splits": r["splits"],
                    "input_sets_rotated": NSETS, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "mla_latent_attn (split kernel + merge)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "mla_latent_attn_up_v (split kernel + merge fused into the up-projection)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic / (attn_ms * 1e-3) / 1e9, 2),
-                     "algorithmic_bytes_per_launch": latent_bytes, "avg_launch_ms": round(attn_ms, 6)},
+                     "algorithmic_bytes_per_launch": call_bytes, "latent_bytes_per_launch": latent_bytes,
+                     "avg_launch_ms": round(attn_ms, 6)},
         "stages_ms": {k: round(v, 6) for k, v in r["stage_ms"].items()},
         "tokens_per_s": round(B * Q / (r["ms_step"] * 1e-3), 1),
     }
@@ -514,15 +529,21 @@ def main():
         # process run below the steady clock
         s = time_path("verify_b16_q6_l32768", max(10, args.steps // 5), max(100, args.warmup), 1)
         ws2 = s["workload"]
-        flops = 4 * ws2.q.shape[2] * ws2.cache.shape[2] * attended_positions(ws2)
-        t_attn = s["stage_ms"]["latent_attn"] * 1e-3
+        flops = attn_up_v_flops(ws2)
+        t_attn = s["stage_ms"]["latent_attn_up_v"] * 1e-3
         tf = flops / t_attn / 1e12
+        # the attention alone (mla_latent_attn: split kernel + merge kernel), for comparison
+        attn_flops = 4 * ws2.q.shape[2] * ws2.cache.shape[2] * attended_positions(ws2)
+        tf_attn = attn_flops / (s["stage_ms"]["latent_attn"] * 1e-3) / 1e12
         result["secondary"] = {
-            "workload": "verify_b16_q6_l32768", "metric": "latent attention TFLOP/s (q_len=6)",
+            "workload": "verify_b16_q6_l32768",
+            "metric": "latent attention + up-projection TFLOP/s (q_len=6), mla_latent_attn_up_v",
             "value": round(tf, 2), "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS, "bound": "mfma",
-            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "attn_flops": flops,
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops": flops,
             "ms_per_step": round(s["ms_step"], 6), "stages_ms": {k: round(v, 6) for k, v in s["stage_ms"].items()},
-            "splits": s["splits"]}
+            "splits": s["splits"],
+            "latent_attn_only": {"value": round(tf_attn, 2), "unit": "TFLOP/s", "frac": round(tf_attn / BF16_PEAK_TFLOPS, 4),
+                                 "flops": attn_flops}}
     if not args.no_indexer:
         torch.cuda.empty_cache()
         log("[bench] timing the k-pooled indexer")

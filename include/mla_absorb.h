@@ -277,6 +277,35 @@ int mla_naive_attn(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int
 int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, int32_t H, int32_t D,
              int32_t R, void* stream);
 
+/*
+ * Latent attention and the value up-projection in one call (page "Module 05", section 3: the
+ * value sum accumulates in latent space and U_h^V is applied once per query and head).  The
+ * attention is mla_latent_attn, or mla_latent_attn_indexed when idx is given; the merge of its
+ * split partials is fused into the up-projection, so the accumulated latents never travel
+ * through device memory as a separate array.  The result equals mla_up_v applied to the o_lat
+ * of the separate attention call up to the rounding of the merge (same arithmetic, same order).
+ *   q_abs, cache, cache_batch_stride, cache_len, B, Q, H, R, max_cache_len, scale, num_splits
+ *                      as in mla_latent_attn
+ *   idx, idx_len, K_max  as in mla_latent_attn_indexed, or idx = idx_len = NULL (K_max ignored)
+ *                      for dense attention
+ *   w_v    [H][D][R] bf16   U_h^V (D == 256)
+ *   out    [B][Q][H][D] fp32 output
+ *   lse    [B][Q][H] fp32   output (may be NULL)
+ *   workspace, workspace_bytes  caller-owned device scratch of at least
+ *                      mla_latent_attn_up_v_workspace_size() bytes (never 0: with one split it
+ *                      holds the accumulated latents)
+ * Errors: MLA_ERR_NULL (a required pointer, or only one of idx / idx_len), MLA_ERR_SHAPE,
+ * MLA_ERR_ARG, MLA_ERR_WORKSPACE, MLA_ERR_DEVICE, MLA_ERR_HIP.  Device-side preconditions and
+ * empty-query behaviour as in the attention calls (out = NaN for a query that sees nothing).
+ */
+size_t mla_latent_attn_up_v_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R,
+                                           int32_t max_positions, int32_t num_splits, int32_t indexed);
+int mla_latent_attn_up_v(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
+                         const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t K_max,
+                         int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len, float scale,
+                         int32_t num_splits, const uint16_t* w_v, int32_t D, float* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,8 @@ MLA_ERR_DEVICE = -6
 
 EXPORTS = ("mla_status_string", "mla_absorb_q", "mla_latent_attn_num_splits", "mla_latent_attn_workspace_size",
            "mla_latent_attn", "mla_latent_attn_indexed", "mla_up_v", "mla_kpool_keys", "mla_indexer_scores",
-           "mla_indexer_select", "mla_latent_append", "mla_expand_kv", "mla_naive_attn")
+           "mla_indexer_select", "mla_latent_append", "mla_expand_kv", "mla_naive_attn",
+           "mla_latent_attn_up_v_workspace_size", "mla_latent_attn_up_v")
 
 
 class MlaError(RuntimeError):
@@ -58,6 +59,11 @@ def lib() -> ctypes.CDLL:
         L.mla_latent_attn_indexed.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp,
                                               vp, vp, sz, vp]
         L.mla_latent_attn_indexed.restype = ctypes.c_int
+        L.mla_latent_attn_up_v_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.mla_latent_attn_up_v_workspace_size.restype = sz
+        L.mla_latent_attn_up_v.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32,
+                                           vp, vp, vp, sz, vp]
+        L.mla_latent_attn_up_v.restype = ctypes.c_int
         L.mla_up_v.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
         L.mla_up_v.restype = ctypes.c_int
         L.mla_kpool_keys.argtypes = [vp, vp, i64, vp, vp, i32, i32, i32, i32, vp, i32, vp]
@@ -211,6 +217,49 @@ def mla_up_v(o_lat: torch.Tensor, w_v: torch.Tensor, out: Optional[torch.Tensor]
     _need(out, torch.float32, "out")
     _check(lib().mla_up_v(_ptr(o_lat), _ptr(w_v), _ptr(out), rows, H, D, R, _stream(stream)), "mla_up_v")
     return out
+
+
+def mla_latent_attn_up_v_workspace_size(B: int, Q: int, H: int, R: int, max_positions: int, num_splits: int = 0,
+                                        indexed: bool = False) -> int:
+    return int(lib().mla_latent_attn_up_v_workspace_size(B, Q, H, R, max_positions, num_splits, int(bool(indexed))))
+
+
+def mla_latent_attn_up_v(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int,
+                         scale: float, w_v: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                         idx_len: Optional[torch.Tensor] = None, num_splits: int = 0, out=None, lse=None,
+                         workspace=None, want_lse=True, stream=None):
+    """Latent attention (dense, or indexed when idx / idx_len are given) followed by the value
+    up-projection, the split merge fused into the latter.  Returns (out [B, Q, H, D] fp32,
+    lse [B, Q, H] fp32)."""
+    _need(q_abs, torch.bfloat16, "q_abs")
+    _need(cache, torch.bfloat16, "cache", contiguous=False)
+    _need(cache_len, torch.int32, "cache_len")
+    _need(w_v, torch.bfloat16, "w_v")
+    B, Q, H, R = q_abs.shape
+    D = w_v.shape[1]
+    if tuple(w_v.shape) != (H, D, R):
+        raise ValueError("w_v must be [H, D, R]")
+    indexed = idx is not None
+    K_max = 0
+    if indexed:
+        _need(idx, torch.int32, "idx")
+        _need(idx_len, torch.int32, "idx_len")
+        K_max = idx.shape[-1]
+    if out is None:
+        out = torch.empty((B, Q, H, D), dtype=torch.float32, device=q_abs.device)
+    _need(out, torch.float32, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=q_abs.device)
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    need = mla_latent_attn_up_v_workspace_size(B, Q, H, R, K_max if indexed else max_cache_len, num_splits, indexed)
+    workspace = _workspace(workspace, need, q_abs.device)
+    _check(lib().mla_latent_attn_up_v(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
+                                      _ptr(idx_len), K_max, B, Q, H, R, int(max_cache_len), float(scale),
+                                      int(num_splits), _ptr(w_v), D, _ptr(out), _ptr(lse), _ptr(workspace),
+                                      0 if workspace is None else workspace.numel(), _stream(stream)),
+           "mla_latent_attn_up_v")
+    return out, lse
 
 
 # ------------------------------------------------------------------ down-projection and append
@@ -368,12 +417,9 @@ def mla_indexer(q: torch.Tensor, k: torch.Tensor, g: torch.Tensor, cache_len: to
 
 def mla_forward(q, w_k, w_v, cache, cache_len, max_cache_len, scale, idx=None, idx_len=None, num_splits=0,
                 stream=None):
-    """The whole absorbed path: absorb_q -> latent attention (dense or indexed) -> up_v.
+    """The whole absorbed path: absorb_q -> latent attention (dense or indexed) with the
+    up-projection fused into the split merge (mla_latent_attn_up_v).
     Returns (out [B, Q, H, D] fp32, lse [B, Q, H] fp32)."""
     q_abs = mla_absorb_q(q, w_k, stream=stream)
-    if idx is None:
-        o_lat, lse = mla_latent_attn(q_abs, cache, cache_len, max_cache_len, scale, num_splits, stream=stream)
-    else:
-        o_lat, lse = mla_latent_attn_indexed(q_abs, cache, cache_len, idx, idx_len, max_cache_len, scale,
-                                             num_splits, stream=stream)
-    return mla_up_v(o_lat, w_v, stream=stream), lse
+    return mla_latent_attn_up_v(q_abs, cache, cache_len, max_cache_len, scale, w_v, idx, idx_len, num_splits,
+                                stream=stream)

@@ -54,49 +54,15 @@ __device__ __forceinline__ float quad_sum(float x) {
   return half_swap_sum(x);
 }
 
-// Merge of row `row`'s split partials; thread t owns latents 4t .. 4t+3.  The splits are taken
-// eight at a time with every load of a group issued together (one memory round trip per group),
-// and merged online: the running maximum M moves when a group holds a larger one, and what was
-// accumulated is rescaled by 2^(M_old - M_new).  Splits that saw no position (l = 0) weigh nothing.
+// Merge of row `row`'s split partials (merge_splits); thread t owns latents 4t .. 4t+3.
 __device__ __forceinline__ void merge_row(const AttnArgs& a, size_t row, int t) {
   const size_t rows = (size_t)a.B * a.Q * a.H;
-  const int S = a.num_splits;
-  const float* ml = a.part_ml + 2 * row;
-  const float* po = a.part_o + row * kLatent + 4 * t;
-  float M = -INFINITY, Ls = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float mm[8], ll[8];
-    f32x4 v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int s = min(s0 + k, S - 1);
-      mm[k] = ml[2 * s * rows];
-      ll[k] = ml[2 * s * rows + 1];
-      v[k] = *(const f32x4*)(po + (size_t)s * rows * kLatent);
-    }
-    float Mg = M;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (s0 + k < S && ll[k] > 0.f) Mg = fmaxf(Mg, mm[k]);
-    if (Mg == -INFINITY) continue;  // no split of this group saw a position
-    const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
-    Ls *= alpha;
-    acc *= alpha;
-    M = Mg;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float w = (s0 + k < S && ll[k] > 0.f) ? __builtin_amdgcn_exp2f(mm[k] - M) : 0.f;
-      Ls += w * ll[k];
-      acc += w * v[k];
-    }
-  }
-  const float inv = 1.0f / Ls;
-  *(f32x4*)(a.o_lat + row * kLatent + 4 * t) = acc * inv;
-  // __builtin_amdgcn_logf is the hardware base-2 logarithm
-  if (a.lse != nullptr && t == 0) a.lse[row] = (M + __builtin_amdgcn_logf(Ls)) * 0.69314718055994531f;
+  float lse2;
+  const f32x4 o = merge_splits(a.part_o + row * kLatent + 4 * t, a.part_ml + 2 * row, rows * kLatent, 2 * rows,
+                               a.num_splits, &lse2);
+  *(f32x4*)(a.o_lat + row * kLatent + 4 * t) = o;
+  if (a.lse != nullptr && t == 0) a.lse[row] = lse2 * 0.69314718055994531f;
 }
-
 
 template <bool INDEXED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))

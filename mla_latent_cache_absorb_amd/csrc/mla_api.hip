@@ -95,6 +95,11 @@ size_t workspace_bytes_for(int32_t B, int32_t Q, int32_t H, int32_t s) {
   return rows * 512 * sizeof(float) + rows * 2 * sizeof(float);
 }
 
+// with the up-projection fused: the partials, or for one split the accumulated latents
+size_t fused_workspace_bytes_for(int32_t B, int32_t Q, int32_t H, int32_t s) {
+  return s > 1 ? workspace_bytes_for(B, Q, H, s) : (size_t)B * Q * H * 512 * sizeof(float);
+}
+
 int device_cus_or_default() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
@@ -108,8 +113,11 @@ int device_cus_or_default() {
 int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride, const int32_t* cache_len,
                 const int32_t* idx, const int32_t* idx_len, int32_t K_max, bool indexed, int32_t B, int32_t Q,
                 int32_t H, int32_t R, int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat,
-                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q_abs || !cache || !cache_len || !o_lat) return MLA_ERR_NULL;
+                float* lse, void* workspace, size_t workspace_bytes, void* stream, const uint16_t* w_v = nullptr,
+                float* out = nullptr) {
+  // w_v != null: the up-projection follows, fused with the split merge, and writes `out`
+  const bool fused = w_v != nullptr;
+  if (!q_abs || !cache || !cache_len || (fused ? !out : !o_lat)) return MLA_ERR_NULL;
   if (indexed && (!idx || !idx_len)) return MLA_ERR_NULL;
   if (!supported(H, 256, R) || B < 1 || Q < 1 || max_cache_len < 1) return MLA_ERR_SHAPE;
   if (max_cache_len < Q) return MLA_ERR_ARG;
@@ -123,7 +131,7 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   const int32_t max_positions = indexed ? K_max : max_cache_len;
   const int s = resolve_splits(B, Q, H, max_positions, num_splits, cus, indexed);
   if (s < 1) return s;
-  const size_t need = workspace_bytes_for(B, Q, H, s);
+  const size_t need = fused ? fused_workspace_bytes_for(B, Q, H, s) : workspace_bytes_for(B, Q, H, s);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
   const int32_t qpu = queries_per_unit(Q, indexed);
   const int32_t q_units = (Q + qpu - 1) / qpu;
@@ -148,7 +156,7 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   a.num_splits = s;
   a.split_len = split_length(max_positions, s);
   a.total_wg = (int32_t)total;
-  a.o_lat = o_lat;
+  a.o_lat = fused ? (s > 1 ? nullptr : (float*)workspace) : o_lat;
   a.lse = lse;
   const size_t rows = (size_t)s * B * Q * H;
   a.part_o = s > 1 ? (float*)workspace : nullptr;
@@ -156,8 +164,21 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
 
   hipStream_t st = (hipStream_t)stream;
   if (mla::launch_latent_attn(a, indexed, st) != hipSuccess) return MLA_ERR_HIP;
-  if (s > 1 && mla::launch_combine(a, st) != hipSuccess) return MLA_ERR_HIP;
-  return MLA_OK;
+  if (!fused) {
+    if (s > 1 && mla::launch_combine(a, st) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+  }
+  if (s == 1) return mla::launch_up_v(a.o_lat, w_v, out, B * Q, H, st) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  mla::MergeUpArgs m{};
+  m.part_o = a.part_o;
+  m.part_ml = a.part_ml;
+  m.num_splits = s;
+  m.rows = B * Q;
+  m.H = H;
+  m.w_v = w_v;
+  m.out = out;
+  m.lse = lse;
+  return mla::launch_merge_up_v(m, cus, st) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // namespace
@@ -215,6 +236,26 @@ int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* cache, int64_
                             void* stream) {
   return attn_common(q_abs, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, true, B, Q, H, R,
                      max_cache_len, scale, num_splits, o_lat, lse, workspace, workspace_bytes, stream);
+}
+
+size_t mla_latent_attn_up_v_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_positions,
+                                           int32_t num_splits, int32_t indexed) {
+  if (R != 512) return 0;
+  const int s = resolve_splits(B, Q, H, max_positions, num_splits, device_cus_or_default(), indexed != 0);
+  if (s < 1 || B < 1 || Q < 1 || H < 1) return 0;
+  return fused_workspace_bytes_for(B, Q, H, s);
+}
+
+int mla_latent_attn_up_v(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
+                         const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t K_max,
+                         int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len, float scale,
+                         int32_t num_splits, const uint16_t* w_v, int32_t D, float* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!w_v) return MLA_ERR_NULL;
+  if ((idx == nullptr) != (idx_len == nullptr)) return MLA_ERR_NULL;
+  if (!supported(H, D, R)) return MLA_ERR_SHAPE;
+  return attn_common(q_abs, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, idx != nullptr, B, Q, H, R,
+                     max_cache_len, scale, num_splits, nullptr, lse, workspace, workspace_bytes, stream, w_v, out);
 }
 
 int mla_kpool_keys(const uint16_t* k, const uint16_t* g, int64_t batch_stride, const int32_t* cache_len,

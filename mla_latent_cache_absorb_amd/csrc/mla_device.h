@@ -185,6 +185,50 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// Log-sum-exp merge of the S split partials of one attention row, for the four latents a
+// thread owns.  part_o points at the row's four latents in split 0, part_ml at the row's
+// (m, l) pair in split 0; split s lies `o_step` floats (`ml_step` floats) further on.  m is a
+// running maximum in log2 units and l the sum of 2^(score - m), so the merged row is
+// sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  The splits are taken eight
+// at a time with every load of a group issued together (one memory round trip per group) and
+// merged online: the running maximum moves when a group holds a larger one, and what was
+// accumulated is rescaled by 2^(M_old - M_new).  Splits that saw no position (l = 0) weigh
+// nothing.  Returns the normalised latents; *lse2 = M + log2(sum) (log2 units).
+__device__ __forceinline__ f32x4 merge_splits(const float* part_o, const float* part_ml, size_t o_step,
+                                              size_t ml_step, int S, float* lse2) {
+  float M = -INFINITY, Ls = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float mm[8], ll[8];
+    f32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = min(s0 + k, S - 1);
+      mm[k] = part_ml[s * ml_step];
+      ll[k] = part_ml[s * ml_step + 1];
+      v[k] = *(const f32x4*)(part_o + s * o_step);
+    }
+    float Mg = M;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < S && ll[k] > 0.f) Mg = fmaxf(Mg, mm[k]);
+    if (Mg == -INFINITY) continue;  // no split of this group saw a position
+    const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
+    Ls *= alpha;
+    acc *= alpha;
+    M = Mg;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = (s0 + k < S && ll[k] > 0.f) ? __builtin_amdgcn_exp2f(mm[k] - M) : 0.f;
+      Ls += w * ll[k];
+      acc += w * v[k];
+    }
+  }
+  // __builtin_amdgcn_logf is the hardware base-2 logarithm
+  *lse2 = M + __builtin_amdgcn_logf(Ls);
+  return acc * (1.0f / Ls);
+}
+
 // Map the hardware workgroup id to a logical id so that consecutive logical ids run on the
 // same XCD: workgroups are dispatched round-robin over the 8 XCDs of an MI355X, so XCD x
 // receives hardware ids x, x+8, x+16, ...; those become one contiguous block of logical ids.

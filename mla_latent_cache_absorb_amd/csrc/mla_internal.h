@@ -115,4 +115,18 @@ hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_a
 hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H,
                        hipStream_t stream);
 
+// split-K partials merged straight into the up-projection
+struct MergeUpArgs {
+  const float* part_o;     // [S][rows][H][R] fp32 unnormalised partial sums
+  const float* part_ml;    // [S][rows][H][2] fp32 (running max in log2 units, sum)
+  int32_t num_splits;
+  int32_t rows, H;         // rows = B * Q
+  const uint16_t* w_v;     // [H][D][R] bf16
+  float* out;              // [rows][H][D] fp32
+  float* lse;              // [rows][H] fp32 or null
+  int32_t rows_per_group, groups, total_wg;  // set by the launcher
+};
+int merge_up_v_rows_per_group(int rows, int H, int cus);
+hipError_t launch_merge_up_v(MergeUpArgs a, int cus, hipStream_t stream);
+
 }  // namespace mla

@@ -123,3 +123,35 @@ def test_append_host_validation(L):
     assert L.mla_latent_append(fake, fake, fake, 512 * 64, fake, 0, 1, 4096, 512, 64, None) == binding.MLA_ERR_SHAPE
     assert L.mla_latent_append(fake, fake, fake, 512 * 63, fake, 1, 1, 4096, 512, 64, None) == binding.MLA_ERR_ARG
     assert L.mla_latent_append(fake, fake, fake, 512 * 64, fake, 1, 6, 4096, 512, 5, None) == binding.MLA_ERR_ARG
+
+
+def test_fused_up_projection_host_validation(L):
+    fake = ctypes.c_void_p(0x1000)
+    f = L.mla_latent_attn_up_v
+    # args: q_abs cache stride cache_len idx idx_len K_max B Q H R max_len scale splits w_v D out lse ws bytes stream
+    ok = [fake, fake, 51200, fake, None, None, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake, 256, fake, None, fake, 1 << 30,
+          None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["q", "c", "st", "cl", "idx", "idx_len", "K", "B", "Q", "H", "R", "L", "scale", "s", "w_v", "D", "out",
+                 "lse", "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(w_v=None) == binding.MLA_ERR_NULL
+    assert call(out=None) == binding.MLA_ERR_NULL
+    assert call(idx=fake) == binding.MLA_ERR_NULL          # idx without idx_len
+    assert call(idx_len=fake) == binding.MLA_ERR_NULL      # idx_len without idx
+    assert call(D=128) == binding.MLA_ERR_SHAPE
+    assert call(H=96) == binding.MLA_ERR_SHAPE
+    assert call(scale=0.0) == binding.MLA_ERR_ARG
+    assert call(st=512 * 99) == binding.MLA_ERR_ARG
+    assert call(idx=fake, idx_len=fake, K=0) == binding.MLA_ERR_ARG
+    # workspace: the split partials, or the accumulated latents when there is one split
+    s = binding.mla_latent_attn_num_splits(32, 1, 64, 8192, 0)
+    assert binding.mla_latent_attn_up_v_workspace_size(32, 1, 64, 512, 8192, 0) == \
+        binding.mla_latent_attn_workspace_size(32, 1, 64, 512, 8192, 0) == s * 32 * 64 * 514 * 4
+    assert binding.mla_latent_attn_up_v_workspace_size(2, 3, 64, 512, 256, 1) == 2 * 3 * 64 * 512 * 4
+    assert binding.mla_latent_attn_up_v_workspace_size(2, 3, 64, 256, 256, 1) == 0
