@@ -306,6 +306,34 @@ int mla_latent_attn_up_v(const uint16_t* q_abs, const uint16_t* cache, int64_t c
                          int32_t num_splits, const uint16_t* w_v, int32_t D, float* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Debug check of the attention calls' device-side preconditions (the calls themselves do not
+ * check device data: on bad data they stay within the cache and index rows but their result
+ * is not the attention asked for).  Page "Module 05", section 4 (query t sees j <= t); page
+ * "Module 08", section 2 (the Q new positions are the cache's last Q); colibri "DSA with
+ * k-pooling" (a query's positions are a sorted selection of its prefix).
+ *   cache_len  [B] int32 (device)
+ *   idx, idx_len  as in mla_latent_attn_indexed, or both NULL to check a dense call
+ *   B, Q, K_max, max_cache_len  as in the attention call (K_max ignored when idx is NULL)
+ *   flags      one int32 (device), output: 0 when every precondition holds, else the OR of
+ *              the MLA_BAD_* bits below.  Read it after the stream has reached this call.
+ * Enqueues one single-workgroup kernel; allocates nothing, clears nothing beforehand (the
+ * flag word is written whole), never synchronises.  Meant for debugging: it reads every listed
+ * index slot.  Errors: MLA_ERR_NULL (cache_len, flags, or only one of idx / idx_len),
+ * MLA_ERR_SHAPE (B, Q or max_cache_len < 1), MLA_ERR_ARG (K_max < 1 with idx),
+ * MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+enum mla_bad_input {
+  MLA_BAD_CACHE_LEN_SHORT = 1,  /* cache_len[b] < Q */
+  MLA_BAD_CACHE_LEN_LONG = 2,   /* cache_len[b] > max_cache_len */
+  MLA_BAD_IDX_LEN = 4,          /* idx_len[b][i] outside [1, K_max] */
+  MLA_BAD_IDX_RANGE = 8,        /* a listed position outside [0, min(cache_len[b], max_cache_len)) */
+  MLA_BAD_IDX_ORDER = 16,       /* listed positions not strictly ascending */
+  MLA_BAD_IDX_CAUSAL = 32       /* a listed position past the query's own, cache_len[b] - Q + i */
+};
+int mla_check_attn_inputs(const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t B,
+                          int32_t Q, int32_t K_max, int32_t max_cache_len, int32_t* flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

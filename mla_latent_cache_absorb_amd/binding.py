@@ -26,7 +26,7 @@ MLA_ERR_DEVICE = -6
 EXPORTS = ("mla_status_string", "mla_absorb_q", "mla_latent_attn_num_splits", "mla_latent_attn_workspace_size",
            "mla_latent_attn", "mla_latent_attn_indexed", "mla_up_v", "mla_kpool_keys", "mla_indexer_scores",
            "mla_indexer_select", "mla_latent_append", "mla_expand_kv", "mla_naive_attn",
-           "mla_latent_attn_up_v_workspace_size", "mla_latent_attn_up_v")
+           "mla_latent_attn_up_v_workspace_size", "mla_latent_attn_up_v", "mla_check_attn_inputs")
 
 
 class MlaError(RuntimeError):
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.mla_latent_attn_up_v.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32,
                                            vp, vp, vp, sz, vp]
         L.mla_latent_attn_up_v.restype = ctypes.c_int
+        L.mla_check_attn_inputs.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+        L.mla_check_attn_inputs.restype = ctypes.c_int
         L.mla_up_v.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
         L.mla_up_v.restype = ctypes.c_int
         L.mla_kpool_keys.argtypes = [vp, vp, i64, vp, vp, i32, i32, i32, i32, vp, i32, vp]
@@ -163,6 +165,40 @@ def _workspace(workspace, need, device):
     return workspace
 
 
+BAD_INPUT_BITS = {1: "cache_len < Q", 2: "cache_len > max_cache_len", 4: "idx_len outside [1, K_max]",
+                  8: "a listed position outside the cache", 16: "listed positions not strictly ascending",
+                  32: "a listed position past the query's own"}
+
+
+def mla_check_attn_inputs(cache_len: torch.Tensor, Q: int, max_cache_len: int, idx: Optional[torch.Tensor] = None,
+                          idx_len: Optional[torch.Tensor] = None, stream=None) -> int:
+    """Check the attention calls' device-side preconditions on the GPU; returns the flag word
+    (0 = all hold; else an OR of the keys of BAD_INPUT_BITS).  Synchronises the stream."""
+    _need(cache_len, torch.int32, "cache_len")
+    B = cache_len.numel()
+    K_max = 0
+    if idx is not None:
+        _need(idx, torch.int32, "idx")
+        _need(idx_len, torch.int32, "idx_len")
+        K_max = idx.shape[-1]
+    flags = torch.empty(1, dtype=torch.int32, device=cache_len.device)
+    _check(lib().mla_check_attn_inputs(_ptr(cache_len), _ptr(idx), _ptr(idx_len), B, int(Q), K_max,
+                                       int(max_cache_len), _ptr(flags), _stream(stream)), "mla_check_attn_inputs")
+    (torch.cuda.current_stream() if stream is None else stream).synchronize()
+    return int(flags.item())
+
+
+def _debug_check(cache_len, Q, max_cache_len, idx=None, idx_len=None, stream=None):
+    """With MLA_CHECK_INPUTS=1 in the environment, every attention call first checks its
+    device-side preconditions and raises MlaError(MLA_ERR_ARG) naming the ones that fail."""
+    if os.environ.get("MLA_CHECK_INPUTS", "0") in ("", "0"):
+        return
+    f = mla_check_attn_inputs(cache_len, Q, max_cache_len, idx, idx_len, stream)
+    if f:
+        what = ", ".join(v for k, v in BAD_INPUT_BITS.items() if f & k)
+        raise MlaError(MLA_ERR_ARG, f"device-side preconditions fail ({what})")
+
+
 def mla_latent_attn(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int,
                     scale: float, num_splits: int = 0, o_lat=None, lse=None, workspace=None, want_lse=True,
                     stream=None):
@@ -173,6 +209,7 @@ def mla_latent_attn(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.T
     _need(cache_len, torch.int32, "cache_len")
     B, Q, H, R = q_abs.shape
     o_lat, lse = _attn_outputs(q_abs, o_lat, lse, want_lse)
+    _debug_check(cache_len, Q, max_cache_len, stream=stream)
     need = mla_latent_attn_workspace_size(B, Q, H, R, max_cache_len, num_splits)
     workspace = _workspace(workspace, need, q_abs.device)
     _check(lib().mla_latent_attn(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), B, Q, H, R,
@@ -194,6 +231,7 @@ def mla_latent_attn_indexed(q_abs: torch.Tensor, cache: torch.Tensor, cache_len:
     B, Q, H, R = q_abs.shape
     K_max = idx.shape[-1]
     o_lat, lse = _attn_outputs(q_abs, o_lat, lse, want_lse)
+    _debug_check(cache_len, Q, max_cache_len, idx, idx_len, stream=stream)
     need = mla_latent_attn_workspace_size(B, Q, H, R, K_max, num_splits, indexed=True)
     workspace = _workspace(workspace, need, q_abs.device)
     _check(lib().mla_latent_attn_indexed(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
@@ -252,6 +290,7 @@ def mla_latent_attn_up_v(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: to
         lse = torch.empty((B, Q, H), dtype=torch.float32, device=q_abs.device)
     if lse is not None:
         _need(lse, torch.float32, "lse")
+    _debug_check(cache_len, Q, max_cache_len, idx, idx_len, stream=stream)
     need = mla_latent_attn_up_v_workspace_size(B, Q, H, R, K_max if indexed else max_cache_len, num_splits, indexed)
     workspace = _workspace(workspace, need, q_abs.device)
     _check(lib().mla_latent_attn_up_v(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),

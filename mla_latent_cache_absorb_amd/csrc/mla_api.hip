@@ -258,6 +258,22 @@ int mla_latent_attn_up_v(const uint16_t* q_abs, const uint16_t* cache, int64_t c
                      max_cache_len, scale, num_splits, nullptr, lse, workspace, workspace_bytes, stream, w_v, out);
 }
 
+int mla_check_attn_inputs(const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t B,
+                          int32_t Q, int32_t K_max, int32_t max_cache_len, int32_t* flags, void* stream) {
+  static_assert(mla::kBadCacheLenShort == MLA_BAD_CACHE_LEN_SHORT && mla::kBadCacheLenLong == MLA_BAD_CACHE_LEN_LONG &&
+                    mla::kBadIdxLen == MLA_BAD_IDX_LEN && mla::kBadIdxRange == MLA_BAD_IDX_RANGE &&
+                    mla::kBadIdxOrder == MLA_BAD_IDX_ORDER && mla::kBadIdxCausal == MLA_BAD_IDX_CAUSAL,
+                "flag bits");
+  if (!cache_len || !flags) return MLA_ERR_NULL;
+  if ((idx == nullptr) != (idx_len == nullptr)) return MLA_ERR_NULL;
+  if (B < 1 || Q < 1 || max_cache_len < 1) return MLA_ERR_SHAPE;
+  if (idx != nullptr && K_max < 1) return MLA_ERR_ARG;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  mla::CheckArgs a{cache_len, idx, idx_len, B, Q, idx ? K_max : 0, max_cache_len, flags};
+  return mla::launch_check_inputs(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_kpool_keys(const uint16_t* k, const uint16_t* g, int64_t batch_stride, const int32_t* cache_len,
                    const int32_t* pool_begin, int32_t B, int32_t max_cache_len, int32_t d, int32_t pool,
                    float* pooled, int32_t max_pools, void* stream) {

@@ -129,4 +129,16 @@ struct MergeUpArgs {
 int merge_up_v_rows_per_group(int rows, int H, int cus);
 hipError_t launch_merge_up_v(MergeUpArgs a, int cus, hipStream_t stream);
 
+// ---- device-side precondition check (bits of the flag word, as in the public header)
+constexpr int kBadCacheLenShort = 1, kBadCacheLenLong = 2, kBadIdxLen = 4, kBadIdxRange = 8, kBadIdxOrder = 16,
+              kBadIdxCausal = 32;
+struct CheckArgs {
+  const int32_t* cache_len;  // [B]
+  const int32_t* idx;        // [B][Q][K_max] or null (dense)
+  const int32_t* idx_len;    // [B][Q] (with idx)
+  int32_t B, Q, K_max, max_cache_len;
+  int32_t* flags;            // one int32, written
+};
+hipError_t launch_check_inputs(const CheckArgs& a, hipStream_t stream);
+
 }  // namespace mla

@@ -155,3 +155,19 @@ def test_fused_up_projection_host_validation(L):
         binding.mla_latent_attn_workspace_size(32, 1, 64, 512, 8192, 0) == s * 32 * 64 * 514 * 4
     assert binding.mla_latent_attn_up_v_workspace_size(2, 3, 64, 512, 256, 1) == 2 * 3 * 64 * 512 * 4
     assert binding.mla_latent_attn_up_v_workspace_size(2, 3, 64, 256, 256, 1) == 0
+
+
+def test_input_check_host_validation(L):
+    fake = ctypes.c_void_p(0x1000)
+    f = L.mla_check_attn_inputs
+    # args: cache_len idx idx_len B Q K_max max_cache_len flags stream
+    assert f(None, None, None, 1, 1, 0, 10, fake, None) == binding.MLA_ERR_NULL
+    assert f(fake, None, None, 1, 1, 0, 10, None, None) == binding.MLA_ERR_NULL
+    assert f(fake, fake, None, 1, 1, 4, 10, fake, None) == binding.MLA_ERR_NULL
+    assert f(fake, None, fake, 1, 1, 4, 10, fake, None) == binding.MLA_ERR_NULL
+    assert f(fake, None, None, 0, 1, 0, 10, fake, None) == binding.MLA_ERR_SHAPE
+    assert f(fake, None, None, 1, 0, 0, 10, fake, None) == binding.MLA_ERR_SHAPE
+    assert f(fake, None, None, 1, 1, 0, 0, fake, None) == binding.MLA_ERR_SHAPE
+    assert f(fake, fake, fake, 1, 1, 0, 10, fake, None) == binding.MLA_ERR_ARG
+    # the flag bits the header names
+    assert set(binding.BAD_INPUT_BITS) == {1, 2, 4, 8, 16, 32}
