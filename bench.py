@@ -179,7 +179,7 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
         else:
             binding.mla_up_v(o_lat, d["w_v"], out=out)
 
-    stage = {}
+    stage, pct = {}, {}
     for k in ("absorb_q", "latent_attn_up_v", "latent_attn", "up_v"):
         if k.startswith("latent_attn"):
             for s in range(3):
@@ -192,6 +192,15 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
             e1.record(stream)
             torch.cuda.synchronize()
             stage[k] = e0.elapsed_time(e1) / steps
+            # the spread: each call between its own pair of events
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            ev[0].record(stream)
+            for s in range(steps):
+                one_stage(k, s)
+                ev[s + 1].record(stream)
+            torch.cuda.synchronize()
+            per = sorted(ev[s].elapsed_time(ev[s + 1]) for s in range(steps))
+            pct[k] = [per[int(f * (steps - 1) + 0.5)] for f in (0.1, 0.5, 0.9)]
             continue
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -208,7 +217,7 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
         del graph
     del sets
     torch.cuda.empty_cache()
-    return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, splits=splits, workload=w0)
+    return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, stage_pct_ms=pct, splits=splits, workload=w0)
 
 
 def time_indexer(name: str, steps: int, warmup: int):
@@ -521,9 +530,12 @@ def main():
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic / (attn_ms * 1e-3) / 1e9, 2),
-                     "algorithmic_bytes_per_launch": latent_bytes, "avg_launch_ms": round(attn_ms, 6)},
+                     "algorithmic_bytes_per_launch": latent_bytes, "avg_launch_ms": round(attn_ms, 6),
+                     "launch_ms_p10_p50_p90": [round(x, 6) for x in r["stage_pct_ms"]["latent_attn"]]},
         "fused_attn_up_v": {"call": "mla_latent_attn_up_v (split kernel + merge fused into the up-projection)",
-                            "avg_launch_ms": round(fused_ms, 6), "algorithmic_bytes_per_launch": fused_bytes,
+                            "avg_launch_ms": round(fused_ms, 6),
+                            "launch_ms_p10_p50_p90": [round(x, 6) for x in r["stage_pct_ms"]["latent_attn_up_v"]],
+                            "algorithmic_bytes_per_launch": fused_bytes,
                             "achieved": round(fused_gbs, 2), "unit": "GB/s",
                             "frac": round(fused_gbs / HBM_PEAK_GBS, 4)},
         "stages_ms": {k: round(v, 6) for k, v in r["stage_ms"].items()},
@@ -547,6 +559,7 @@ def main():
             "frac": round(tf / BF16_PEAK_TFLOPS, 4), "attn_flops": flops,
             "ms_per_step": round(s["ms_step"], 6), "stages_ms": {k: round(v, 6) for k, v in s["stage_ms"].items()},
             "splits": s["splits"],
+            "launch_ms_p10_p50_p90": [round(x, 6) for x in s["stage_pct_ms"]["latent_attn"]],
             "fused_attn_up_v": {"value": round(tf_fused, 2), "unit": "TFLOP/s",
                                 "frac": round(tf_fused / BF16_PEAK_TFLOPS, 4), "flops": fused_flops}}
     if not args.no_indexer:
