@@ -416,6 +416,61 @@ def time_crossover(reps: int = 3):
     return rows
 
 
+QLEN_SWEEP = (16, 32768, (1, 2, 3, 4, 5, 6, 7, 8))   # batch, cache length, query counts
+
+
+def time_qlen_sweep(steps: int = 10, warmup: int = 20):
+    """The latent attention (mla_latent_attn, split kernel + merge) at one to eight query
+    positions per pass (draft depths 0..7) on 16 sequences of 32,768 positions.  Intensity is
+    128 Q FLOP/B: HBM-bound at Q = 1 and 2, matrix-core-bound from Q = 3 on (the ridge is
+    2.5e15 / 8e12 = 312 FLOP/B).  Each depth is timed over `steps` back-to-back calls between
+    HIP events, two caches alternating.  Inputs: torch.randn on the GPU with the workloads'
+    distributions (timing only)."""
+    import torch
+    from mla_latent_cache_absorb_amd import binding, workloads as wl
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0x51)
+    B, L, qs = QLEN_SWEEP
+    H, R = wl.HEADS, wl.LATENT
+    caches = [(torch.randn(B, L, R, generator=gen, device=dev)).to(torch.bfloat16) for _ in range(2)]
+    cl = torch.full((B,), L, dtype=torch.int32, device=dev)
+    rows = []
+    for Q in qs:
+        # absorbed queries: q ~ N(0, 1) through U^K ~ N(0, 1/512) over 256 dims gives N(0, 1/2)
+        q_abs = (torch.randn(B, Q, H, R, generator=gen, device=dev) * 0.5 ** 0.5).to(torch.bfloat16)
+        o = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, L, 0), 1), dtype=torch.uint8,
+                         device=dev)
+        call = lambda k: binding.mla_latent_attn(q_abs, caches[k & 1], cl, L, wl.SCALE, 0, o_lat=o, lse=lse,
+                                                 workspace=ws)
+        for k in range(warmup):
+            call(k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(steps):
+            call(k)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        visible = B * (Q * (L - Q) + Q * (Q + 1) // 2)
+        flops = 4 * H * R * visible
+        lat_bytes = B * L * R * 2
+        tf = flops / (ms * 1e-3) / 1e12
+        gbs = lat_bytes / (ms * 1e-3) / 1e9
+        bound = "hbm" if 128 * Q < BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1000 else "mfma"
+        rows.append({"q_len": Q, "ms": round(ms, 5), "splits": binding.mla_latent_attn_num_splits(B, Q, H, L, 0),
+                     "TFLOP/s": round(tf, 2), "latent_GB/s": round(gbs, 2), "bound": bound,
+                     "frac": round(gbs / HBM_PEAK_GBS if bound == "hbm" else tf / BF16_PEAK_TFLOPS, 4)})
+        del q_abs, o, lse, ws
+    del caches
+    torch.cuda.empty_cache()
+    return {"batch": B, "cache_len": L, "rows": rows}
+
+
 def cpu_baseline(name: str, budget_s: float = 12.0):
     """The fp64 oracle (expanded form) on whole sequences of the same workload, until about
     budget_s of CPU time has been spent."""
@@ -454,6 +509,9 @@ def main():
     ap.add_argument("--no-indexer", action="store_true")
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-crossover", action="store_true")
+    ap.add_argument("--no-qlen-sweep", action="store_true")
+    ap.add_argument("--qlen-sweep-only", action="store_true",
+                    help="time only the latent attention at 1..8 query positions (for profiling it on its own)")
     ap.add_argument("--crossover-only", action="store_true",
                     help="time only the absorbed / naive comparison (for profiling it on its own)")
     ap.add_argument("--append-only", action="store_true",
@@ -488,6 +546,9 @@ def main():
         log(f"[bench] copied {args.calibrate_copy} MiB three times")
         del src, dst
         torch.cuda.empty_cache()
+    if args.qlen_sweep_only:
+        print(json.dumps({"qlen_sweep": time_qlen_sweep()}), flush=True)
+        return
     if args.crossover_only:
         print(json.dumps({"crossover": time_crossover()}), flush=True)
         return
@@ -572,6 +633,9 @@ def main():
     if not args.no_crossover:
         log("[bench] timing the absorbed and naive forms at decode and prefill shapes")
         result["crossover"] = time_crossover()
+    if not args.no_qlen_sweep:
+        log("[bench] timing the latent attention at 1..8 query positions")
+        result["qlen_sweep"] = time_qlen_sweep()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(args.workload)

@@ -86,9 +86,9 @@ int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int32_
  *                  clamped to [1, 1024] and to the number of 32-position tiles, then lowered
  *                  so that no split is empty once the positions are cut into equal runs of
  *                  whole tiles (e.g. 8 tiles asked for 5 splits use 4 splits of 2 tiles)
- *   indexed        0 for mla_latent_attn, 1 for mla_latent_attn_indexed (the automatic
- *                  choice differs: single-query and indexed calls are priced as bandwidth
- *                  bound, dense multi-query calls as matrix-core bound)
+ *   indexed        0 for mla_latent_attn, 1 for mla_latent_attn_indexed (both are priced
+ *                  the same way: rounds of one workgroup per CU times the tiles of a split,
+ *                  plus the partials each extra split writes and the merge reads back)
  * Returns the split count (>= 1), or a negative status for bad sizes.
  */
 int32_t mla_latent_attn_num_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions,

@@ -39,7 +39,7 @@ int check_device(int* cus) {
 // times the tiles of one split, plus the partial results each extra split writes and the
 // merge reads back (a 128 KiB partial per query is worth four 32 KiB tiles each way) and a
 // fixed cost for the merge launch.
-int32_t choose_splits(int64_t units, int32_t queries_per_unit, int32_t max_positions, int cus) {
+int32_t choose_splits(int64_t units, int32_t max_positions, int cus) {
   const int64_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
   const int64_t slots = cus > 0 ? cus : 256;
   const int64_t smax = tiles < mla::kMaxSplits ? tiles : mla::kMaxSplits;
@@ -50,7 +50,7 @@ int32_t choose_splits(int64_t units, int32_t queries_per_unit, int32_t max_posit
     if ((s - 1) * per >= tiles) continue;  // would leave an empty split
     const int64_t rounds = (units * s + slots - 1) / slots;
     double cost = (double)rounds * (double)per;
-    if (s > 1) cost += (double)(units * queries_per_unit * s * 8) / (double)slots + 3.0;
+    if (s > 1) cost += (double)(units * s * 8) / (double)slots + 3.0;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = (int32_t)s;
@@ -68,18 +68,16 @@ int32_t split_length(int32_t max_positions, int32_t s) {
 
 bool supported(int32_t H, int32_t D, int32_t R) { return R == 512 && D == 256 && H > 0 && H % 64 == 0; }
 
-// queries handled by one workgroup: two for dense multi-query calls, else one
-int32_t queries_per_unit(int32_t, bool) { return 1; }
-
+// `indexed` is accepted for both attention calls; the choice depends on the workgroup count
+// (one per sequence, query and 64-head group) and the tiles only
 int resolve_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions, int32_t num_splits, int cus,
-                   bool indexed) {
+                   bool /*indexed*/) {
   if (B < 1 || Q < 1 || H < 64 || H % 64 != 0 || max_positions < 1) return MLA_ERR_SHAPE;
   if (num_splits < 0) return MLA_ERR_ARG;
   const int32_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
   int32_t s;
   if (num_splits == 0) {
-    const int32_t qpu = queries_per_unit(Q, indexed);
-    s = choose_splits((int64_t)B * ((Q + qpu - 1) / qpu) * (H / 64), qpu, max_positions, cus);
+    s = choose_splits((int64_t)B * Q * (H / 64), max_positions, cus);
   } else {
     s = num_splits > mla::kMaxSplits ? mla::kMaxSplits : num_splits;
     if (s > tiles) s = tiles;
@@ -133,9 +131,7 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   if (s < 1) return s;
   const size_t need = fused ? fused_workspace_bytes_for(B, Q, H, s) : workspace_bytes_for(B, Q, H, s);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
-  const int32_t qpu = queries_per_unit(Q, indexed);
-  const int32_t q_units = (Q + qpu - 1) / qpu;
-  const int64_t total = (int64_t)B * q_units * (H / 64) * s;
+  const int64_t total = (int64_t)B * Q * (H / 64) * s;
   if (total > 0x7fffffff || (int64_t)B * Q * H > 0x7fffffff) return MLA_ERR_SHAPE;
 
   mla::AttnArgs a;
@@ -150,7 +146,6 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   a.Q = Q;
   a.H = H;
   a.HG = H / 64;
-  a.q_units = q_units;
   a.max_cache_len = max_cache_len;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_splits = s;

@@ -18,7 +18,6 @@ struct AttnArgs {
   const int32_t* idx_len;         // [B][Q]        (indexed only)
   int32_t K_max;
   int32_t B, Q, H, HG;            // HG = H / 64 head groups
-  int32_t q_units;                // Q, or (Q + 1) / 2 when a workgroup takes a pair of queries
   int32_t max_cache_len;
   float scale_log2;               // softmax scale * log2(e)
   int32_t num_splits, split_len;  // split_len: positions (or index slots) per split, multiple of the tile
@@ -29,7 +28,6 @@ struct AttnArgs {
   float* part_ml;                 // [S][B*Q][H][2] fp32 (running max in log2 units, sum)
 };
 
-// q_units < Q selects the query-pair variant (dense only)
 hipError_t launch_latent_attn(const AttnArgs& a, bool indexed, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
 // ---- k-pooled indexer
