@@ -15,7 +15,7 @@ the pool-completion causality rule after rollback):
 * the incomplete tail pool is appended when asked for, which makes a row topk + pool - 1 wide;
 * ties go to the lower index, so selection is deterministic.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 * `topk` counts positions and is a multiple of `pool`: topk / pool pools are selected, each
   expanded to its `pool` positions (the only reading under which the row is topk + pool - 1
   wide); with fewer selectable pools, all of them are selected;

@@ -13,7 +13,7 @@ What the pages fix:
   width is 4096; section 3: the MLA latent cache is truncatable by position, and the state after
   a rollback must equal the state of a run that never generated the rejected tokens.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 * c_t = W h_t, a plain linear map from the hidden state h_t (width 4096) to the latent (width
   512), W stored as [512][4096] (row r holds the weights of latent channel r); no bias and no
   normalisation of the latent, since the pages name none;

@@ -43,7 +43,7 @@ attention.  The absorbed-form stages (`absorbed_query`, `latent_attention`,
 `up_project`) are given too, as plain definitions, so each library stage can be
 checked on its own.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 * query i (0-based) of a pass of Q new positions sits at position
   cache_len - Q + i and its own latent is already in the cache; it sees every
   position j <= that position (inclusive, "only j <= t");

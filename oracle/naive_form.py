@@ -11,7 +11,7 @@ j <= t (section 4).  `mla_oracle.mla_reference` is this form end to end; the two
 out here so that a GPU expansion and a GPU attention over expanded keys and values can each be
 checked on their own (the attention against the GPU's own rounded keys and values).
 
-Reading taken where the pages are silent (listed in the design doc): a GPU naive form stores the
+Reading taken where the pages are silent: a GPU naive form stores the
 expanded keys and values as bf16, rounded to nearest even, like the cache they come from.
 """
 from __future__ import annotations
