@@ -25,8 +25,9 @@ ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for every kernel: the compiler would otherwise form them
 # from ordinary float code.  The host pass warns that it does not know the feature (harmless).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                # MFMA accumulators in VGPRs: with two waves per SIMD each wave has 256
-                # registers, which the attention kernel needs as one pool
+                # MFMA accumulators in VGPRs: accumulators and operands share one register
+                # budget (168 per wave in the attention kernel, three waves per SIMD) instead of
+                # being split between VGPRs and AGPRs with copies between them
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
           "-I", INCLUDE, "-I", CSRC]

@@ -138,31 +138,6 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
 // s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned
 __device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// acc *= alpha for an MFMA accumulator that lives in AGPRs, done in place (read, multiply,
-// write back one register at a time).  Written in asm so that the only other uses of the
-// accumulator are matrix-core operands and the compiler keeps it in AGPRs instead of copying
-// it to VGPRs around every use.  The leading s_nop covers the matrix core's write latency
-// should an MFMA that writes acc still be in flight; the trailing one covers a following
-// MFMA that reads acc as its accumulator input.
-__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    float x = acc[k];
-    float tmp;
-    if (k == 0)
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\tv_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\t"
-                   "v_accvgpr_write_b32 %0, %1"
-                   : "+a"(x), "=&v"(tmp) : "v"(alpha));
-    else if (k == 15)
-      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1\n\ts_nop 4"
-                   : "+a"(x), "=&v"(tmp) : "v"(alpha));
-    else
-      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                   : "+a"(x), "=&v"(tmp) : "v"(alpha));
-    acc[k] = x;
-  }
-}
-
 // A copy of x that the compiler cannot see through.  Address arithmetic derived from it inside
 // a loop stays in the loop (recomputed with a VALU op or two per use) instead of being hoisted
 // into loop-invariant registers, which the big kernels cannot spare.
