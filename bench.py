@@ -471,6 +471,99 @@ def time_qlen_sweep(steps: int = 10, warmup: int = 20):
     return {"batch": B, "cache_len": L, "rows": rows}
 
 
+def time_other_configs(steps: int = 20, warmup: int = 20):
+    """The headline attention call (mla_latent_attn / mla_latent_attn_indexed) on the two other
+    full-size workloads: decode of 4 sequences of 131,072 positions with 1% of each sequence's
+    latents scaled by 8, and the indexed verification of 32 sequences (4 queries, lengths
+    uniform in [4096, 65536]) over 2,048 positions drawn per query from the committed prefix plus
+    the causal tail.  Inputs are drawn on the GPU with those shapes and structures (timing only;
+    the parity tests use the seeded CPU workloads).  Two input sets alternate; each call is timed
+    over `steps` back-to-back calls between HIP events."""
+    import torch
+    from mla_latent_cache_absorb_amd import binding, workloads as wl
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0xC3)
+    H, R = wl.HEADS, wl.LATENT
+    out = []
+
+    def run(call, nsets):
+        for k in range(warmup):
+            call(k % nsets)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(steps):
+            call(k % nsets)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # decode, 4 x 131072, spiked
+    B, Q, L = 4, 1, 131072
+    sets = []
+    for _ in range(2):
+        c = torch.randn(B, L, R, generator=gen, device=dev)
+        for b in range(B):
+            pos = torch.randperm(L, generator=gen, device=dev)[: round(0.01 * L)]
+            c[b, pos] *= 8.0
+        sets.append((c.to(torch.bfloat16), (torch.randn(B, Q, H, R, generator=gen, device=dev) * 0.5 ** 0.5)
+                     .to(torch.bfloat16)))
+        del c
+    cl = torch.full((B,), L, dtype=torch.int32, device=dev)
+    o = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, L, 0), 1), dtype=torch.uint8, device=dev)
+    ms = run(lambda k: binding.mla_latent_attn(sets[k][1], sets[k][0], cl, L, wl.SCALE, 0, o_lat=o, lse=lse,
+                                               workspace=ws), 2)
+    lat = B * L * R * 2
+    gbs = lat / (ms * 1e-3) / 1e9
+    out.append({"workload": "decode_b4_l131072_spiked", "call": "mla_latent_attn", "ms": round(ms, 5),
+                "splits": binding.mla_latent_attn_num_splits(B, Q, H, L, 0), "latent_bytes": lat,
+                "GB/s": round(gbs, 2), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    del sets, o, lse, ws
+    torch.cuda.empty_cache()
+
+    # indexed verification, 32 x 4, ragged
+    B, Q, Lmax, n_index = 32, 4, 65536, 2048
+    K = n_index + Q
+    g_cpu = torch.Generator()
+    g_cpu.manual_seed(0xC4)
+    lens = torch.randint(4096, Lmax + 1, (B,), generator=g_cpu, dtype=torch.int32)
+    idx = torch.full((B, Q, K), -1, dtype=torch.int32)
+    idx_len = torch.empty((B, Q), dtype=torch.int32)
+    for b in range(B):
+        first_new = int(lens[b]) - Q
+        for i in range(Q):
+            drawn = torch.sort(torch.randperm(first_new, generator=g_cpu)[:n_index]).values
+            row = torch.cat([drawn, torch.arange(first_new, first_new + i + 1)])
+            idx[b, i, : row.numel()] = row.to(torch.int32)
+            idx_len[b, i] = row.numel()
+    idx, idx_len, cl = idx.to(dev), idx_len.to(dev), lens.to(dev)
+    sets = [((torch.randn(B, Lmax, R, generator=gen, device=dev)).to(torch.bfloat16),
+             (torch.randn(B, Q, H, R, generator=gen, device=dev) * 0.5 ** 0.5).to(torch.bfloat16)) for _ in range(2)]
+    o = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, K, 0, indexed=True), 1),
+                     dtype=torch.uint8, device=dev)
+    ms = run(lambda k: binding.mla_latent_attn_indexed(sets[k][1], sets[k][0], cl, idx, idx_len, Lmax, wl.SCALE, 0,
+                                                       o_lat=o, lse=lse, workspace=ws), 2)
+    rows = int(idx_len.sum())
+    lat = rows * R * 2
+    flops = 4 * H * R * rows
+    gbs = lat / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    out.append({"workload": "indexed_verify_b32_q4_ragged", "call": "mla_latent_attn_indexed", "ms": round(ms, 5),
+                "splits": binding.mla_latent_attn_num_splits(B, Q, H, K, 0, indexed=True), "latent_bytes": lat,
+                "index_bytes": B * Q * K * 4, "GB/s": round(gbs, 2), "bound": "hbm",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOP/s": round(tf, 2),
+                "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})
+    del sets, o, lse, ws, idx, idx_len
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(name: str, budget_s: float = 12.0):
     """The fp64 oracle (expanded form) on whole sequences of the same workload, until about
     budget_s of CPU time has been spent."""
@@ -510,6 +603,9 @@ def main():
     ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-crossover", action="store_true")
     ap.add_argument("--no-qlen-sweep", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--other-configs-only", action="store_true",
+                    help="time only the attention on the 131,072-position decode and the indexed verification")
     ap.add_argument("--qlen-sweep-only", action="store_true",
                     help="time only the latent attention at 1..8 query positions (for profiling it on its own)")
     ap.add_argument("--crossover-only", action="store_true",
@@ -546,6 +642,9 @@ def main():
         log(f"[bench] copied {args.calibrate_copy} MiB three times")
         del src, dst
         torch.cuda.empty_cache()
+    if args.other_configs_only:
+        print(json.dumps({"other_configs": time_other_configs()}), flush=True)
+        return
     if args.qlen_sweep_only:
         print(json.dumps({"qlen_sweep": time_qlen_sweep()}), flush=True)
         return
@@ -636,6 +735,9 @@ def main():
     if not args.no_qlen_sweep:
         log("[bench] timing the latent attention at 1..8 query positions")
         result["qlen_sweep"] = time_qlen_sweep()
+    if not args.no_other_configs:
+        log("[bench] timing the attention on the long-context decode and the indexed verification")
+        result["other_configs"] = time_other_configs()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(args.workload)

@@ -71,6 +71,10 @@ void latent_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][64 * kPStride];  // P [head][pos] bf16
   __shared__ float abuf[2][64];                                            // rescale factor per head
   __shared__ float mlbuf[2][64];                                           // final (m, l) per head
+  // indexed calls: each value wave's index slots for 16 tiles at a time (double-buffered), and a
+  // byte per tile row telling the score waves whether its listed position is inside the cache
+  __shared__ __attribute__((aligned(16))) int32_t ibuf[INDEXED ? 8 : 1][2][64];
+  __shared__ __attribute__((aligned(16))) uint8_t vrow[INDEXED ? kRing : 1][kTile];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps it in SGPRs
@@ -161,10 +165,14 @@ void latent_attn_kernel(AttnArgs a) {
         const int nvalid = s_end - base;
         uint32_t valid = nvalid >= kTile ? 0xffffffffu : ((1u << nvalid) - 1u);
         if constexpr (INDEXED) {
+          // row validity posted by the value waves when they copied this tile (two steps ago)
+          const uint32_t* vb = (const uint32_t*)vrow[t % kRing];
 #pragma unroll
-          for (int r = 0; r < kTile; ++r) {
-            const int p = idx_row[min(base + r, s_end - 1)];
-            if (!(p >= 0 && p < L)) valid &= ~(1u << r);
+          for (int w = 0; w < kTile / 4; ++w) {
+            const uint32_t x = vb[w];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (((x >> (8 * j)) & 0xffu) == 0) valid &= ~(1u << (4 * w + j));
           }
         }
         if (valid != 0xffffffffu) {
@@ -223,13 +231,28 @@ void latent_attn_kernel(AttnArgs a) {
     const int vh = v >> 2, lq = v & 3;  // heads 32vh .., latents 128lq ..
     const int hl = lane & 31, hf = lane >> 5;
     // tile copies: rows 4v .. 4v+3 of a tile
+    // Indexed calls: the index slots of this wave's rows (4v .. 4v+3 of every tile) for tiles
+    // 16k .. 16k+15 are copied straight into the wave's own LDS block k & 1 (lane l: tile 16k +
+    // l / 4, row 4v + l % 4; slots past the split repeat its last slot).  The copy is counted by
+    // the same vmcnt waits as the tile copies, so reading a slot never waits on memory.
+    auto load_idx_block = [&](int k) {
+      const int tile = 16 * k + (lane >> 2);
+      const int slot = min(s_begin + tile * kTile + kRowsPerVWave * v + (lane & 3), s_end - 1);
+      const uint32_t ls = __builtin_amdgcn_readfirstlane(lds_addr(&ibuf[INDEXED ? v : 0][k & 1][0]));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(ls), "v"(idx_row + slot)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
+    };
     auto issue_row = [&](int t, int rr) {
       const int r = kRowsPerVWave * v + rr;
-      const int slot = s_begin + t * kTile + r;
       const uint32_t dst = lds0 + (t % kRing) * kTileBytes + r * kRowBytes;
       if constexpr (INDEXED) {
-        int p = idx_row[min(slot, s_end - 1)];
-        p = (p >= 0 && p < L) ? p : 0;
+        int p = __builtin_amdgcn_readfirstlane(ibuf[v][(t >> 4) & 1][4 * (t & 15) + rr]);
+        const bool ok = p >= 0 && p < L;
+        if (lane == 0) vrow[t % kRing][r] = ok;
+        p = ok ? p : 0;
         row_to_lds(seq + (size_t)p * kRowBytes, dst, lane16, (uint32_t)(swz(r) << 4));
       } else {
         const int first = s_begin + t * kTile;
@@ -240,6 +263,12 @@ void latent_attn_kernel(AttnArgs a) {
     };
     // Every row read is a visible row: rows past the split repeat its last row and indexed
     // slots naming a position outside the cache read row 0; the score waves mask both out.
+    if constexpr (INDEXED) {
+      if (ntiles > 0) {
+        load_idx_block(0);
+        wait_vmcnt<0>();
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       if (t < ntiles)
@@ -273,8 +302,15 @@ void latent_attn_kernel(AttnArgs a) {
         if (t + 1 < ntiles) wait_vmcnt<kRowsPerVWave>();
         else wait_vmcnt<0>();
       }
+      // the previous step's row-validity bytes must be in LDS before the score waves pass the
+      // barrier (the compiler places no LDS wait before a barrier reached along the back edge)
+      if constexpr (INDEXED) wait_lds_reads();
       __syncthreads();  // step t opens
       const int cp = t + 2;  // tile copied in this step, into the stage of tile t-2
+      // the next block of index slots, needed from step 16k + 14 on, is copied in step 16k, before
+      // this step's tile copies: the wait that opens step 16k + 1 has it in LDS
+      if constexpr (INDEXED)
+        if ((t & 15) == 0 && 16 * (t / 16 + 1) < ntiles) load_idx_block(t / 16 + 1);
       if (t == 0) {
         if (cp < ntiles)
 #pragma unroll
