@@ -245,11 +245,22 @@ void latent_attn_kernel(AttnArgs a) {
                    : "memory", "m0");
 #pragma clang diagnostic pop
     };
+    // the wave's four listed positions of tile t, read from its index block in one 16-byte read
+    auto tile_slots = [&](int t) {
+      if constexpr (INDEXED) {
+        const int4 q = *(const int4*)&ibuf[v][(t >> 4) & 1][4 * (t & 15)];
+        return int4{__builtin_amdgcn_readfirstlane(q.x), __builtin_amdgcn_readfirstlane(q.y),
+                    __builtin_amdgcn_readfirstlane(q.z), __builtin_amdgcn_readfirstlane(q.w)};
+      } else {
+        return int4{0, 0, 0, 0};
+      }
+    };
+    int4 slots = {0, 0, 0, 0};
     auto issue_row = [&](int t, int rr) {
       const int r = kRowsPerVWave * v + rr;
       const uint32_t dst = lds0 + (t % kRing) * kTileBytes + r * kRowBytes;
       if constexpr (INDEXED) {
-        int p = __builtin_amdgcn_readfirstlane(ibuf[v][(t >> 4) & 1][4 * (t & 15) + rr]);
+        int p = rr == 0 ? slots.x : rr == 1 ? slots.y : rr == 2 ? slots.z : slots.w;
         const bool ok = p >= 0 && p < L;
         if (lane == 0) vrow[t % kRing][r] = ok;
         p = ok ? p : 0;
@@ -271,9 +282,11 @@ void latent_attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      if (t < ntiles)
+      if (t < ntiles) {
+        slots = tile_slots(t);
 #pragma unroll
         for (int rr = 0; rr < kRowsPerVWave; ++rr) issue_row(t, rr);
+      }
 
     // transpose reads for the A operand (lane l: latent l % 32 of a 32-latent block, positions
     // 8(l/32) .. +7 of a 16-position k-step): in each 16-lane group g, lane 4e + q names tile
@@ -311,6 +324,7 @@ void latent_attn_kernel(AttnArgs a) {
       // this step's tile copies: the wait that opens step 16k + 1 has it in LDS
       if constexpr (INDEXED)
         if ((t & 15) == 0 && 16 * (t / 16 + 1) < ntiles) load_idx_block(t / 16 + 1);
+      if (cp < ntiles) slots = tile_slots(cp);
       if (t == 0) {
         if (cp < ntiles)
 #pragma unroll
