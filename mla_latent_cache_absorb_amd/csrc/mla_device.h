@@ -160,48 +160,85 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Log-sum-exp merge of the S split partials of one attention row, for the four latents a
-// thread owns.  part_o points at the row's four latents in split 0, part_ml at the row's
-// (m, l) pair in split 0; split s lies `o_step` floats (`ml_step` floats) further on.  m is a
-// running maximum in log2 units and l the sum of 2^(score - m), so the merged row is
-// sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  The splits are taken eight
-// at a time with every load of a group issued together (one memory round trip per group) and
-// merged online: the running maximum moves when a group holds a larger one, and what was
-// accumulated is rescaled by 2^(M_old - M_new).  Splits that saw no position (l = 0) weigh
-// nothing.  Returns the normalised latents; *lse2 = M + log2(sum) (log2 units).
+// Log-sum-exp merge of split-K attention partials.  A split's partial is (m, l, o): m a running
+// maximum in log2 units, l = sum 2^(score - m) and o the unnormalised weighted sum of its latents;
+// the merged row is sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  The splits
+// are taken in groups of eight, every load of a group issued together.  A group is first reduced
+// on its own, relative to its own maximum Mg (splits that saw no position, l = 0, weigh nothing),
+// and the group results are then folded in order into a running (M, L, o), rescaling what was
+// accumulated by 2^(M_old - M_new) and the group by 2^(Mg - M_new).  The sequential form below
+// and the wide merge kernel (groups reduced by different threads, folded in the same order) give
+// identical bits.  With one group the fold multiplies by one and adds zero, so it is exact.
+struct MergeGroup {
+  float mm[8], ll[8];
+  f32x4 v[8];
+};
+struct MergePartial {
+  float M, L;
+  f32x4 acc;
+};
+
+// part_o: the row's four latents (of this thread) in split 0; part_ml: the row's (m, l) in
+// split 0; split s lies o_step (ml_step) floats further on
+__device__ __forceinline__ void merge_load(MergeGroup& g, const float* part_o, const float* part_ml, size_t o_step,
+                                           size_t ml_step, int S, int s0) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int s = min(s0 + k, S - 1);
+    g.mm[k] = part_ml[s * ml_step];
+    g.ll[k] = part_ml[s * ml_step + 1];
+    g.v[k] = *(const f32x4*)(part_o + s * o_step);
+  }
+}
+
+// one group reduced relative to its own maximum; false when none of its splits saw a position
+__device__ __forceinline__ bool merge_group(const MergeGroup& g, int S, int s0, MergePartial& r) {
+  float Mg = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (s0 + k < S && g.ll[k] > 0.f) Mg = fmaxf(Mg, g.mm[k]);
+  if (Mg == -INFINITY) return false;
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float w = (s0 + k < S && g.ll[k] > 0.f) ? __builtin_amdgcn_exp2f(g.mm[k] - Mg) : 0.f;
+    L = __builtin_fmaf(w, g.ll[k], L);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, g.v[k][e], acc[e]);
+  }
+  r.M = Mg;
+  r.L = L;
+  r.acc = acc;
+  return true;
+}
+
+// every product and sum is written out as one fused multiply-add so that each kernel that folds
+// rounds the same way (the compiler may otherwise contract the two forms differently)
+__device__ __forceinline__ void merge_fold(float& M, float& L, f32x4& acc, const MergePartial& r) {
+  const float Mn = fmaxf(M, r.M);
+  const float a = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+  const float b = __builtin_amdgcn_exp2f(r.M - Mn);
+  L = __builtin_fmaf(r.L, b, __builtin_fmaf(L, a, 0.f));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(r.acc[e], b, __builtin_fmaf(acc[e], a, 0.f));
+  M = Mn;
+}
+
+// the whole merge for the four latents a thread owns; *lse2 = M + log2(L) (log2 units)
 __device__ __forceinline__ f32x4 merge_splits(const float* part_o, const float* part_ml, size_t o_step,
                                               size_t ml_step, int S, float* lse2) {
-  float M = -INFINITY, Ls = 0.f;
+  float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 8) {
-    float mm[8], ll[8];
-    f32x4 v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int s = min(s0 + k, S - 1);
-      mm[k] = part_ml[s * ml_step];
-      ll[k] = part_ml[s * ml_step + 1];
-      v[k] = *(const f32x4*)(part_o + s * o_step);
-    }
-    float Mg = M;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (s0 + k < S && ll[k] > 0.f) Mg = fmaxf(Mg, mm[k]);
-    if (Mg == -INFINITY) continue;  // no split of this group saw a position
-    const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
-    Ls *= alpha;
-    acc *= alpha;
-    M = Mg;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float w = (s0 + k < S && ll[k] > 0.f) ? __builtin_amdgcn_exp2f(mm[k] - M) : 0.f;
-      Ls += w * ll[k];
-      acc += w * v[k];
-    }
+    MergeGroup g;
+    merge_load(g, part_o, part_ml, o_step, ml_step, S, s0);
+    MergePartial r;
+    if (merge_group(g, S, s0, r)) merge_fold(M, L, acc, r);
   }
   // __builtin_amdgcn_logf is the hardware base-2 logarithm
-  *lse2 = M + __builtin_amdgcn_logf(Ls);
-  return acc * (1.0f / Ls);
+  *lse2 = M + __builtin_amdgcn_logf(L);
+  return acc * (1.0f / L);
 }
 
 // Map the hardware workgroup id to a logical id so that consecutive logical ids run on the

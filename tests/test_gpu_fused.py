@@ -7,7 +7,8 @@ mla_up_v on the same inputs.  Those do the same arithmetic in the same order (th
 same hi / lo split of the merged latents, the same matrix products), so the two must agree bit
 for bit.  The cases cover every row-group size the launcher picks (16, 8 and 4 rows, with a
 ragged last group), one split (no merge: the plain up-projection), dense and indexed attention,
-and two head groups.
+two head groups, and more than eight splits (the wide merge kernel, one and two rounds of
+eight groups).
 """
 import numpy as np
 import pytest
@@ -51,6 +52,8 @@ CASES = [
     (3, 6, 700, 200, 0, 64, 1),     # one split: no merge
     (2, 4, 600, 300, 100, 64, 3),   # indexed
     (2, 3, 400, 150, 0, 128, 2),    # two head groups
+    (3, 2, 1500, 600, 0, 64, 12),   # more than eight splits: the wide merge, one round of groups
+    (2, 1, 5000, 4000, 0, 64, 70),  # nine groups of splits: two rounds of the wide merge
 ]
 
 
