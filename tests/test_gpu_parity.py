@@ -141,6 +141,61 @@ def test_many_splits_more_workgroups_than_cus():
     np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=1e-3)
 
 
+def test_maximum_split_count():
+    # 1,024 splits of one 32-position tile each over a 32,768-position cache: the largest split
+    # count, the wide merge in sixteen rounds of eight groups; the fused call gives the same bits
+    spec = wl.make_spec(1, 1, 32768, workload_id=630)
+    w = wl.make_workload(spec)
+    assert binding.mla_latent_attn_num_splits(1, 1, 64, 32768, 5000) == 1024
+    qa = bf16(wl.latent_query_bits(spec))
+    c, cl, wv = bf16(w.cache), i32(w.cache_len), bf16(w.w_v)
+    print("1024 splits", flush=True)
+    o, lse = binding.mla_latent_attn(qa, c, cl, 32768, w.scale, 1024)
+    out_s = binding.mla_up_v(o, wv)
+    out_f, lse_f = binding.mla_latent_attn_up_v(qa, c, cl, 32768, w.scale, wv, num_splits=1024)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f.view(torch.int32), out_s.view(torch.int32))
+    assert torch.equal(lse_f.view(torch.int32), lse.view(torch.int32))
+    hs = [0, 21, 63]
+    ref, lse_ref = oracle.latent_attention(F(bits(qa)), w.cache, w.cache_len, w.scale, heads=hs)
+    assert_parity(o.cpu().numpy()[:, :, hs], ref, "1024 splits")
+    np.testing.assert_allclose(lse.cpu().numpy()[:, :, hs], lse_ref, rtol=0, atol=1e-3)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_empty_visible_sets(splits):
+    # cache_len < Q: a query before the cache's first position sees nothing and gets o_lat = NaN,
+    # lse = -inf, out = NaN, as documented; every other query of the call is unaffected.
+    # Sequence 0 (length 1): queries 0, 1 empty, query 2 sees position 0.  Sequence 1 (length 2):
+    # query 0 empty, queries 1 and 2 see 0 and 0..1.  Sequence 2 (length 90): every query normal.
+    Q, Lmax = 3, 100
+    spec = wl.make_spec(3, Q, Lmax, workload_id=640)
+    w = wl.make_workload(spec)
+    lens = np.array([1, 2, 90], np.int32)
+    w.cache_len[:] = lens
+    for b in range(3):
+        w.cache[b, lens[b]:] = wl.BF16_NAN
+    qa_bits = wl.latent_query_bits(spec)
+    qa, c, cl, wv = bf16(qa_bits), bf16(w.cache), i32(lens), bf16(w.w_v)
+    o, lse = binding.mla_latent_attn(qa, c, cl, Lmax, w.scale, splits)
+    out, lse_f = binding.mla_latent_attn_up_v(qa, c, cl, Lmax, w.scale, wv, num_splits=splits)
+    torch.cuda.synchronize()
+    o, lse, out, lse_f = o.cpu().numpy(), lse.cpu().numpy(), out.cpu().numpy(), lse_f.cpu().numpy()
+    empty = [(0, 0), (0, 1), (1, 0)]
+    for b, i in empty:
+        assert np.isnan(o[b, i]).all() and np.isnan(out[b, i]).all(), (b, i)
+        assert np.all(lse[b, i] == -np.inf) and np.all(lse_f[b, i] == -np.inf), (b, i)
+    # the visible queries, each against the oracle on the pass it is the tail of
+    for b, qs in ((0, [2]), (1, [1, 2]), (2, [0, 1, 2])):
+        n = len(qs)
+        sub_q = F(qa_bits)[b:b + 1, qs[0]:]
+        ref, lse_ref = oracle.latent_attention(sub_q, w.cache[b:b + 1], lens[b:b + 1], w.scale)
+        assert np.isfinite(o[b, qs]).all() and np.isfinite(out[b, qs]).all()
+        assert_parity(o[b:b + 1, qs], ref, f"visible queries of sequence {b}")
+        np.testing.assert_allclose(lse[b:b + 1, qs], lse_ref, rtol=0, atol=1e-3)
+        assert n == ref.shape[1]
+
+
 # ------------------------------------------------------------------ q_len sweep
 # Draft depths 0..7 (one to eight query positions per pass): the query-to-position mapping and
 # the causal tail of the last tile for every depth, dense and indexed, ragged lengths, through
