@@ -399,15 +399,17 @@ void latent_attn_kernel(AttnArgs a) {
 // Merge of the split partials: one workgroup of 128 threads per (b, i, head).
 __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) { merge_row(a, blockIdx.x, threadIdx.x); }
 
-// Merge of more than eight splits: 1,024 threads per (b, i, head), thread group q = t / 128
-// reduces group r0 + q of a round of eight groups, all eight groups' loads in flight together,
-// and thread group 0 folds the round's results in group order (the order merge_splits uses, so
-// the bits are the same): one memory round trip per eight groups instead of one per group.
+// Merge of more than eight splits: G = min(8, groups of eight splits) thread groups of 128 per
+// (b, i, head).  Thread group q reduces group r0 + q of a round of G groups, all the round's loads
+// in flight together, and thread group 0 folds the round's results in group order (the order
+// merge_splits uses, so the bits are the same): one memory round trip per G groups instead of
+// one per group.
 __global__ __launch_bounds__(1024) void combine_wide_kernel(AttnArgs a) {
   __shared__ f32x4 gacc[8][128];
   __shared__ float gM[8][128], gL[8][128];
   const size_t row = blockIdx.x;
   const int t = threadIdx.x & 127, q = threadIdx.x >> 7;
+  const int G = blockDim.x >> 7;  // thread groups, 2 .. 8
   const size_t rows = (size_t)a.B * a.Q * a.H;
   const int S = a.num_splits;
   const int ngroups = (S + 7) / 8;
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(1024) void combine_wide_kernel(AttnArgs a) {
   const float* pml = a.part_ml + 2 * row;
   float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int r0 = 0; r0 < ngroups; r0 += 8) {
+  for (int r0 = 0; r0 < ngroups; r0 += G) {
     const int g = r0 + q;
     MergePartial p;
     bool ok = false;
@@ -429,7 +431,7 @@ __global__ __launch_bounds__(1024) void combine_wide_kernel(AttnArgs a) {
     gacc[q][t] = ok ? p.acc : f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
     if (q == 0)
-      for (int k = 0; k < 8 && r0 + k < ngroups; ++k)
+      for (int k = 0; k < G && r0 + k < ngroups; ++k)
         if (gM[k][t] != -INFINITY) merge_fold(M, L, acc, MergePartial{gM[k][t], gL[k][t], gacc[k][t]});
     __syncthreads();  // the round's slots are rewritten by the next round
   }
@@ -452,7 +454,11 @@ hipError_t launch_latent_attn(const AttnArgs& a, bool indexed, hipStream_t strea
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<AttnArgs*>(&a)};
   const dim3 grid(a.B * a.Q * a.H);
-  if (a.num_splits > 8) return hipLaunchKernel((const void*)&combine_wide_kernel, grid, dim3(1024), args, 0, stream);
+  if (a.num_splits > 8) {
+    const int groups = (a.num_splits + 7) / 8;
+    const dim3 block(128 * (groups < 8 ? groups : 8));
+    return hipLaunchKernel((const void*)&combine_wide_kernel, grid, block, args, 0, stream);
+  }
   return hipLaunchKernel((const void*)&combine_kernel, grid, dim3(128), args, 0, stream);
 }
 
