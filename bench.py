@@ -592,7 +592,7 @@ def cpu_baseline(name: str, budget_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     # the GPU reaches its steady clock only after some tens of milliseconds of work: 200 decode
     # steps (about 18 ms) come before the timed ones
     ap.add_argument("--warmup", type=int, default=200)
