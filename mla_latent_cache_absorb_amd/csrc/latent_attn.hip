@@ -21,6 +21,14 @@
 // query registers and the accumulators.  One latent row serves all 64 heads: the cache is read
 // once per (query, split); the queries of one split are placed on one XCD and share the tiles
 // through its L2.
+//
+// Indexed calls gather the listed rows instead of a run of positions: each value wave stages its
+// rows' index slots in LDS ahead of use (copied like the tiles, so no load waits on memory inside
+// the loop) and posts each row's validity for the score waves' mask.
+//
+// The split partials (m, l, o) are merged by log-sum-exp (merge_splits): combine_kernel for up to
+// eight splits, combine_wide_kernel above that (one thread group per group of eight splits), or
+// the fused merge and up-projection of mla_latent_attn_up_v; all three give the same bits.
 #include "mla_device.h"
 #include "mla_internal.h"
 
