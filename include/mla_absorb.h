@@ -282,8 +282,9 @@ int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, 
  * value sum accumulates in latent space and U_h^V is applied once per query and head).  The
  * attention is mla_latent_attn, or mla_latent_attn_indexed when idx is given; the merge of its
  * split partials is fused into the up-projection, so the accumulated latents never travel
- * through device memory as a separate array.  The result equals mla_up_v applied to the o_lat
- * of the separate attention call up to the rounding of the merge (same arithmetic, same order).
+ * through device memory as a separate array.  The result has the same bits as mla_up_v applied
+ * to the o_lat of the separate attention call with the same split count (same merge arithmetic in
+ * the same order, same up-projection).
  *   q_abs, cache, cache_batch_stride, cache_len, B, Q, H, R, max_cache_len, scale, num_splits
  *                      as in mla_latent_attn
  *   idx, idx_len, K_max  as in mla_latent_attn_indexed, or idx = idx_len = NULL (K_max ignored)
