@@ -102,6 +102,116 @@ __global__ __launch_bounds__(kDownThreads) void latent_down_kernel(DownArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------- long passes (prefill)
+// A tiled product for passes of many tokens: a workgroup owns 64 tokens x 128 channels, four
+// waves of 32 channels x 64 tokens, and streams the hidden dimension through LDS 64 at a time
+// (double-buffered, one copy instruction per 8 rows x 128 bytes, chunk c of row r at slot
+// c ^ ((r >> 1) & 7)).  The sum keeps latent_down_kernel's order exactly: per K-slice of 256 a
+// partial from zero over the same eight MFMA 16x16x32 k-steps, the partials added to the total in
+// slice order, so a token gets the same bits in either kernel.  The operands are swapped (W rows
+// as A, tokens as B), so each lane holds four consecutive channels of one token and stores them
+// as one 8-byte write.
+constexpr int kGemmM = 64;                          // tokens per workgroup
+constexpr int kGemmN = 128;                         // channels per workgroup
+constexpr int kGemmK = 64;                          // hidden per stage
+constexpr int kGemmRowBytes = kGemmK * 2;           // 128 bytes: 8 chunks of 16
+constexpr int kGemmStages = kHidden / kGemmK;       // 64
+constexpr int kStagesPerSlice = kSlice / kGemmK;    // 4
+static_assert(kSlice % kGemmK == 0 && kGemmK % 32 == 0, "a stage holds whole k-steps of one slice");
+
+__device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
+
+__global__ __launch_bounds__(256) void down_gemm_kernel(DownArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ldsW[2][kGemmN * kGemmRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ldsH[2][kGemmM * kGemmRowBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kGemmN;  // channels
+  const int m0 = blockIdx.y * kGemmM;  // tokens
+  const int rows = a.B * a.Q;
+
+  auto issue = [&](int st, int buf) {
+    const int kb = st * kGemmRowBytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // W: 16 copies of 8 rows, four per wave
+      const int j = wave * 4 + u;
+      const int r = 8 * j + (lane >> 3);
+      const int chunk = (lane & 7) ^ gemm_swz(r);
+      copy16_to_lds((const uint8_t*)(a.w + (size_t)(n0 + r) * kHidden) + kb + 16 * chunk, lds_addr(&ldsW[buf][1024 * j]));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // tokens: 8 copies of 8 rows, two per wave; rows past the pass repeat its last
+      const int j = wave * 2 + u;
+      const int r = 8 * j + (lane >> 3);
+      const int chunk = (lane & 7) ^ gemm_swz(r);
+      const int tok = min(m0 + r, rows - 1);
+      copy16_to_lds((const uint8_t*)(a.h + (size_t)tok * kHidden) + kb + 16 * chunk, lds_addr(&ldsH[buf][1024 * j]));
+    }
+  };
+
+  const int ql = lane & 15, g = lane >> 4;
+  f32x4 total[2][4], part[2][4];  // [channel block x][token block y]
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) total[x][y] = part[x][y] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  for (int st = 0; st < kGemmStages; ++st) {
+    const int buf = st & 1;
+    wait_vmcnt<0>();
+    __syncthreads();  // stage st landed for every wave; every wave is done reading the other buffer
+    if (st + 1 < kGemmStages) issue(st + 1, buf ^ 1);
+    if (st % kStagesPerSlice == 0) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) part[x][y] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < kGemmK / 32; ++ks) {  // k = 32ks + 8g + e within the stage
+      const int chunk = 4 * ks + g;
+      bf16x8 fw[2], fh[4];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int r = 32 * wave + 16 * x + ql;
+        fw[x] = *(const bf16x8*)&ldsW[buf][r * kGemmRowBytes + 16 * (chunk ^ gemm_swz(r))];
+      }
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int r = 16 * y + ql;
+        fh[y] = *(const bf16x8*)&ldsH[buf][r * kGemmRowBytes + 16 * (chunk ^ gemm_swz(r))];
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) part[x][y] = mfma16x16(fw[x], fh[y], part[x][y]);
+    }
+    if (st % kStagesPerSlice == kStagesPerSlice - 1) {  // a slice is complete: add it in slice order
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) total[x][y] += part[x][y];
+    }
+  }
+  // lane holds channels n0 + 32 wave + 16x + 4g .. +3 of token m0 + 16y + ql
+#pragma unroll
+  for (int y = 0; y < 4; ++y) {
+    const int nn = m0 + 16 * y + ql;
+    if (nn >= rows) continue;
+    const int b = nn / a.Q, i = nn - b * a.Q;
+    const int pos = min(a.cache_len[b], a.max_cache_len) - a.Q + i;
+    if (pos < 0) continue;
+    uint16_t* dst = a.cache + (size_t)b * a.cache_bstride + (size_t)pos * kLatent + n0 + 32 * wave + 4 * g;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const uint32_t lo = (uint32_t)f32_to_bf16_bits(total[x][y][0]) | ((uint32_t)f32_to_bf16_bits(total[x][y][1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_bits(total[x][y][2]) | ((uint32_t)f32_to_bf16_bits(total[x][y][3]) << 16);
+      *(uint2*)(dst + 16 * x) = uint2{lo, hi};
+    }
+  }
+}
+
 }  // namespace
 
 int down_row_groups(int rows) {
@@ -111,6 +221,11 @@ int down_row_groups(int rows) {
 
 hipError_t launch_latent_down(const DownArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<DownArgs*>(&a)};
+  const int rows = a.B * a.Q;
+  if (rows >= kDownGemmMinRows) {
+    const dim3 grid(kLatent / kGemmN, (rows + kGemmM - 1) / kGemmM), block(256);
+    return hipLaunchKernel((const void*)&down_gemm_kernel, grid, block, args, 0, stream);
+  }
   const dim3 grid(kLatent / kDownCols, down_row_groups(a.B * a.Q)), block(kDownThreads);
   return hipLaunchKernel((const void*)&latent_down_kernel, grid, block, args, 0, stream);
 }

@@ -76,6 +76,7 @@ struct DownArgs {
   int32_t B, Q, max_cache_len;
 };
 int down_row_groups(int rows);
+constexpr int kDownGemmMinRows = 2048;  // passes of this many tokens or more use the tiled product
 hipError_t launch_latent_down(const DownArgs& a, hipStream_t stream);
 
 // ---- the naive (expanded) form

@@ -58,11 +58,12 @@ def check_rows(got, cache_before, lens, h_bits, w_bits):
     return n_exact / max(n_all, 1)
 
 
-@pytest.mark.parametrize("B,Q,L", [(1, 1, 4), (3, 5, 40), (2, 17, 64), (33, 16, 20)])
+@pytest.mark.parametrize("B,Q,L", [(1, 1, 4), (3, 5, 40), (2, 17, 64), (33, 16, 20), (4, 520, 600)])
 def test_exact_inputs_bit_exact(B, Q, L):
     # small integers: every partial sum is an integer below 2^24, exact in fp32 in any order, so
     # the stored rows equal the oracle's bit for bit (ragged lengths, a ragged last tile of 16
-    # tokens, and more tiles than row groups for B*Q = 528)
+    # tokens, more tiles than row groups for B*Q = 528; B*Q = 2080 takes the tiled product for
+    # long passes, with a ragged last tile of 32)
     rng = np.random.default_rng(100 + B * Q)
     h = small_int_bits(rng, (B, Q, HIDDEN))
     w = small_int_bits(rng, (R, HIDDEN))
@@ -141,6 +142,27 @@ def test_full_size_cache_append():
     assert np.all((lo <= v) & (v <= hi))
     cache[ar, pos] = before[ar, pos]
     assert torch.equal(cache.view(torch.int16), before.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,Q", [(1, 2100), (3, 700)])
+def test_long_pass_matches_short_passes(B, Q):
+    # a pass of 2048 tokens or more takes the tiled product; the same tokens appended 100 at a
+    # time take the batch kernel.  Same sum in the same order: identical bits, and rows within
+    # the bound (2100 tokens = 32 tiles of 64 and a ragged one; three sequences of ragged lengths)
+    spec = wl.WORKLOADS["decode_b32_l8192"]
+    inp = wl.make_append_inputs(spec, rows=B * Q)
+    h = inp.h.reshape(B, Q, HIDDEN)
+    L = 2200
+    lens = np.array([2150, 1500, 733][:B], np.int32) if B == 3 else np.array([2120], np.int32)
+    cache0 = np.full((B, L, R), wl.BF16_NAN, np.uint16)
+    print(f"append long pass B={B} Q={Q}", flush=True)
+    long = run_append(cache0, lens, h, inp.w_dkv)
+    assert check_rows(long, cache0, lens, h, inp.w_dkv) > 0.99
+    short = cache0.copy()
+    for k in range(Q // 100):
+        part = np.ascontiguousarray(h[:, 100 * k:100 * (k + 1)])
+        short = run_append(short, lens - Q + 100 * (k + 1), part, inp.w_dkv)
+    np.testing.assert_array_equal(long, short)
 
 
 def test_same_token_same_bits_in_any_batch():
