@@ -180,14 +180,22 @@ struct MergePartial {
 
 // part_o: the row's four latents (of this thread) in split 0; part_ml: the row's (m, l) in
 // split 0; split s lies o_step (ml_step) floats further on
+// slots past the last split are not loaded: they hold a neutral partial (no maximum, zero sum,
+// zero latents), which merge_group weighs by zero like any split that saw no position
 __device__ __forceinline__ void merge_load(MergeGroup& g, const float* part_o, const float* part_ml, size_t o_step,
                                            size_t ml_step, int S, int s0) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int s = min(s0 + k, S - 1);
-    g.mm[k] = part_ml[s * ml_step];
-    g.ll[k] = part_ml[s * ml_step + 1];
-    g.v[k] = *(const f32x4*)(part_o + s * o_step);
+    const int s = s0 + k;
+    if (s < S) {
+      g.mm[k] = part_ml[s * ml_step];
+      g.ll[k] = part_ml[s * ml_step + 1];
+      g.v[k] = *(const f32x4*)(part_o + s * o_step);
+    } else {
+      g.mm[k] = -INFINITY;
+      g.ll[k] = 0.f;
+      g.v[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
   }
 }
 
