@@ -52,6 +52,7 @@ CASES = [
     (3, 6, 700, 200, 0, 64, 1),     # one split: no merge
     (2, 4, 600, 300, 100, 64, 3),   # indexed
     (2, 3, 400, 150, 0, 128, 2),    # two head groups
+    (2, 2, 333, 100, 0, 192, 0),    # three head groups, a length bound that is not a whole tile
     (3, 2, 1500, 600, 0, 64, 12),   # more than eight splits: the wide merge, one round of groups
     (2, 1, 5000, 4000, 0, 64, 70),  # nine groups of splits: two rounds of the wide merge
 ]

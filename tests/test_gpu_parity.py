@@ -92,6 +92,8 @@ LAT_CASES = [
     (2, 6, 300, [300, 97], 0),
     (2, 6, 300, [300, 97], 1),
     (2, 4, 2100, [2100, 1500], 0),
+    (2, 16, 301, [301, 170], 0),    # a 16-position pass; a length bound that is not a whole tile
+    (2, 16, 301, [301, 170], 5),
 ]
 
 
