@@ -86,9 +86,12 @@ int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int32_
  *                  clamped to [1, 1024] and to the number of 32-position tiles, then lowered
  *                  so that no split is empty once the positions are cut into equal runs of
  *                  whole tiles (e.g. 8 tiles asked for 5 splits use 4 splits of 2 tiles)
- *   indexed        0 for mla_latent_attn, 1 for mla_latent_attn_indexed (both are priced
+ *   indexed        0 for mla_latent_attn, 1 for mla_latent_attn_indexed.  Both are priced
  *                  the same way: rounds of one workgroup per CU times the tiles of a split,
- *                  plus the partials each extra split writes and the merge reads back)
+ *                  plus the partials each extra split writes and the merge reads back.  A
+ *                  workgroup takes one query per sequence and 64-head group, except in dense
+ *                  calls with an even Q, where it takes two adjacent queries; the two calls
+ *                  can therefore choose different counts for the same sizes
  * Returns the split count (>= 1), or a negative status for bad sizes.
  */
 int32_t mla_latent_attn_num_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions,
@@ -121,7 +124,9 @@ size_t mla_latent_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R
  * Device-side preconditions (not checked on the host): Q <= cache_len[b] <= max_cache_len.
  * Cache rows at or past min(cache_len[b], max_cache_len) are never read.  A query whose
  * visible set is empty (cache_len[b] < Q) gets o_lat = NaN and lse = -inf.
- * Results are deterministic for a fixed num_splits (no atomics in any reduction).
+ * Results are deterministic for a fixed num_splits (no atomics in any reduction), and for the
+ * same split count equal bit for bit those of mla_latent_attn_indexed given every causal
+ * position.
  */
 int mla_latent_attn(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
                     const int32_t* cache_len, int32_t B, int32_t Q, int32_t H, int32_t R,

@@ -26,6 +26,10 @@
 // rows' index slots in LDS ahead of use (copied like the tiles, so no load waits on memory inside
 // the loop) and posts each row's validity for the score waves' mask.
 //
+// Dense calls with an even number of queries per sequence use latent_attn_pair_kernel instead:
+// the same twelve waves take two adjacent queries over one run of tiles, so that each LDS read of
+// a tile feeds twice the matrix work (the single-query form is bound by its LDS traffic).
+//
 // The split partials (m, l, o) are merged by log-sum-exp (merge_splits): combine_kernel for up to
 // eight splits, combine_wide_kernel above that (one thread group per group of eight splits), or
 // the fused merge and up-projection of mla_latent_attn_up_v; all three give the same bits.
@@ -404,6 +408,307 @@ void latent_attn_kernel(AttnArgs a) {
   }
 }
 
+// Query-pair form of the dense split kernel, used when a sequence has two or more queries.
+// One workgroup = one (sequence b, pair of adjacent queries i0 = i1 + 1, group of 64 heads,
+// split); with an odd query count the first query is alone in its pair.  The two queries differ
+// only in their last visible position, so one run of tiles serves both, and every LDS read of a
+// tile now feeds two products instead of one:
+//   score wave s holds the absorbed queries of heads 16s .. 16s+15 for both queries (128 VGPRs)
+//     and issues two MFMA 16x16x32 per tile read; the softmax runs per query, and P is posted
+//     as 128 rows (query, head)
+//   value wave 4+v (v = 4qq + lq) owns query qq of the pair, all 64 heads and latents
+//     128lq .. 128lq+127: each transposed tile read feeds two MFMA 32x32x16 (the two 32-head
+//     halves), sixteen per step
+// Per step about 264 KiB of LDS traffic serves two queries, against 244 KiB for one in the
+// single-query form.  The later query's extra position is masked out of the earlier one's scores
+// in the last tile; a split that holds only that position gives the earlier query an empty
+// partial (m = -inf, l = 0, o = 0), which the merge handles.  Each query's products, softmax and
+// sums are those of the single-query form in the same order, so the two forms give the same bits.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void latent_attn_pair_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][128 * kPStride];  // P [query][head][pos] bf16
+  __shared__ float abuf[2][128];                                            // rescale factor per row
+  __shared__ float mlbuf[2][128];                                           // final (m, l) per row
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wg = xcd_remap(blockIdx.x, a.total_wg);
+  // logical order (b, head group, split, pair): the pairs of one split of one sequence are
+  // adjacent, so they run on the same XCD and share the tile through its L2
+  const int np = (a.Q + 1) >> 1;
+  const int pr = wg % np;
+  int rest = wg / np;
+  const int split = rest % a.num_splits;
+  rest /= a.num_splits;
+  const int hg = rest % a.HG;
+  const int b = rest / a.HG;
+  const int i0 = a.Q - 1 - 2 * pr;  // later pairs see more positions: they start first
+  const int i1 = i0 - 1;            // -1: no second query
+
+  const int L = min(a.cache_len[b], a.max_cache_len);
+  const int n0 = max(L - a.Q + i0 + 1, 0);  // positions 0 .. cache_len - Q + i0
+  const int n1 = i1 >= 0 ? max(n0 - 1, 0) : 0;
+  const int s_begin = split * a.split_len;
+  const int s_end = min(s_begin + a.split_len, n0);
+  const int s_end1 = min(s_begin + a.split_len, n1);
+  const int ntiles = s_end > s_begin ? (s_end - s_begin + kTile - 1) / kTile : 0;
+  const uint8_t* seq = a.cache + (size_t)b * a.cache_bstride_bytes;
+  const uint32_t lane16 = (uint32_t)lane << 4;
+  const uint32_t lds0 = lds_addr(&smem[0][0]);
+
+  if (wave < 4) {
+    // ======================= score waves =======================
+    const int s = wave;
+    const int c = lane & 15, G = lane >> 4;  // head 16s + c; k / row group G
+    const int h = hg * 64 + 16 * s + c;
+    const float c2 = a.scale_log2;
+    // absorbed queries as B operands: latents 32ks + 8G .. +7 (a lone query is loaded twice)
+    bf16x8 qf[2][16];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int iq = (qq == 0 || i1 < 0) ? i0 : i1;
+      const uint16_t* qrow = a.q_abs + ((size_t)(b * a.Q + iq) * a.H + h) * kLatent + 8 * G;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qf[qq][ks] = *(const bf16x8*)(qrow + 32 * ks);
+    }
+    // running maximum and sum per (query, head) live in mlbuf between steps (no room in VGPRs)
+    if (G == 0) {
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        mlbuf[0][64 * qq + 16 * s + c] = -INFINITY;
+        mlbuf[1][64 * qq + 16 * s + c] = 0.f;
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // the first two tiles have landed (copied by the value waves)
+
+    for (int t = 0; t <= ntiles; ++t) {
+      wait_lds_reads();
+      __syncthreads();  // step t opens: tile t is in LDS; the value waves read P of step t-1
+      if (t == ntiles) break;
+      // the query registers leave no room to keep addresses across steps: each step derives them
+      // from the lane index again (A operand addressing as in the single-query form)
+      const int ln = opaque(lane);
+      const int cl = ln & 15, Gl = ln >> 4;
+      const uint8_t* rb = smem[t % kRing] + (4 * (cl & 3) + (cl >> 2)) * kRowBytes + ((Gl ^ (cl & 3)) << 4);
+      const int hi = cl >> 2;
+      auto rd = [&](int n) {  // n = 2 ks + block
+        const int ks = n >> 1;
+        return *(const bf16x8*)(rb + 16 * kRowBytes * (n & 1) + 256 * (ks >> 2) + (((ks & 3) ^ hi) << 6));
+      };
+      f32x4 sc[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+      constexpr int kAhead = 2;
+      bf16x8 av[kAhead + 1];
+      // the score waves' products issue first, so that their softmax tail overlaps the value
+      // waves' products instead of following them
+      __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+      for (int n = 0; n < kAhead; ++n) av[n] = rd(n);
+#pragma unroll
+      for (int n = 0; n < 32; ++n) {
+        if (n + kAhead < 32) av[(n + kAhead) % (kAhead + 1)] = rd(n + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        sc[0][n & 1] = mfma16(av[n % (kAhead + 1)], qf[0][n >> 1], sc[0][n & 1]);
+        sc[1][n & 1] = mfma16(av[n % (kAhead + 1)], qf[1][n >> 1], sc[1][n & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      const int base = s_begin + t * kTile;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        // lane holds positions 16 blk + 4jj + G of head c; mask those past the query's visible set
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = sc[qq][k >> 2][k & 3];
+        const int nvalid = (qq == 0 ? s_end : s_end1) - base;
+        const uint32_t valid = nvalid >= kTile ? 0xffffffffu : nvalid <= 0 ? 0u : ((1u << nvalid) - 1u);
+        if (valid != 0xffffffffu) {
+          // shifted once (no per-register bit masks to keep live), by the row group taken from
+          // the lane index here rather than kept live across the products
+          const uint32_t vg = valid >> (opaque(lane) >> 4);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (!((vg >> (16 * (k >> 2) + 4 * (k & 3))) & 1u)) v[k] = -INFINITY;
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(v[0], v[4]), fmaxf(v[1], v[5])), fmaxf(fmaxf(v[2], v[6]), fmaxf(v[3], v[7])));
+        tmax = quad_max(tmax) * c2;
+        const int lp = opaque(lane);
+        const int row = 64 * qq + 16 * s + (lp & 15);  // P / rescale / (m, l) row of this lane
+        float m_run = mlbuf[0][row], l_run = mlbuf[1][row];
+        const float m_new = fmaxf(m_run, tmax);
+        const bool need = m_new > m_run + kRescaleLog2;
+        float alpha = 1.f;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float m_use = need ? m_new : m_run;
+          alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
+          l_run *= alpha;
+          m_run = m_use;
+        }
+        const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
+        float p[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -msafe));
+        l_run += quad_sum(((p[0] + p[4]) + (p[1] + p[5])) + ((p[2] + p[6]) + (p[3] + p[7])));
+        if (lp < 16) {
+          mlbuf[0][row] = m_run;
+          mlbuf[1][row] = l_run;
+        }
+        // P row 64qq + 16s + c, transposed across the lanes G as in the single-query form
+        uint8_t* prow = pbuf[t & 1] + row * kPStride + 8 * (lp >> 4);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          unsigned u[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) u[jj] = __builtin_bit_cast(unsigned, p[4 * blk + jj]);
+          auto r01 = __builtin_amdgcn_permlane16_swap(u[0], u[1], false, false);
+          auto r23 = __builtin_amdgcn_permlane16_swap(u[2], u[3], false, false);
+          auto r02 = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
+          auto r13 = __builtin_amdgcn_permlane32_swap(r01[1], r23[1], false, false);
+          s16x4 pv;
+          pv[0] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[0]));
+          pv[1] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[0]));
+          pv[2] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[1]));
+          pv[3] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[1]));
+          *(s16x4*)(prow + 32 * blk) = pv;
+        }
+        if (lp < 16) abuf[t & 1][row] = alpha;
+      }
+    }
+    __syncthreads();  // (m, l) are posted
+  } else {
+    // ======================= value waves =======================
+    const int v = wave - 4;
+    const int qq = v >> 2, lq = v & 3;  // query qq of the pair, latents 128lq ..
+    const int hl = lane & 31, hf = lane >> 5;
+    // tile copies: rows 4v .. 4v+3 of a tile; rows past the split repeat its last row
+    auto issue_row = [&](int t, int rr) {
+      const int r = kRowsPerVWave * v + rr;
+      const uint32_t dst = lds0 + (t % kRing) * kTileBytes + r * kRowBytes;
+      const int first = s_begin + t * kTile;
+      const int row = min(r, s_end - 1 - first);
+      row_to_lds_at(seq + (size_t)first * kRowBytes, (uint32_t)(row * kRowBytes), dst, lane16,
+                    (uint32_t)(swz(r) << 4));
+    };
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (t < ntiles)
+#pragma unroll
+        for (int rr = 0; rr < kRowsPerVWave; ++rr) issue_row(t, rr);
+
+    // transpose reads for the A operand, as in the single-query form
+    const int g = lane >> 4, ip = lane & 15, te = ip >> 2, tq = ip & 3;
+    const int x = 2 * (g & 1) + (tq >> 1);
+    const int row0 = 8 * (g >> 1) + te, row1 = row0 + 4;
+    const int tb0 = row0 * kRowBytes + 256 * lq + ((x ^ ((row0 >> 2) & 3)) << 4) + ((tq & 1) << 3);
+    const int tb1 = row1 * kRowBytes + 256 * lq + ((x ^ ((row1 >> 2) & 3)) << 4) + ((tq & 1) << 3);
+    const int prow0 = 64 * qq + hl;  // P / rescale row of head half 0 (half 1: +32)
+
+    f32x16 o[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) o[mb][nb][k] = 0.f;
+    wait_vmcnt<0>();
+    __syncthreads();  // the first two tiles have landed
+
+    for (int t = 0; t <= ntiles; ++t) {
+      if (t < ntiles) {
+        if (t + 1 < ntiles) wait_vmcnt<kRowsPerVWave>();
+        else wait_vmcnt<0>();
+      }
+      __syncthreads();  // step t opens
+      const int cp = t + 2;  // tile copied in this step, into the stage of tile t-2
+      if (t == 0) {
+        if (cp < ntiles)
+#pragma unroll
+          for (int rr = 0; rr < kRowsPerVWave; ++rr) issue_row(cp, rr);
+        continue;
+      }
+      const int tv_ = t - 1;  // tile whose values this step accumulates
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float alpha = abuf[tv_ & 1][prow0 + 32 * nb];
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) o[mb][nb] *= alpha;
+        }
+      }
+      // P of the first k-step now, of the second once its last product has been issued
+      const uint8_t* pb = pbuf[tv_ & 1] + prow0 * kPStride + 16 * hf;
+      bf16x8 pf[2];  // [head half]
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) pf[nb] = *(const bf16x8*)(pb + 32 * nb * kPStride);
+      const uint8_t* tile = smem[tv_ % kRing];
+      const int fh = opaque(te);
+      const uint8_t* t0 = tile + tb0;
+      const uint8_t* t1 = tile + tb1;
+      constexpr int kAhead = 1;
+      s16x4 tv[kAhead + 1][2];
+      auto load = [&](int n, int slot) {  // n = 4 ks + mb
+        const int sh = 64 * ((n & 3) ^ fh) + 16 * kRowBytes * (n >> 2);
+        tv[slot][0] = lds_read_tr16(t0 + sh);
+        tv[slot][1] = lds_read_tr16(t1 + sh);
+      };
+#pragma unroll
+      for (int n = 0; n < kAhead; ++n) load(n, n);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        if (n + kAhead < 8) load(n + kAhead, (n + kAhead) % (kAhead + 1));
+        if ((n & 1) == 0 && cp < ntiles) issue_row(cp, n >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 av = concat_bf16(tv[n % (kAhead + 1)][0], tv[n % (kAhead + 1)][1]);
+        o[n & 3][0] = mfma32(av, pf[0], o[n & 3][0]);
+        o[n & 3][1] = mfma32(av, pf[1], o[n & 3][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (n == 3)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) pf[nb] = *(const bf16x8*)(pb + 32 * nb * kPStride + 32);
+      }
+    }
+    __syncthreads();  // (m, l) are posted
+    const int iq = qq == 0 ? i0 : i1;
+    if (iq >= 0) {
+      const int bq = b * a.Q + iq;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int hv = hg * 64 + 32 * nb + hl;  // this lane's head (output column)
+        const float m_fin = mlbuf[0][prow0 + 32 * nb];
+        const float l_fin = mlbuf[1][prow0 + 32 * nb];
+        // lane holds head hv, latents 128lq + 32mb + 8ii + 4hf + j
+        if (a.num_splits == 1) {
+          const float inv_l = 1.0f / l_fin;
+          float* orow = a.o_lat + ((size_t)bq * a.H + hv) * kLatent + 128 * lq + 4 * hf;
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+              *(f32x4*)(orow + 32 * mb + 8 * ii) =
+                  (f32x4){o[mb][nb][4 * ii] * inv_l, o[mb][nb][4 * ii + 1] * inv_l, o[mb][nb][4 * ii + 2] * inv_l,
+                          o[mb][nb][4 * ii + 3] * inv_l};
+          if (a.lse != nullptr && hf == 0 && lq == 0)
+            a.lse[(size_t)bq * a.H + hv] = (m_fin + __builtin_amdgcn_logf(l_fin)) * 0.69314718055994531f;
+        } else {
+          const size_t prow_idx = ((size_t)split * a.B * a.Q + bq) * a.H + hv;
+          float* orow = a.part_o + prow_idx * kLatent + 128 * lq + 4 * hf;
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+              *(f32x4*)(orow + 32 * mb + 8 * ii) = (f32x4){o[mb][nb][4 * ii], o[mb][nb][4 * ii + 1],
+                                                           o[mb][nb][4 * ii + 2], o[mb][nb][4 * ii + 3]};
+          if (hf == 0 && lq == 0) {
+            a.part_ml[2 * prow_idx] = m_fin;
+            a.part_ml[2 * prow_idx + 1] = l_fin;
+          }
+        }
+      }
+    }
+  }
+}
+
 // Merge of the split partials: one workgroup of 128 threads per (b, i, head).
 __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) { merge_row(a, blockIdx.x, threadIdx.x); }
 
@@ -455,7 +760,9 @@ __global__ __launch_bounds__(1024) void combine_wide_kernel(AttnArgs a) {
 hipError_t launch_latent_attn(const AttnArgs& a, bool indexed, hipStream_t stream) {
   void* args[] = {const_cast<AttnArgs*>(&a)};
   const dim3 grid(a.total_wg), block(kThreads);
-  const void* k = indexed ? (const void*)&latent_attn_kernel<true> : (const void*)&latent_attn_kernel<false>;
+  const void* k = indexed                    ? (const void*)&latent_attn_kernel<true>
+                  : queries_per_wg(false, a.Q) == 2 ? (const void*)&latent_attn_pair_kernel
+                                                    : (const void*)&latent_attn_kernel<false>;
   return hipLaunchKernel(k, grid, block, args, 0, stream);
 }
 

@@ -68,16 +68,16 @@ int32_t split_length(int32_t max_positions, int32_t s) {
 
 bool supported(int32_t H, int32_t D, int32_t R) { return R == 512 && D == 256 && H > 0 && H % 64 == 0; }
 
-// `indexed` is accepted for both attention calls; the choice depends on the workgroup count
-// (one per sequence, query and 64-head group) and the tiles only
+// the choice depends on the workgroup count per split (one per sequence, 64-head group and query,
+// or pair of queries for dense calls with two or more) and the tiles only
 int resolve_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions, int32_t num_splits, int cus,
-                   bool /*indexed*/) {
+                   bool indexed) {
   if (B < 1 || Q < 1 || H < 64 || H % 64 != 0 || max_positions < 1) return MLA_ERR_SHAPE;
   if (num_splits < 0) return MLA_ERR_ARG;
   const int32_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
   int32_t s;
   if (num_splits == 0) {
-    s = choose_splits((int64_t)B * Q * (H / 64), max_positions, cus);
+    s = choose_splits((int64_t)B * mla::query_units(indexed, Q) * (H / 64), max_positions, cus);
   } else {
     s = num_splits > mla::kMaxSplits ? mla::kMaxSplits : num_splits;
     if (s > tiles) s = tiles;
@@ -131,7 +131,7 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   if (s < 1) return s;
   const size_t need = fused ? fused_workspace_bytes_for(B, Q, H, s) : workspace_bytes_for(B, Q, H, s);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
-  const int64_t total = (int64_t)B * Q * (H / 64) * s;
+  const int64_t total = (int64_t)B * mla::query_units(indexed, Q) * (H / 64) * s;
   if (total > 0x7fffffff || (int64_t)B * Q * H > 0x7fffffff) return MLA_ERR_SHAPE;
 
   mla::AttnArgs a;

@@ -28,6 +28,13 @@ struct AttnArgs {
   float* part_ml;                 // [S][B*Q][H][2] fp32 (running max in log2 units, sum)
 };
 
+// queries one workgroup of the split kernel takes: dense calls with an even number of queries
+// per sequence pair adjacent queries, so one run of tiles serves both (with an odd count the lone
+// query's workgroup would cost a pair's time for one query's work)
+inline int queries_per_wg(bool indexed, int32_t Q) { return !indexed && Q % 2 == 0 ? 2 : 1; }
+// workgroups per (sequence, head group, split)
+inline int32_t query_units(bool indexed, int32_t Q) { return queries_per_wg(indexed, Q) == 2 ? (Q + 1) / 2 : Q; }
+
 hipError_t launch_latent_attn(const AttnArgs& a, bool indexed, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t stream);
 // ---- k-pooled indexer

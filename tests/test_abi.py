@@ -91,7 +91,9 @@ def test_split_choice_without_device(L):
     # workgroups, as few splits (partials) as that allows
     assert binding.mla_latent_attn_num_splits(32, 1, 64, 8192, 0) == 8          # 256 workgroups
     assert binding.mla_latent_attn_num_splits(4, 1, 64, 131072, 0) == 64        # 256 workgroups
-    assert binding.mla_latent_attn_num_splits(16, 6, 64, 32768, 0) == 8         # 768 = 3 rounds
+    # dense calls with several queries take them in pairs: 16 x 3 pairs x 5 splits = 240
+    assert binding.mla_latent_attn_num_splits(16, 6, 64, 32768, 0) == 5
+    assert binding.mla_latent_attn_num_splits(16, 6, 64, 32768, 0, indexed=True) == 8  # 768 = 3 rounds
     assert binding.mla_latent_attn_num_splits(32, 4, 64, 2052, 0, indexed=True) == 2
     assert binding.mla_latent_attn_workspace_size(32, 4, 64, 512, 2052, 0, indexed=True) == 2 * 128 * 64 * 514 * 4
 
