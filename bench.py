@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,10 +39,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """C++ source with comments removed and whitespace collapsed: what the compiler sees.  (The
+    sources hold no comment markers inside string literals.)"""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_digest() -> str:
+    """Digest of the attention kernels' code (comments and layout excluded), recorded beside the
+    counter measurements so that they are used only while the code they measured is unchanged."""
     h = hashlib.sha256()
     for f in ("latent_attn.hip", "up_v.hip", "mla_device.h", "mla_internal.h", "mla_api.hip"):
-        h.update(open(os.path.join(ROOT, "mla_latent_cache_absorb_amd", "csrc", f), "rb").read())
+        h.update(code_text(open(os.path.join(ROOT, "mla_latent_cache_absorb_amd", "csrc", f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -408,9 +408,11 @@ void latent_attn_kernel(AttnArgs a) {
   }
 }
 
-// Query-pair form of the dense split kernel, used when a sequence has two or more queries.
+// Query-pair form of the dense split kernel, used when a sequence has an even number of queries.
 // One workgroup = one (sequence b, pair of adjacent queries i0 = i1 + 1, group of 64 heads,
-// split); with an odd query count the first query is alone in its pair.  The two queries differ
+// split).  The kernel also accepts an odd count, the first query then alone in its pair, but
+// that workgroup costs a pair's step for one query's work, so the launcher (queries_per_wg)
+// keeps odd counts on the single-query form.  The two queries differ
 // only in their last visible position, so one run of tiles serves both, and every LDS read of a
 // tile now feeds two products instead of one:
 //   score wave s holds the absorbed queries of heads 16s .. 16s+15 for both queries (128 VGPRs)
