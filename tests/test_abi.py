@@ -91,9 +91,24 @@ def test_split_choice_without_device(L):
     # workgroups, as few splits (partials) as that allows
     assert binding.mla_latent_attn_num_splits(32, 1, 64, 8192, 0) == 8          # 256 workgroups
     assert binding.mla_latent_attn_num_splits(4, 1, 64, 131072, 0) == 64        # 256 workgroups
-    # dense calls with several queries take them in pairs: 16 x 3 pairs x 5 splits = 240
+    # dense calls with an even number of queries take them in pairs: 16 x 3 pairs x 5 splits = 240
     assert binding.mla_latent_attn_num_splits(16, 6, 64, 32768, 0) == 5
     assert binding.mla_latent_attn_num_splits(16, 6, 64, 32768, 0, indexed=True) == 8  # 768 = 3 rounds
+
+
+def test_split_choice_counts_query_pairs(L):
+    # the work units the choice prices: pairs of queries for dense calls with an even Q, single
+    # queries otherwise, so a dense call with 2P queries chooses as an indexed call with P
+    for B, Lmax in ((16, 32768), (32, 8192), (4, 131072), (3, 1000)):
+        for Q in (2, 4, 6, 8):
+            assert (binding.mla_latent_attn_num_splits(B, Q, 64, Lmax, 0)
+                    == binding.mla_latent_attn_num_splits(B, Q // 2, 64, Lmax, 0, indexed=True)), (B, Q)
+        for Q in (1, 3, 5, 7):
+            assert (binding.mla_latent_attn_num_splits(B, Q, 64, Lmax, 0)
+                    == binding.mla_latent_attn_num_splits(B, Q, 64, Lmax, 0, indexed=True)), (B, Q)
+    # 16 sequences of 32,768 positions: one round of 256 (Q = 2: 16 pairs x 16; Q = 8: 64 x 4)
+    assert binding.mla_latent_attn_num_splits(16, 2, 64, 32768, 0) == 16
+    assert binding.mla_latent_attn_num_splits(16, 8, 64, 32768, 0) == 4
     assert binding.mla_latent_attn_num_splits(32, 4, 64, 2052, 0, indexed=True) == 2
     assert binding.mla_latent_attn_workspace_size(32, 4, 64, 512, 2052, 0, indexed=True) == 2 * 128 * 64 * 514 * 4
 
