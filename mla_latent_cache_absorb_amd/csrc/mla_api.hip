@@ -33,8 +33,8 @@ int check_device(int* cus) {
 }
 
 // The split count.  Independent work units are (sequence, query unit, 64-head group), a
-// query unit being one query, or two queries of one sequence when several share its cache
-// (dense calls with Q > 1); the positions of each unit are cut into `s` contiguous splits of
+// query unit being one query, or two adjacent queries of one sequence in dense calls with an
+// even Q (mla::query_units); the positions of each unit are cut into `s` contiguous splits of
 // whole tiles, one workgroup per CU.  The estimate charges the rounds of resident workgroups
 // times the tiles of one split, plus the partial results each extra split writes and the
 // merge reads back (a 128 KiB partial per query is worth four 32 KiB tiles each way) and a
