@@ -76,6 +76,57 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, size_t row, int t) 
   if (a.lse != nullptr && t == 0) a.lse[row] = lse2 * 0.69314718055994531f;
 }
 
+// Byte offsets, within a tile, of a value wave's transposed A-operand reads for latents 128lq ..
+// (lane l: latent l % 32 of a 32-latent block, positions 8(l/32) .. +7 of a 16-position k-step):
+// in each 16-lane group g, lane 4e + q names tile row base + e, latents 16(g&1) + 4q .. +3, and
+// receives latent 16(g&1) + (lane & 15) of rows base .. base+3; rows 8(g>>1) + e (k-slots 0-3)
+// and +4 (k-slots 4-7).  With the swizzle swz(r) = 4(r & 3) + ((r >> 2) & 3), latent block mb of
+// quarter lq sits at byte 256lq + 64(mb ^ e) + 16(x ^ f) + 8(q & 1), x = 2(g&1) + (q >> 1),
+// f = (row >> 2) & 3; te = e selects the block order.
+struct TrOffsets {
+  int tb0, tb1, te;
+};
+__device__ __forceinline__ TrOffsets transpose_offsets(int lane, int lq) {
+  const int g = lane >> 4, ip = lane & 15, te = ip >> 2, tq = ip & 3;
+  const int x = 2 * (g & 1) + (tq >> 1);
+  const int row0 = 8 * (g >> 1) + te, row1 = row0 + 4;
+  return {row0 * kRowBytes + 256 * lq + ((x ^ ((row0 >> 2) & 3)) << 4) + ((tq & 1) << 3),
+          row1 * kRowBytes + 256 * lq + ((x ^ ((row1 >> 2) & 3)) << 4) + ((tq & 1) << 3), te};
+}
+
+// A value wave's result for one head column hv of row bq: lane holds latents 128lq + 32mb + 8ii
+// + 4hf + j.  With one split, o_lat = o / l and lse = (m + log2 l) ln 2 are final; otherwise the
+// unnormalised partial and its (m, l) go to the split's slot for the merge.
+__device__ __forceinline__ void store_value_rows(const AttnArgs& a, int split, int bq, int hv, int lq, int hf,
+                                                 float m_fin, float l_fin, const f32x16 (&o)[4]) {
+  if (a.num_splits == 1) {
+    const float inv_l = 1.0f / l_fin;
+    float* orow = a.o_lat + ((size_t)bq * a.H + hv) * kLatent + 128 * lq + 4 * hf;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        *(f32x4*)(orow + 32 * mb + 8 * ii) = (f32x4){o[mb][4 * ii] * inv_l, o[mb][4 * ii + 1] * inv_l,
+                                                    o[mb][4 * ii + 2] * inv_l, o[mb][4 * ii + 3] * inv_l};
+    // __builtin_amdgcn_logf is the hardware base-2 logarithm
+    if (a.lse != nullptr && hf == 0 && lq == 0)
+      a.lse[(size_t)bq * a.H + hv] = (m_fin + __builtin_amdgcn_logf(l_fin)) * 0.69314718055994531f;
+  } else {
+    const size_t prow_idx = ((size_t)split * a.B * a.Q + bq) * a.H + hv;
+    float* orow = a.part_o + prow_idx * kLatent + 128 * lq + 4 * hf;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        *(f32x4*)(orow + 32 * mb + 8 * ii) =
+            (f32x4){o[mb][4 * ii], o[mb][4 * ii + 1], o[mb][4 * ii + 2], o[mb][4 * ii + 3]};
+    if (hf == 0 && lq == 0) {
+      a.part_ml[2 * prow_idx] = m_fin;
+      a.part_ml[2 * prow_idx + 1] = l_fin;
+    }
+  }
+}
+
 template <bool INDEXED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void latent_attn_kernel(AttnArgs a) {
@@ -300,17 +351,9 @@ void latent_attn_kernel(AttnArgs a) {
         for (int rr = 0; rr < kRowsPerVWave; ++rr) issue_row(t, rr);
       }
 
-    // transpose reads for the A operand (lane l: latent l % 32 of a 32-latent block, positions
-    // 8(l/32) .. +7 of a 16-position k-step): in each 16-lane group g, lane 4e + q names tile
-    // row base + e, latents 16(g&1) + 4q .. +3, and receives latent 16(g&1) + (lane & 15) of
-    // rows base .. base+3; rows 8(g>>1) + e (k-slots 0-3) and +4 (k-slots 4-7).  With the
-    // swizzle swz(r) = 4(r & 3) + ((r >> 2) & 3), latent block mb of quarter lq sits at byte
-    // 256lq + 64(mb ^ e) + 16(x ^ f) + 8(q & 1), x = 2(g&1) + (q >> 1), f = (row >> 2) & 3.
-    const int g = lane >> 4, ip = lane & 15, te = ip >> 2, tq = ip & 3;
-    const int x = 2 * (g & 1) + (tq >> 1);
-    const int row0 = 8 * (g >> 1) + te, row1 = row0 + 4;
-    const int tb0 = row0 * kRowBytes + 256 * lq + ((x ^ ((row0 >> 2) & 3)) << 4) + ((tq & 1) << 3);
-    const int tb1 = row1 * kRowBytes + 256 * lq + ((x ^ ((row1 >> 2) & 3)) << 4) + ((tq & 1) << 3);
+    // transpose reads for the A operand
+    const TrOffsets tro = transpose_offsets(lane, lq);
+    const int tb0 = tro.tb0, tb1 = tro.tb1, te = tro.te;
     const int hv = hg * 64 + 32 * vh + hl;  // this lane's head (output column)
 
     f32x16 o[4];
@@ -376,35 +419,7 @@ void latent_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();  // (m, l) are posted
-    const float m_fin = mlbuf[0][32 * vh + hl];
-    const float l_fin = mlbuf[1][32 * vh + hl];
-    // lane holds head hv, latents 128lq + 32mb + 8ii + 4hf + j
-    if (a.num_splits == 1) {
-      const float inv_l = 1.0f / l_fin;
-      float* orow = a.o_lat + ((size_t)bq * a.H + hv) * kLatent + 128 * lq + 4 * hf;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          *(f32x4*)(orow + 32 * mb + 8 * ii) = (f32x4){o[mb][4 * ii] * inv_l, o[mb][4 * ii + 1] * inv_l,
-                                                      o[mb][4 * ii + 2] * inv_l, o[mb][4 * ii + 3] * inv_l};
-      // __builtin_amdgcn_logf is the hardware base-2 logarithm
-      if (a.lse != nullptr && hf == 0 && lq == 0)
-        a.lse[(size_t)bq * a.H + hv] = (m_fin + __builtin_amdgcn_logf(l_fin)) * 0.69314718055994531f;
-    } else {
-      const size_t prow_idx = ((size_t)split * a.B * a.Q + bq) * a.H + hv;
-      float* orow = a.part_o + prow_idx * kLatent + 128 * lq + 4 * hf;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          *(f32x4*)(orow + 32 * mb + 8 * ii) =
-              (f32x4){o[mb][4 * ii], o[mb][4 * ii + 1], o[mb][4 * ii + 2], o[mb][4 * ii + 3]};
-      if (hf == 0 && lq == 0) {
-        a.part_ml[2 * prow_idx] = m_fin;
-        a.part_ml[2 * prow_idx + 1] = l_fin;
-      }
-    }
+    store_value_rows(a, split, bq, hv, lq, hf, mlbuf[0][32 * vh + hl], mlbuf[1][32 * vh + hl], o);
   }
 }
 
@@ -599,20 +614,17 @@ void latent_attn_pair_kernel(AttnArgs a) {
         for (int rr = 0; rr < kRowsPerVWave; ++rr) issue_row(t, rr);
 
     // transpose reads for the A operand, as in the single-query form
-    const int g = lane >> 4, ip = lane & 15, te = ip >> 2, tq = ip & 3;
-    const int x = 2 * (g & 1) + (tq >> 1);
-    const int row0 = 8 * (g >> 1) + te, row1 = row0 + 4;
-    const int tb0 = row0 * kRowBytes + 256 * lq + ((x ^ ((row0 >> 2) & 3)) << 4) + ((tq & 1) << 3);
-    const int tb1 = row1 * kRowBytes + 256 * lq + ((x ^ ((row1 >> 2) & 3)) << 4) + ((tq & 1) << 3);
+    const TrOffsets tro = transpose_offsets(lane, lq);
+    const int tb0 = tro.tb0, tb1 = tro.tb1, te = tro.te;
     const int prow0 = 64 * qq + hl;  // P / rescale row of head half 0 (half 1: +32)
 
-    f32x16 o[4][2];
+    f32x16 o[2][4];  // [head half][latent block]
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int k = 0; k < 16; ++k) o[mb][nb][k] = 0.f;
+        for (int k = 0; k < 16; ++k) o[nb][mb][k] = 0.f;
     wait_vmcnt<0>();
     __syncthreads();  // the first two tiles have landed
 
@@ -635,7 +647,7 @@ void latent_attn_pair_kernel(AttnArgs a) {
         const float alpha = abuf[tv_ & 1][prow0 + 32 * nb];
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) o[mb][nb] *= alpha;
+          for (int mb = 0; mb < 4; ++mb) o[nb][mb] *= alpha;
         }
       }
       // P of the first k-step now, of the second once its last product has been issued
@@ -662,8 +674,8 @@ void latent_attn_pair_kernel(AttnArgs a) {
         if ((n & 1) == 0 && cp < ntiles) issue_row(cp, n >> 1);
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8 av = concat_bf16(tv[n % (kAhead + 1)][0], tv[n % (kAhead + 1)][1]);
-        o[n & 3][0] = mfma32(av, pf[0], o[n & 3][0]);
-        o[n & 3][1] = mfma32(av, pf[1], o[n & 3][1]);
+        o[0][n & 3] = mfma32(av, pf[0], o[0][n & 3]);
+        o[1][n & 3] = mfma32(av, pf[1], o[1][n & 3]);
         __builtin_amdgcn_sched_barrier(0);
         if (n == 3)
 #pragma unroll
@@ -673,40 +685,10 @@ void latent_attn_pair_kernel(AttnArgs a) {
     __syncthreads();  // (m, l) are posted
     const int iq = qq == 0 ? i0 : i1;
     if (iq >= 0) {
-      const int bq = b * a.Q + iq;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int hv = hg * 64 + 32 * nb + hl;  // this lane's head (output column)
-        const float m_fin = mlbuf[0][prow0 + 32 * nb];
-        const float l_fin = mlbuf[1][prow0 + 32 * nb];
-        // lane holds head hv, latents 128lq + 32mb + 8ii + 4hf + j
-        if (a.num_splits == 1) {
-          const float inv_l = 1.0f / l_fin;
-          float* orow = a.o_lat + ((size_t)bq * a.H + hv) * kLatent + 128 * lq + 4 * hf;
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-              *(f32x4*)(orow + 32 * mb + 8 * ii) =
-                  (f32x4){o[mb][nb][4 * ii] * inv_l, o[mb][nb][4 * ii + 1] * inv_l, o[mb][nb][4 * ii + 2] * inv_l,
-                          o[mb][nb][4 * ii + 3] * inv_l};
-          if (a.lse != nullptr && hf == 0 && lq == 0)
-            a.lse[(size_t)bq * a.H + hv] = (m_fin + __builtin_amdgcn_logf(l_fin)) * 0.69314718055994531f;
-        } else {
-          const size_t prow_idx = ((size_t)split * a.B * a.Q + bq) * a.H + hv;
-          float* orow = a.part_o + prow_idx * kLatent + 128 * lq + 4 * hf;
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-              *(f32x4*)(orow + 32 * mb + 8 * ii) = (f32x4){o[mb][nb][4 * ii], o[mb][nb][4 * ii + 1],
-                                                           o[mb][nb][4 * ii + 2], o[mb][nb][4 * ii + 3]};
-          if (hf == 0 && lq == 0) {
-            a.part_ml[2 * prow_idx] = m_fin;
-            a.part_ml[2 * prow_idx + 1] = l_fin;
-          }
-        }
-      }
+      for (int nb = 0; nb < 2; ++nb)
+        store_value_rows(a, split, b * a.Q + iq, hg * 64 + 32 * nb + hl, lq, hf, mlbuf[0][prow0 + 32 * nb],
+                         mlbuf[1][prow0 + 32 * nb], o[nb]);
     }
   }
 }
