@@ -76,6 +76,58 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, size_t row, int t) 
   if (a.lse != nullptr && t == 0) a.lse[row] = lse2 * 0.69314718055994531f;
 }
 
+// Largest of this lane's eight scores of a tile and those of the other three lanes of its head
+// (one column of the two 16x16 score blocks), times scale * log2(e).
+__device__ __forceinline__ float tile_max(const float (&v)[8], float c2) {
+  const float m = fmaxf(fmaxf(fmaxf(v[0], v[4]), fmaxf(v[1], v[5])), fmaxf(fmaxf(v[2], v[6]), fmaxf(v[3], v[7])));
+  return quad_max(m) * c2;
+}
+
+// One tile of the online softmax for this lane's head (scale > 0 keeps the order of the maxima):
+// the running maximum m_run (scale * log2(e) units) moves only when it grows by more than
+// 2^kRescaleLog2, so the accumulators are rarely rescaled; p receives 2^(v c2 - m_run) and l_run
+// their sum over the head's four lanes.  Returns the factor the head's accumulated values must be
+// rescaled by.
+__device__ __forceinline__ float softmax_step(const float (&v)[8], float tmax, float c2, float& m_run, float& l_run,
+                                              float (&p)[8]) {
+  const float m_new = fmaxf(m_run, tmax);
+  const bool need = m_new > m_run + kRescaleLog2;
+  float alpha = 1.f;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float m_use = need ? m_new : m_run;
+    alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
+    l_run *= alpha;
+    m_run = m_use;
+  }
+  const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -msafe));
+  l_run += quad_sum(((p[0] + p[4]) + (p[1] + p[5])) + ((p[2] + p[6]) + (p[3] + p[7])));
+  return alpha;
+}
+
+// P of one head in bf16 at prow (its row, plus 8 bytes per lane group G).  Lane G holds positions
+// 16 blk + 4jj + G; a 4 x 4 transpose across the lanes G = 0..3 of the head (pairs G^1 swapped
+// first, then G^2) gives it positions 16 blk + 4G + jj, four consecutive entries of the row.
+__device__ __forceinline__ void store_p_row(uint8_t* prow, const float (&p)[8]) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    unsigned u[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) u[jj] = __builtin_bit_cast(unsigned, p[4 * blk + jj]);
+    auto r01 = __builtin_amdgcn_permlane16_swap(u[0], u[1], false, false);
+    auto r23 = __builtin_amdgcn_permlane16_swap(u[2], u[3], false, false);
+    auto r02 = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
+    auto r13 = __builtin_amdgcn_permlane32_swap(r01[1], r23[1], false, false);
+    s16x4 pv;
+    pv[0] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[0]));
+    pv[1] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[0]));
+    pv[2] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[1]));
+    pv[3] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[1]));
+    *(s16x4*)(prow + 32 * blk) = pv;
+  }
+}
+
 // Byte offsets, within a tile, of a value wave's transposed A-operand reads for latents 128lq ..
 // (lane l: latent l % 32 of a 32-latent block, positions 8(l/32) .. +7 of a 16-position k-step):
 // in each 16-lane group g, lane 4e + q names tile row base + e, latents 16(g&1) + 4q .. +3, and
@@ -244,43 +296,9 @@ void latent_attn_kernel(AttnArgs a) {
             if (!((valid >> (16 * (k >> 2) + 4 * (k & 3) + G)) & 1u)) v[k] = -INFINITY;
         }
       }
-      // online softmax (scale > 0 keeps the order of the maxima)
-      float tmax = fmaxf(fmaxf(fmaxf(v[0], v[4]), fmaxf(v[1], v[5])), fmaxf(fmaxf(v[2], v[6]), fmaxf(v[3], v[7])));
-      tmax = quad_max(tmax) * c2;
-      const float m_new = fmaxf(m_run, tmax);
-      const bool need = m_new > m_run + kRescaleLog2;
-      float alpha = 1.f;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_use = need ? m_new : m_run;
-        alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
-        l_run *= alpha;
-        m_run = m_use;
-      }
-      const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
       float p[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -msafe));
-      l_run += quad_sum(((p[0] + p[4]) + (p[1] + p[5])) + ((p[2] + p[6]) + (p[3] + p[7])));
-      // P in bf16: head row 16s + c.  Lane G holds positions 16 blk + 4jj + G; a 4 x 4
-      // transpose across the lanes G = 0..3 of head c (pairs G^1 swapped first, then G^2) gives
-      // it positions 16 blk + 4G + jj, four consecutive entries of the row
-      uint8_t* prow = pbuf[t & 1] + (16 * s + c) * kPStride + 8 * G;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        unsigned u[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) u[jj] = __builtin_bit_cast(unsigned, p[4 * blk + jj]);
-        auto r01 = __builtin_amdgcn_permlane16_swap(u[0], u[1], false, false);
-        auto r23 = __builtin_amdgcn_permlane16_swap(u[2], u[3], false, false);
-        auto r02 = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
-        auto r13 = __builtin_amdgcn_permlane32_swap(r01[1], r23[1], false, false);
-        s16x4 pv;
-        pv[0] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[0]));
-        pv[1] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[0]));
-        pv[2] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[1]));
-        pv[3] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[1]));
-        *(s16x4*)(prow + 32 * blk) = pv;
-      }
+      const float alpha = softmax_step(v, tile_max(v, c2), c2, m_run, l_run, p);
+      store_p_row(pbuf[t & 1] + (16 * s + c) * kPStride + 8 * G, p);  // P row of head 16s + c
       if (G == 0) abuf[t & 1][16 * s + c] = alpha;
     }
     if (G == 0) {
@@ -548,47 +566,17 @@ void latent_attn_pair_kernel(AttnArgs a) {
           for (int k = 0; k < 8; ++k)
             if (!((vg >> (16 * (k >> 2) + 4 * (k & 3))) & 1u)) v[k] = -INFINITY;
         }
-        float tmax = fmaxf(fmaxf(fmaxf(v[0], v[4]), fmaxf(v[1], v[5])), fmaxf(fmaxf(v[2], v[6]), fmaxf(v[3], v[7])));
-        tmax = quad_max(tmax) * c2;
+        const float tmax = tile_max(v, c2);
         const int lp = opaque(lane);
         const int row = 64 * qq + 16 * s + (lp & 15);  // P / rescale / (m, l) row of this lane
         float m_run = mlbuf[0][row], l_run = mlbuf[1][row];
-        const float m_new = fmaxf(m_run, tmax);
-        const bool need = m_new > m_run + kRescaleLog2;
-        float alpha = 1.f;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          const float m_use = need ? m_new : m_run;
-          alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
-          l_run *= alpha;
-          m_run = m_use;
-        }
-        const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
         float p[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k], c2, -msafe));
-        l_run += quad_sum(((p[0] + p[4]) + (p[1] + p[5])) + ((p[2] + p[6]) + (p[3] + p[7])));
+        const float alpha = softmax_step(v, tmax, c2, m_run, l_run, p);
         if (lp < 16) {
           mlbuf[0][row] = m_run;
           mlbuf[1][row] = l_run;
         }
-        // P row 64qq + 16s + c, transposed across the lanes G as in the single-query form
-        uint8_t* prow = pbuf[t & 1] + row * kPStride + 8 * (lp >> 4);
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          unsigned u[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) u[jj] = __builtin_bit_cast(unsigned, p[4 * blk + jj]);
-          auto r01 = __builtin_amdgcn_permlane16_swap(u[0], u[1], false, false);
-          auto r23 = __builtin_amdgcn_permlane16_swap(u[2], u[3], false, false);
-          auto r02 = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
-          auto r13 = __builtin_amdgcn_permlane32_swap(r01[1], r23[1], false, false);
-          s16x4 pv;
-          pv[0] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[0]));
-          pv[1] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[0]));
-          pv[2] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r02[1]));
-          pv[3] = __builtin_bit_cast(short, (__bf16)__builtin_bit_cast(float, (unsigned)r13[1]));
-          *(s16x4*)(prow + 32 * blk) = pv;
-        }
+        store_p_row(pbuf[t & 1] + row * kPStride + 8 * (lp >> 4), p);
         if (lp < 16) abuf[t & 1][row] = alpha;
       }
     }
