@@ -1,6 +1,6 @@
 """Boundaries the product keeps (CPU only): the library package never imports the oracle, no
-product source reads the reference pages, and the benchmark refuses more than one GPU with a
-message."""
+product source reads the reference pages, the benchmark refuses more than one GPU with a
+message, and its measured-traffic figure is tied to the kernels' code."""
 import os
 import re
 import subprocess
@@ -35,3 +35,18 @@ def test_bench_refuses_several_gpus():
                        text=True, cwd=ROOT, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_counter_digest_follows_code_not_comments():
+    # bench.py reports measured HBM traffic only while the kernels' code matches the code the
+    # counters were taken on: comments and layout must not change the digest, code must
+    sys.path.insert(0, ROOT)
+    import bench
+
+    src = "int f(int x) {  // doubles x\n  /* no-op */ return 2 * x;\n}\n"
+    assert bench.code_text(src) == bench.code_text("int f(int x)\n{\n return 2 * x; // twice\n}")
+    assert bench.code_text(src) != bench.code_text(src.replace("2 * x", "3 * x"))
+    assert bench.code_text("a /* b */ c // d\ne") == "a c e"
+    digest = bench.kernel_source_digest()
+    assert re.fullmatch(r"[0-9a-f]{16}", digest)
+    assert bench.kernel_source_digest() == digest
