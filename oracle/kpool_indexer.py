@@ -31,7 +31,13 @@ from __future__ import annotations
 
 import numpy as np
 
-from .mla_oracle import bf16_bits_to_f64
+from .mla_oracle import bf16_bits_to_f64, query_position
+
+
+def complete_pools(cache_len: int, pool: int) -> int:
+    """Pools whose every member position lies inside a cache of cache_len positions (pool p holds
+    positions p*pool .. p*pool + pool - 1)."""
+    return int(cache_len) // int(pool)
 
 
 def pooled_keys(k_bits: np.ndarray, g_bits: np.ndarray, pool: int, n_pools: int) -> np.ndarray:
@@ -85,11 +91,11 @@ def indexer_reference(q_bits: np.ndarray, k_bits: np.ndarray, g_bits: np.ndarray
     all_scores = []
     for b in range(B):
         L = int(cache_len[b])
-        n_pools = L // pool
+        n_pools = complete_pools(L, pool)
         pk = pooled_keys(k_bits[b], g_bits[b], pool, n_pools)
         row_scores = []
         for i in range(Q):
-            t = L - Q + i
+            t = query_position(L, Q, i)
             s = pool_scores(q_bits[b, i], pk) if n_pools else np.zeros(0)
             sel = select_positions(s, t, pool, topk, tail) if t >= 0 else np.zeros(0, np.int32)
             idx[b, i, : sel.size] = sel
