@@ -231,6 +231,76 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
     return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, stage_pct_ms=pct, splits=splits, workload=w0)
 
 
+def time_latency(name: str = "decode_b1_l256", samples: int = 200):
+    """Per-call latency of the path at batch 1 (Module 05 section 5's decode-shaped workload,
+    one sequence whose cache grows by one position per call): absorb_q, the fused attention with
+    up-projection, and the two together.  Each is captured in a HIP graph of one call; every
+    sample is one replay between its own pair of HIP events, started behind a short GPU spin so
+    that the events bracket the kernels rather than the host's launch.  Reports p10 / p50 / p90
+    and the mean of back-to-back replays of a graph of `samples` calls (launch gaps hidden)."""
+    import torch
+    from mla_latent_cache_absorb_amd import binding
+
+    dev = torch.device("cuda:0")
+    from mla_latent_cache_absorb_amd import workloads as wl
+    w = wl.make_workload(name)
+    d = to_device(w, dev)
+    B, Q, H, D = w.q.shape
+    R = w.cache.shape[2]
+    Lmax = int(w.cache.shape[1])
+    q_abs = torch.empty((B, Q, H, R), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(binding.mla_latent_attn_up_v_workspace_size(B, Q, H, R, Lmax, 0), 1), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "absorb_q": lambda: binding.mla_absorb_q(d["q"], d["w_k"], q_abs=q_abs),
+        "latent_attn_up_v": lambda: binding.mla_latent_attn_up_v(q_abs, d["cache"], d["cache_len"], Lmax, w.scale,
+                                                                 d["w_v"], out=out, lse=lse, workspace=ws),
+    }
+    calls["path"] = lambda: (calls["absorb_q"](), calls["latent_attn_up_v"]())
+    spin = getattr(torch.cuda, "_sleep", None)
+    res = {"workload": name, "batch": B, "q_len": Q, "cache_len": Lmax,
+           "splits": binding.mla_latent_attn_num_splits(B, Q, H, Lmax, 0)}
+    for k, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1):
+            fn()
+        gn = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gn):
+            for _ in range(samples):
+                fn()
+        for _ in range(10):
+            g1.replay()
+        gn.replay()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(samples):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if spin is not None:
+                spin(20000)
+            e0.record(stream)
+            g1.replay()
+            e1.record(stream)
+            e1.synchronize()
+            per.append(e0.elapsed_time(e1))
+        per.sort()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gn.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[k] = {"p10_p50_p90_ms": [round(per[int(f * (samples - 1) + 0.5)], 6) for f in (0.1, 0.5, 0.9)],
+                  "mean_back_to_back_ms": round(e0.elapsed_time(e1) / samples, 6)}
+        del g1, gn
+    res["sample_note"] = ("each sample one graph replay between its own events, behind a GPU spin"
+                          if spin is not None else "each sample one graph replay between its own events")
+    return res
+
+
 def time_indexer(name: str, steps: int, warmup: int):
     """The k-pooled indexer on the sequences of `name`: pooled keys (a full build, and a decode
     step's build of each sequence's newest pool), pool scores for all queries, top-k selection
@@ -596,7 +666,13 @@ def cpu_baseline(name: str, budget_s: float = 12.0):
         done += 1
     dt = time.perf_counter() - t0
     gbs = rows * w.cache.shape[2] * 2 / dt / 1e9
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    # cores = the BLAS threads the oracle ran on; the host's own core counts are stated beside it
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "host_cpus_usable": affinity,
             "sample": f"{done} of {B} sequences of {name} (all {w.q.shape[2]} heads, expanded fp64), {dt:.1f} s"}
 
 
@@ -615,6 +691,9 @@ def main():
     ap.add_argument("--no-crossover", action="store_true")
     ap.add_argument("--no-qlen-sweep", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--latency-only", action="store_true",
+                    help="time only the batch-1 decode latency (256 positions), for profiling it on its own")
     ap.add_argument("--other-configs-only", action="store_true",
                     help="time only the attention on the 131,072-position decode and the indexed verification")
     ap.add_argument("--qlen-sweep-only", action="store_true",
@@ -653,6 +732,9 @@ def main():
         log(f"[bench] copied {args.calibrate_copy} MiB three times")
         del src, dst
         torch.cuda.empty_cache()
+    if args.latency_only:
+        print(json.dumps({"latency_b1": time_latency()}), flush=True)
+        return
     if args.other_configs_only:
         print(json.dumps({"other_configs": time_other_configs()}), flush=True)
         return
@@ -733,6 +815,9 @@ def main():
             "launch_ms_p10_p50_p90": [round(x, 6) for x in s["stage_pct_ms"]["latent_attn"]],
             "fused_attn_up_v": {"value": round(tf_fused, 2), "unit": "TFLOP/s",
                                 "frac": round(tf_fused / BF16_PEAK_TFLOPS, 4), "flops": fused_flops}}
+    if not args.no_latency:
+        log("[bench] timing the batch-1 decode latency")
+        result["latency_b1"] = time_latency()
     if not args.no_indexer:
         torch.cuda.empty_cache()
         log("[bench] timing the k-pooled indexer")

@@ -15,8 +15,8 @@
  *                         "DSA with k-pooling");
  *     3. mla_up_v         out_h = U_h^V o_lat,h, the one expansion at the end.
  *   Composed, they equal ordinary softmax attention on the expanded keys and values
- *   (an identity, not an approximation); the scores equal the expanded scores, with the
- *   same scale.
+ *   (exactly: only the order of the products changes, colibri "MLA is absorbed"); the scores
+ *   equal the expanded scores, with the same scale.
  *
  * Conventions shared by every call
  *   - All tensor arguments are DEVICE pointers owned by the caller (the library never

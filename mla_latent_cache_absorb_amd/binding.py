@@ -102,11 +102,34 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# Every wrapper checks, in this order and before anything is launched: each tensor's dtype and
+# layout (_need), every extent against the sizes the call is given (_shape and the wrapper's own
+# checks, ValueError), then that every tensor lives on the GPU of the first one (_gpu).  The C ABI
+# receives raw pointers and cannot see a tensor's extent, so a mismatch caught here would
+# otherwise become an out-of-bounds device access.
 def _need(t: torch.Tensor, dtype, name: str, contiguous: bool = True):
-    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
-        raise TypeError(f"{name} must be a {dtype} tensor on the GPU")
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise TypeError(f"{name} must be a {dtype} tensor")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _shape(t: Optional[torch.Tensor], want, name: str):
+    if t is not None and tuple(t.shape) != tuple(int(x) for x in want):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in want)}, got {tuple(t.shape)}")
+
+
+def _gpu(*tensors):
+    """Every given tensor (None skipped) is on the GPU, the same one as the first."""
+    ts = [t for t in tensors if t is not None]
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda or t.device != dev:
+            raise TypeError(f"every tensor must be on the same GPU ({dev}); got one on {t.device}")
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 # ----------------------------------------------------------------------------------------
@@ -115,13 +138,18 @@ def mla_absorb_q(q: torch.Tensor, w_k: torch.Tensor, q_abs: Optional[torch.Tenso
     """q [..., H, D] bf16, w_k [H, D, R] bf16 -> q_abs [..., H, R] bf16 = prescale * W_k^T q."""
     _need(q, torch.bfloat16, "q")
     _need(w_k, torch.bfloat16, "w_k")
+    if w_k.dim() != 3:
+        raise ValueError("w_k must be [H, D, R]")
     H, D, R = w_k.shape
-    rows = q.numel() // (H * D)
-    if q.shape[-2:] != (H, D):
+    if q.dim() < 2 or tuple(q.shape[-2:]) != (H, D):
         raise ValueError("q must end in [H, D]")
+    rows = q.numel() // (H * D)
+    if q_abs is not None:
+        _need(q_abs, torch.bfloat16, "q_abs")
+        _shape(q_abs, tuple(q.shape[:-1]) + (R,), "q_abs")
+    _gpu(q, w_k, q_abs)
     if q_abs is None:
         q_abs = torch.empty(q.shape[:-1] + (R,), dtype=torch.bfloat16, device=q.device)
-    _need(q_abs, torch.bfloat16, "q_abs")
     _check(lib().mla_absorb_q(_ptr(q), _ptr(w_k), _ptr(q_abs), rows, H, D, R, float(prescale), _stream(stream)),
            "mla_absorb_q")
     return q_abs
@@ -145,16 +173,57 @@ def _cache_stride(cache: torch.Tensor) -> int:
     return int(cache.stride(0))
 
 
+def _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx=None, idx_len=None):
+    """dtype and extent checks shared by the attention calls; returns (B, Q, H, R, K_max)."""
+    _need(q_abs, torch.bfloat16, "q_abs")
+    _need(cache, torch.bfloat16, "cache", contiguous=False)
+    _need(cache_len, torch.int32, "cache_len")
+    if q_abs.dim() != 4:
+        raise ValueError("q_abs must be [B, Q, H, R]")
+    B, Q, H, R = q_abs.shape
+    _cache_stride(cache)
+    if cache.shape[0] != B or cache.shape[2] != R:
+        raise ValueError(f"cache must be [B={B}, L, R={R}], got {tuple(cache.shape)}")
+    if int(max_cache_len) < 1 or cache.shape[1] < int(max_cache_len):
+        raise ValueError(f"max_cache_len ({max_cache_len}) must be in [1, cache.shape[1] = {cache.shape[1]}]")
+    _shape(cache_len, (B,), "cache_len")
+    K_max = 0
+    if (idx is None) != (idx_len is None):
+        raise ValueError("idx and idx_len go together")
+    if idx is not None:
+        _need(idx, torch.int32, "idx")
+        _need(idx_len, torch.int32, "idx_len")
+        if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, Q) or idx.shape[2] < 1:
+            raise ValueError(f"idx must be [B={B}, Q={Q}, K_max >= 1], got {tuple(idx.shape)}")
+        K_max = int(idx.shape[2])
+        _shape(idx_len, (B, Q), "idx_len")
+    return B, Q, H, R, K_max
+
+
 def _attn_outputs(q_abs, o_lat, lse, want_lse):
+    B, Q, H, R = q_abs.shape
+    if o_lat is not None:
+        _need(o_lat, torch.float32, "o_lat")
+        _shape(o_lat, (B, Q, H, R), "o_lat")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+        _shape(lse, (B, Q, H), "lse")
+    return o_lat, lse
+
+
+def _alloc_outputs(q_abs, o_lat, lse, want_lse):
     B, Q, H, R = q_abs.shape
     if o_lat is None:
         o_lat = torch.empty((B, Q, H, R), dtype=torch.float32, device=q_abs.device)
-    _need(o_lat, torch.float32, "o_lat")
     if lse is None and want_lse:
         lse = torch.empty((B, Q, H), dtype=torch.float32, device=q_abs.device)
-    if lse is not None:
-        _need(lse, torch.float32, "lse")
     return o_lat, lse
+
+
+def _workspace_arg(workspace):
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor")
+    return workspace
 
 
 def _workspace(workspace, need, device):
@@ -175,12 +244,20 @@ def mla_check_attn_inputs(cache_len: torch.Tensor, Q: int, max_cache_len: int, i
     """Check the attention calls' device-side preconditions on the GPU; returns the flag word
     (0 = all hold; else an OR of the keys of BAD_INPUT_BITS).  Synchronises the stream."""
     _need(cache_len, torch.int32, "cache_len")
+    if cache_len.dim() != 1:
+        raise ValueError("cache_len must be [B]")
     B = cache_len.numel()
     K_max = 0
+    if (idx is None) != (idx_len is None):
+        raise ValueError("idx and idx_len go together")
     if idx is not None:
         _need(idx, torch.int32, "idx")
         _need(idx_len, torch.int32, "idx_len")
+        if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, int(Q)) or idx.shape[2] < 1:
+            raise ValueError(f"idx must be [B={B}, Q={Q}, K_max >= 1], got {tuple(idx.shape)}")
+        _shape(idx_len, (B, Q), "idx_len")
         K_max = idx.shape[-1]
+    _gpu(cache_len, idx, idx_len)
     flags = torch.empty(1, dtype=torch.int32, device=cache_len.device)
     _check(lib().mla_check_attn_inputs(_ptr(cache_len), _ptr(idx), _ptr(idx_len), B, int(Q), K_max,
                                        int(max_cache_len), _ptr(flags), _stream(stream)), "mla_check_attn_inputs")
@@ -204,17 +281,16 @@ def mla_latent_attn(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.T
                     stream=None):
     """Dense latent attention.  q_abs [B, Q, H, R] bf16; cache [B, L_max, R] bf16 (a view with any
     batch stride); cache_len [B] int32 on the GPU.  Returns (o_lat [B, Q, H, R] fp32, lse [B, Q, H])."""
-    _need(q_abs, torch.bfloat16, "q_abs")
-    _need(cache, torch.bfloat16, "cache", contiguous=False)
-    _need(cache_len, torch.int32, "cache_len")
-    B, Q, H, R = q_abs.shape
+    B, Q, H, R, _ = _attn_inputs(q_abs, cache, cache_len, max_cache_len)
     o_lat, lse = _attn_outputs(q_abs, o_lat, lse, want_lse)
+    _gpu(q_abs, cache, cache_len, o_lat, lse, _workspace_arg(workspace))
+    o_lat, lse = _alloc_outputs(q_abs, o_lat, lse, want_lse)
     _debug_check(cache_len, Q, max_cache_len, stream=stream)
     need = mla_latent_attn_workspace_size(B, Q, H, R, max_cache_len, num_splits)
     workspace = _workspace(workspace, need, q_abs.device)
     _check(lib().mla_latent_attn(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), B, Q, H, R,
                                  int(max_cache_len), float(scale), int(num_splits), _ptr(o_lat), _ptr(lse),
-                                 _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)),
+                                 _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "mla_latent_attn")
     return o_lat, lse
 
@@ -223,21 +299,19 @@ def mla_latent_attn_indexed(q_abs: torch.Tensor, cache: torch.Tensor, cache_len:
                             idx_len: torch.Tensor, max_cache_len: int, scale: float, num_splits: int = 0,
                             o_lat=None, lse=None, workspace=None, want_lse=True, stream=None):
     """Indexed latent attention: idx [B, Q, K_max] int32 (sorted positions), idx_len [B, Q] int32."""
-    _need(q_abs, torch.bfloat16, "q_abs")
-    _need(cache, torch.bfloat16, "cache", contiguous=False)
-    _need(cache_len, torch.int32, "cache_len")
-    _need(idx, torch.int32, "idx")
-    _need(idx_len, torch.int32, "idx_len")
-    B, Q, H, R = q_abs.shape
-    K_max = idx.shape[-1]
+    if idx is None or idx_len is None:
+        raise ValueError("the indexed call needs idx and idx_len")
+    B, Q, H, R, K_max = _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx, idx_len)
     o_lat, lse = _attn_outputs(q_abs, o_lat, lse, want_lse)
+    _gpu(q_abs, cache, cache_len, idx, idx_len, o_lat, lse, _workspace_arg(workspace))
+    o_lat, lse = _alloc_outputs(q_abs, o_lat, lse, want_lse)
     _debug_check(cache_len, Q, max_cache_len, idx, idx_len, stream=stream)
     need = mla_latent_attn_workspace_size(B, Q, H, R, K_max, num_splits, indexed=True)
     workspace = _workspace(workspace, need, q_abs.device)
     _check(lib().mla_latent_attn_indexed(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
                                          _ptr(idx_len), K_max, B, Q, H, R, int(max_cache_len), float(scale),
                                          int(num_splits), _ptr(o_lat), _ptr(lse), _ptr(workspace),
-                                         0 if workspace is None else workspace.numel(), _stream(stream)),
+                                         _nbytes(workspace), _stream(stream)),
            "mla_latent_attn_indexed")
     return o_lat, lse
 
@@ -246,13 +320,18 @@ def mla_up_v(o_lat: torch.Tensor, w_v: torch.Tensor, out: Optional[torch.Tensor]
     """o_lat [..., H, R] fp32, w_v [H, D, R] bf16 -> out [..., H, D] fp32 = W_v o_lat."""
     _need(o_lat, torch.float32, "o_lat")
     _need(w_v, torch.bfloat16, "w_v")
+    if w_v.dim() != 3:
+        raise ValueError("w_v must be [H, D, R]")
     H, D, R = w_v.shape
-    if o_lat.shape[-2:] != (H, R):
+    if o_lat.dim() < 2 or tuple(o_lat.shape[-2:]) != (H, R):
         raise ValueError("o_lat must end in [H, R]")
     rows = o_lat.numel() // (H * R)
+    if out is not None:
+        _need(out, torch.float32, "out")
+        _shape(out, tuple(o_lat.shape[:-1]) + (D,), "out")
+    _gpu(o_lat, w_v, out)
     if out is None:
         out = torch.empty(o_lat.shape[:-1] + (D,), dtype=torch.float32, device=o_lat.device)
-    _need(out, torch.float32, "out")
     _check(lib().mla_up_v(_ptr(o_lat), _ptr(w_v), _ptr(out), rows, H, D, R, _stream(stream)), "mla_up_v")
     return out
 
@@ -269,34 +348,30 @@ def mla_latent_attn_up_v(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: to
     """Latent attention (dense, or indexed when idx / idx_len are given) followed by the value
     up-projection, the split merge fused into the latter.  Returns (out [B, Q, H, D] fp32,
     lse [B, Q, H] fp32)."""
-    _need(q_abs, torch.bfloat16, "q_abs")
-    _need(cache, torch.bfloat16, "cache", contiguous=False)
-    _need(cache_len, torch.int32, "cache_len")
+    B, Q, H, R, K_max = _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx, idx_len)
     _need(w_v, torch.bfloat16, "w_v")
-    B, Q, H, R = q_abs.shape
+    if w_v.dim() != 3 or w_v.shape[0] != H or w_v.shape[2] != R:
+        raise ValueError(f"w_v must be [H={H}, D, R={R}], got {tuple(w_v.shape)}")
     D = w_v.shape[1]
-    if tuple(w_v.shape) != (H, D, R):
-        raise ValueError("w_v must be [H, D, R]")
     indexed = idx is not None
-    K_max = 0
-    if indexed:
-        _need(idx, torch.int32, "idx")
-        _need(idx_len, torch.int32, "idx_len")
-        K_max = idx.shape[-1]
-    if out is None:
-        out = torch.empty((B, Q, H, D), dtype=torch.float32, device=q_abs.device)
-    _need(out, torch.float32, "out")
-    if lse is None and want_lse:
-        lse = torch.empty((B, Q, H), dtype=torch.float32, device=q_abs.device)
+    if out is not None:
+        _need(out, torch.float32, "out")
+        _shape(out, (B, Q, H, D), "out")
     if lse is not None:
         _need(lse, torch.float32, "lse")
+        _shape(lse, (B, Q, H), "lse")
+    _gpu(q_abs, cache, cache_len, w_v, idx, idx_len, out, lse, _workspace_arg(workspace))
+    if out is None:
+        out = torch.empty((B, Q, H, D), dtype=torch.float32, device=q_abs.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=q_abs.device)
     _debug_check(cache_len, Q, max_cache_len, idx, idx_len, stream=stream)
     need = mla_latent_attn_up_v_workspace_size(B, Q, H, R, K_max if indexed else max_cache_len, num_splits, indexed)
     workspace = _workspace(workspace, need, q_abs.device)
     _check(lib().mla_latent_attn_up_v(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
                                       _ptr(idx_len), K_max, B, Q, H, R, int(max_cache_len), float(scale),
                                       int(num_splits), _ptr(w_v), D, _ptr(out), _ptr(lse), _ptr(workspace),
-                                      0 if workspace is None else workspace.numel(), _stream(stream)),
+                                      _nbytes(workspace), _stream(stream)),
            "mla_latent_attn_up_v")
     return out, lse
 
@@ -309,14 +384,18 @@ def mla_latent_append(h: torch.Tensor, w_dkv: torch.Tensor, cache: torch.Tensor,
     _need(h, torch.bfloat16, "h")
     _need(w_dkv, torch.bfloat16, "w_dkv")
     _need(cache_len, torch.int32, "cache_len")
-    if cache.dtype != torch.bfloat16:
-        raise TypeError("cache must be bfloat16")
-    if h.dim() != 3:
-        raise ValueError("h must be [B, Q, hidden]")
+    _need(cache, torch.bfloat16, "cache", contiguous=False)
+    if h.dim() != 3 or w_dkv.dim() != 2:
+        raise ValueError("h must be [B, Q, hidden] and w_dkv [R, hidden]")
     B, Q, hidden = h.shape
     R = w_dkv.shape[0]
-    if w_dkv.shape != (R, hidden) or cache.shape[0] != B or cache.shape[2] != R or cache_len.numel() != B:
-        raise ValueError("shape mismatch between h, w_dkv, cache and cache_len")
+    _cache_stride(cache)
+    if w_dkv.shape != (R, hidden) or cache.shape[0] != B or cache.shape[2] != R:
+        raise ValueError("shape mismatch between h, w_dkv and cache")
+    if int(max_cache_len) < 1 or cache.shape[1] < int(max_cache_len):
+        raise ValueError(f"max_cache_len ({max_cache_len}) must be in [1, cache.shape[1] = {cache.shape[1]}]")
+    _shape(cache_len, (B,), "cache_len")
+    _gpu(h, w_dkv, cache, cache_len)
     _check(lib().mla_latent_append(_ptr(h), _ptr(w_dkv), _ptr(cache), _cache_stride(cache), _ptr(cache_len), B, Q,
                                    hidden, R, int(max_cache_len), _stream(stream)), "mla_latent_append")
     return cache
@@ -337,18 +416,26 @@ def mla_expand_kv(cache: torch.Tensor, cache_len: torch.Tensor, w_k: torch.Tenso
     _need(cache_len, torch.int32, "cache_len")
     _need(w_k, torch.bfloat16, "w_k")
     _need(w_v, torch.bfloat16, "w_v")
+    if w_k.dim() != 3 or w_v.shape != w_k.shape:
+        raise ValueError("w_k and w_v must both be [H, D, R]")
     H, D, R = w_k.shape
+    _cache_stride(cache)
     B = cache.shape[0]
     L = int(max_cache_len)
+    if cache.shape[2] != R or L < 1 or cache.shape[1] < L:
+        raise ValueError(f"cache must be [B, L >= max_cache_len, R={R}], got {tuple(cache.shape)}")
+    _shape(cache_len, (B,), "cache_len")
     vt_len = vt_length(L)
+    for t, name in ((k_out, "k_out"), (vt_out, "vt_out")):
+        if t is not None:
+            _need(t, torch.bfloat16, name)
+    _shape(k_out, (B, L, H, D), "k_out")
+    _shape(vt_out, (B, H, D, vt_len), "vt_out")
+    _gpu(cache, cache_len, w_k, w_v, k_out, vt_out)
     if k_out is None:
         k_out = torch.empty((B, L, H, D), dtype=torch.bfloat16, device=cache.device)
     if vt_out is None:
         vt_out = torch.empty((B, H, D, vt_len), dtype=torch.bfloat16, device=cache.device)
-    _need(k_out, torch.bfloat16, "k_out")
-    _need(vt_out, torch.bfloat16, "vt_out")
-    if k_out.shape != (B, L, H, D) or vt_out.shape != (B, H, D, vt_len):
-        raise ValueError("k_out must be [B, max_cache_len, H, D] and vt_out [B, H, D, vt_length(max_cache_len)]")
     _check(lib().mla_expand_kv(_ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(w_k), _ptr(w_v), B, H, D, R,
                                L, _ptr(k_out), _ptr(vt_out), vt_len, _stream(stream)), "mla_expand_kv")
     return k_out, vt_out
@@ -363,9 +450,20 @@ def mla_naive_attn(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, cache_len
     _need(k, torch.bfloat16, "k")
     _need(vt, torch.bfloat16, "vt")
     _need(cache_len, torch.int32, "cache_len")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, Q, H, D]")
     B, Q, H, D = q.shape
-    if k.shape != (B, int(max_cache_len), H, D) or vt.shape[:3] != (B, H, D):
-        raise ValueError("k / vt do not match q and max_cache_len")
+    _shape(k, (B, int(max_cache_len), H, D), "k")
+    if vt.dim() != 4 or tuple(vt.shape[:3]) != (B, H, D) or vt.shape[3] < int(max_cache_len):
+        raise ValueError(f"vt must be [B={B}, H={H}, D={D}, >= max_cache_len], got {tuple(vt.shape)}")
+    _shape(cache_len, (B,), "cache_len")
+    if out is not None:
+        _need(out, torch.float32, "out")
+        _shape(out, (B, Q, H, D), "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+        _shape(lse, (B, Q, H), "lse")
+    _gpu(q, k, vt, cache_len, out, lse)
     if out is None:
         out = torch.empty((B, Q, H, D), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
@@ -396,17 +494,24 @@ def mla_kpool_keys(k: torch.Tensor, g: torch.Tensor, cache_len: torch.Tensor, ma
     _need(k, torch.bfloat16, "k", contiguous=False)
     _need(g, torch.bfloat16, "g", contiguous=False)
     _need(cache_len, torch.int32, "cache_len")
-    B, _, d = k.shape
     stride = _rows(k, "k")
+    B, Lk, d = k.shape
     if _rows(g, "g") != stride or g.shape != k.shape:
         raise ValueError("g must have the layout of k")
+    if int(max_cache_len) < 1 or Lk < int(max_cache_len):
+        raise ValueError(f"max_cache_len ({max_cache_len}) must be in [1, k.shape[1] = {Lk}]")
+    _shape(cache_len, (B,), "cache_len")
     if max_pools is None:
         max_pools = max(1, max_cache_len // pool)
-    if pooled is None:
-        pooled = torch.empty((B, max_pools, d), dtype=torch.float32, device=k.device)
-    _need(pooled, torch.float32, "pooled")
+    if pooled is not None:
+        _need(pooled, torch.float32, "pooled")
+        _shape(pooled, (B, max_pools, d), "pooled")
     if pool_begin is not None:
         _need(pool_begin, torch.int32, "pool_begin")
+        _shape(pool_begin, (B,), "pool_begin")
+    _gpu(k, g, cache_len, pooled, pool_begin)
+    if pooled is None:
+        pooled = torch.empty((B, max_pools, d), dtype=torch.float32, device=k.device)
     _check(lib().mla_kpool_keys(_ptr(k), _ptr(g), stride, _ptr(cache_len), _ptr(pool_begin), B, int(max_cache_len),
                                 d, int(pool), _ptr(pooled), int(max_pools), _stream(stream)), "mla_kpool_keys")
     return pooled
@@ -417,11 +522,20 @@ def mla_indexer_scores(q: torch.Tensor, pooled: torch.Tensor, cache_len: torch.T
     """q [B, Q, d] bf16, pooled [B, max_pools, d] fp32 -> scores [B, Q, max_pools] fp32."""
     _need(q, torch.bfloat16, "q")
     _need(pooled, torch.float32, "pooled")
+    _need(cache_len, torch.int32, "cache_len")
+    if q.dim() != 3 or pooled.dim() != 3:
+        raise ValueError("q must be [B, Q, d] and pooled [B, max_pools, d]")
     B, Q, d = q.shape
     max_pools = pooled.shape[1]
+    if pooled.shape[0] != B or pooled.shape[2] != d:
+        raise ValueError(f"pooled must be [B={B}, max_pools, d={d}], got {tuple(pooled.shape)}")
+    _shape(cache_len, (B,), "cache_len")
+    if scores is not None:
+        _need(scores, torch.float32, "scores")
+        _shape(scores, (B, Q, max_pools), "scores")
+    _gpu(q, pooled, cache_len, scores)
     if scores is None:
         scores = torch.empty((B, Q, max_pools), dtype=torch.float32, device=q.device)
-    _need(scores, torch.float32, "scores")
     _check(lib().mla_indexer_scores(_ptr(q), _ptr(pooled), _ptr(cache_len), B, Q, d, int(pool), max_pools,
                                     int(max_cache_len), _ptr(scores), _stream(stream)), "mla_indexer_scores")
     return scores
@@ -432,14 +546,24 @@ def mla_indexer_select(scores: torch.Tensor, cache_len: torch.Tensor, max_cache_
                        stream=None):
     """scores [B, Q, max_pools] fp32 -> (idx [B, Q, topk + pool - 1] int32, idx_len [B, Q] int32)."""
     _need(scores, torch.float32, "scores")
+    _need(cache_len, torch.int32, "cache_len")
+    if scores.dim() != 3:
+        raise ValueError("scores must be [B, Q, max_pools]")
     B, Q, max_pools = scores.shape
+    _shape(cache_len, (B,), "cache_len")
     K_max = topk + (pool - 1 if tail else 0)
+    if idx is not None:
+        _need(idx, torch.int32, "idx")
+        if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, Q):
+            raise ValueError(f"idx must be [B={B}, Q={Q}, K_max], got {tuple(idx.shape)}")
+    if idx_len is not None:
+        _need(idx_len, torch.int32, "idx_len")
+        _shape(idx_len, (B, Q), "idx_len")
+    _gpu(scores, cache_len, idx, idx_len)
     if idx is None:
         idx = torch.empty((B, Q, K_max), dtype=torch.int32, device=scores.device)
     if idx_len is None:
         idx_len = torch.empty((B, Q), dtype=torch.int32, device=scores.device)
-    _need(idx, torch.int32, "idx")
-    _need(idx_len, torch.int32, "idx_len")
     _check(lib().mla_indexer_select(_ptr(scores), _ptr(cache_len), B, Q, int(pool), max_pools, int(max_cache_len),
                                     int(topk), int(bool(tail)), _ptr(idx), _ptr(idx_len), idx.shape[2],
                                     _stream(stream)), "mla_indexer_select")

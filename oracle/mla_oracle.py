@@ -31,8 +31,8 @@ It is written in plain numpy, in float64, following the pages:
     ABSORBED form.
 * colibri "GLM-5.3-Flash engine (c/glm53.c)", section "MLA is absorbed": the
   two identities score_j = q.(W_k c_j) = (W_k^T q).c_j and
-  out = sum_j a_j (W_v c_j) = W_v (sum_j a_j c_j), "an identity, not an
-  approximation".
+  out = sum_j a_j (W_v c_j) = W_v (sum_j a_j c_j); the absorbed form is exact,
+  only the order of the products changes.
 * "Module 08 -- Vision, MTP, and Hybrid Serving State", section 2 (the full
   model verifies the drafted tokens in one forward pass) and section 3 (the MLA
   latent cache is truncatable by position).

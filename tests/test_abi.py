@@ -188,3 +188,110 @@ def test_input_check_host_validation(L):
     assert f(fake, fake, fake, 1, 1, 0, 10, fake, None) == binding.MLA_ERR_ARG
     # the flag bits the header names
     assert set(binding.BAD_INPUT_BITS) == {1, 2, 4, 8, 16, 32}
+
+
+# --------------------------------------------------------------------------------------------
+# The binding checks every tensor's extent against the call's sizes before anything is launched:
+# on tensors in host memory a mismatch raises ValueError and matching shapes get as far as the
+# device check (TypeError), so none of these calls reaches the library's compute entry points.
+def _bf(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _i32(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.int32)
+
+
+def _f32(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+def _attn_args(B=2, Q=3, H=64, R=512, L=40):
+    return dict(q_abs=_bf(B, Q, H, R), cache=_bf(B, L, R), cache_len=_i32(B), max_cache_len=L, scale=0.0625)
+
+
+def _expect(exc, fn, **kw):
+    with pytest.raises(exc):
+        fn(**kw)
+
+
+def test_attention_wrappers_check_every_extent(L):
+    ok = _attn_args()
+    _expect(TypeError, binding.mla_latent_attn, **ok)      # shapes fine: stopped by the device check
+    bad = [
+        dict(cache=_bf(3, 40, 512)),                        # more sequences than q_abs
+        dict(cache=_bf(1, 40, 512)),                        # fewer
+        dict(cache=_bf(2, 40, 256)),                        # another latent width
+        dict(max_cache_len=41),                             # longer than the cache rows
+        dict(max_cache_len=0),
+        dict(cache_len=_i32(3)),
+        dict(cache_len=_i32(2, 1)),
+        dict(o_lat=_f32(2, 3, 64, 256)),
+        dict(lse=_f32(2, 3, 63)),
+        dict(q_abs=_bf(2, 3, 64 * 512)),                    # not [B, Q, H, R]
+    ]
+    for b in bad:
+        _expect(ValueError, binding.mla_latent_attn, **{**ok, **b})
+    idx_ok = dict(idx=_i32(2, 3, 7), idx_len=_i32(2, 3))
+    _expect(TypeError, binding.mla_latent_attn_indexed, **ok, **idx_ok)
+    for b in (dict(idx=_i32(2, 2, 7)), dict(idx=_i32(3, 3, 7)), dict(idx=_i32(2, 3, 0)), dict(idx=_i32(2, 3)),
+              dict(idx_len=_i32(2, 2)), dict(idx_len=_i32(3, 3)), dict(idx_len=None)):
+        _expect(ValueError, binding.mla_latent_attn_indexed, **ok, **{**idx_ok, **b})
+        _expect(ValueError, binding.mla_latent_attn_up_v, **ok, w_v=_bf(64, 256, 512), **{**idx_ok, **b})
+    _expect(TypeError, binding.mla_latent_attn_up_v, **ok, w_v=_bf(64, 256, 512))
+    for b in (dict(w_v=_bf(32, 256, 512)), dict(w_v=_bf(64, 256, 256)), dict(out=_f32(2, 3, 64, 512)),
+              dict(lse=_f32(2, 3)), dict(cache=_bf(2, 39, 512))):
+        _expect(ValueError, binding.mla_latent_attn_up_v, **{**ok, "w_v": _bf(64, 256, 512), **b})
+    # the debug precondition check
+    _expect(TypeError, binding.mla_check_attn_inputs, cache_len=_i32(2), Q=3, max_cache_len=40, **idx_ok)
+    _expect(ValueError, binding.mla_check_attn_inputs, cache_len=_i32(2), Q=4, max_cache_len=40, **idx_ok)
+    _expect(ValueError, binding.mla_check_attn_inputs, cache_len=_i32(2), Q=3, max_cache_len=40,
+            idx=_i32(2, 3, 7), idx_len=_i32(2, 4))
+
+
+def test_projection_wrappers_check_every_extent(L):
+    _expect(TypeError, binding.mla_absorb_q, q=_bf(4, 64, 256), w_k=_bf(64, 256, 512))
+    _expect(ValueError, binding.mla_absorb_q, q=_bf(4, 64, 128), w_k=_bf(64, 256, 512))
+    _expect(ValueError, binding.mla_absorb_q, q=_bf(4, 64, 256), w_k=_bf(64, 256, 512), q_abs=_bf(4, 64, 256))
+    _expect(ValueError, binding.mla_absorb_q, q=_bf(4, 64, 256), w_k=_bf(64, 256, 512), q_abs=_bf(3, 64, 512))
+    _expect(TypeError, binding.mla_up_v, o_lat=_f32(4, 64, 512), w_v=_bf(64, 256, 512))
+    _expect(ValueError, binding.mla_up_v, o_lat=_f32(4, 32, 512), w_v=_bf(64, 256, 512))
+    _expect(ValueError, binding.mla_up_v, o_lat=_f32(4, 64, 512), w_v=_bf(64, 256, 512), out=_f32(4, 64, 512))
+    # down-projection with cache append
+    ap = dict(h=_bf(2, 3, 4096), w_dkv=_bf(512, 4096), cache=_bf(2, 40, 512), cache_len=_i32(2), max_cache_len=40)
+    _expect(TypeError, binding.mla_latent_append, **ap)
+    for b in (dict(cache=_bf(3, 40, 512)), dict(cache_len=_i32(1)), dict(max_cache_len=41),
+              dict(w_dkv=_bf(512, 2048)), dict(cache=_bf(2, 40, 256))):
+        _expect(ValueError, binding.mla_latent_append, **{**ap, **b})
+
+
+def test_naive_and_indexer_wrappers_check_every_extent(L):
+    ex = dict(cache=_bf(2, 40, 512), cache_len=_i32(2), w_k=_bf(64, 256, 512), w_v=_bf(64, 256, 512),
+              max_cache_len=40)
+    _expect(TypeError, binding.mla_expand_kv, **ex)
+    for b in (dict(cache_len=_i32(3)), dict(w_v=_bf(64, 128, 512)), dict(max_cache_len=41),
+              dict(k_out=_bf(2, 40, 64, 128)), dict(vt_out=_bf(2, 64, 256, 40))):
+        _expect(ValueError, binding.mla_expand_kv, **{**ex, **b})
+    na = dict(q=_bf(2, 3, 64, 256), k=_bf(2, 40, 64, 256), vt=_bf(2, 64, 256, 64), cache_len=_i32(2),
+              max_cache_len=40, scale=0.0625)
+    _expect(TypeError, binding.mla_naive_attn, **na)
+    for b in (dict(k=_bf(2, 39, 64, 256)), dict(vt=_bf(2, 64, 256, 32)), dict(cache_len=_i32(1)),
+              dict(out=_f32(2, 3, 64, 512)), dict(lse=_f32(2, 3, 32))):
+        _expect(ValueError, binding.mla_naive_attn, **{**na, **b})
+    kp = dict(k=_bf(2, 40, 128), g=_bf(2, 40, 128), cache_len=_i32(2), max_cache_len=40, pool=4)
+    _expect(TypeError, binding.mla_kpool_keys, **kp)
+    for b in (dict(g=_bf(2, 40, 64)), dict(cache_len=_i32(3)), dict(max_cache_len=41),
+              dict(pooled=_f32(2, 9, 128)), dict(pool_begin=_i32(1))):
+        _expect(ValueError, binding.mla_kpool_keys, **{**kp, **b})
+    sc = dict(q=_bf(2, 4, 128), pooled=_f32(2, 10, 128), cache_len=_i32(2), max_cache_len=40, pool=4)
+    _expect(TypeError, binding.mla_indexer_scores, **sc)
+    for b in (dict(pooled=_f32(3, 10, 128)), dict(pooled=_f32(2, 10, 64)), dict(cache_len=_i32(1)),
+              dict(scores=_f32(2, 4, 9))):
+        _expect(ValueError, binding.mla_indexer_scores, **{**sc, **b})
+    se = dict(scores=_f32(2, 4, 10), cache_len=_i32(2), max_cache_len=40, pool=4, topk=8)
+    _expect(TypeError, binding.mla_indexer_select, **se)
+    for b in (dict(cache_len=_i32(3)), dict(idx=_i32(2, 3, 11)), dict(idx_len=_i32(2, 3))):
+        _expect(ValueError, binding.mla_indexer_select, **{**se, **b})
