@@ -128,13 +128,15 @@ def expand_values(c: np.ndarray, w_v_h: np.ndarray) -> np.ndarray:
 def softmax_attention(q_h: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     """Textbook attention of one query against T keys/values:
     s_j = scale * q.k_j; a = exp(s - max s) / sum exp(s - max s); out = sum_j a_j v_j.
-    Returns (out [D], lse, s [T], a [T]) with lse = max s + ln sum exp(s - max s)."""
-    s = scale * (k @ q_h)
-    m = s.max()
+    Returns (out [D], lse, s [T], a [T]) with lse = max s + ln sum exp(s - max s).
+    q_h may also be [n, D], n queries against the same keys and values: each is one column of
+    s and a ([T, n]), and out is [n, D], lse [n]."""
+    s = scale * (k @ np.asarray(q_h).T)
+    m = s.max(axis=0)
     e = np.exp(s - m)
-    z = e.sum()
+    z = e.sum(axis=0)
     a = e / z
-    return a @ v, m + np.log(z), s, a
+    return a.T @ v, m + np.log(z), s, a
 
 
 def _select(seq: Optional[Iterable[int]], n: int) -> list:
@@ -207,10 +209,10 @@ def latent_attention(q_abs, cache_bits, cache_len, scale, *, idx=None, idx_len=N
                            None if idx is None else idx[b], None if idx_len is None else idx_len[b], qs)
         for iq, i in enumerate(qs):
             c = bf16_bits_to_f64(cache_bits[b, vis[i]])      # [T, R]
-            for ih, h in enumerate(hs):
-                o, l, _, _ = softmax_attention(np.asarray(q_abs[b, i, h], np.float64), c, c, scale)
-                o_lat[ib, iq, ih] = o
-                lse[ib, iq, ih] = l
+            # every requested head of the query against the same cached latents (K = V = c)
+            o, l, _, _ = softmax_attention(np.asarray(q_abs[b, i, hs], np.float64), c, c, scale)
+            o_lat[ib, iq] = o
+            lse[ib, iq] = l
     return o_lat, lse
 
 

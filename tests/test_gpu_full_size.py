@@ -1,0 +1,115 @@
+"""GPU parity at the full sizes of the four large workloads, over every output the attention call
+produces, and the selection probes at those same shapes and split counts.
+
+* Every (sequence, query, head) row of o_lat and lse from mla_latent_attn / mla_latent_attn_indexed
+  (automatic split count, as the benchmark runs them) against the oracle's latent-space attention
+  (Module 05, section 3: scores against the cached latent, the value sum kept in latent space),
+  with the absorbed queries drawn by the seeded generator.  Bar: max|gpu - ref| <= 1e-2 *
+  max|ref| + 1e-3 over the whole output; lse within 1e-3.
+* The count / bit-sum probe (zero query, position-coded latents) at each workload's exact shape
+  and split count: every query of every sequence, every head, must recover the exact integer
+  counts of its causal set (Module 05, section 4: only positions up to the query's own), or of
+  its listed set for the indexed workload, whose slots past idx_len name positions outside the
+  set (reading them would change the counts).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_cache_absorb_amd import binding, workloads as wl
+from tests import probe_inputs as pi
+from tests.gpu_util import DEV, assert_parity, bf16, i32
+
+pytestmark = pytest.mark.gpu
+
+F = oracle.bf16_bits_to_f64
+
+FULL = ["decode_b32_l8192", "verify_b16_q6_l32768", "decode_b4_l131072_spiked", "indexed_verify_b32_q4_ragged"]
+
+
+def split_count(w):
+    B, Q = w.q.shape[:2]
+    if w.idx is None:
+        return binding.mla_latent_attn_num_splits(B, Q, 64, int(w.cache.shape[1]), 0)
+    return binding.mla_latent_attn_num_splits(B, Q, 64, int(w.idx.shape[2]), 0, indexed=True)
+
+
+def attend(w, q_abs_bits, cache_bits):
+    q, c, cl = bf16(q_abs_bits), bf16(cache_bits), i32(w.cache_len)
+    Lmax = int(cache_bits.shape[1])
+    if w.idx is None:
+        o, lse = binding.mla_latent_attn(q, c, cl, Lmax, w.scale, 0)
+    else:
+        o, lse = binding.mla_latent_attn_indexed(q, c, cl, i32(w.idx), i32(w.idx_len), Lmax, w.scale, 0)
+    torch.cuda.synchronize()
+    res = o.cpu().numpy(), lse.cpu().numpy()
+    del q, c, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_every_row_of_o_lat(name):
+    print(f"{name}: generating inputs", flush=True)
+    w = wl.make_workload(name)
+    qa = wl.latent_query_bits(name)
+    print(f"{name}: attention on the GPU, {split_count(w)} splits", flush=True)
+    o, lse = attend(w, qa, w.cache)
+    print(f"{name}: oracle over every (sequence, query, head)", flush=True)
+    ref, lse_ref = oracle.latent_attention(F(qa), w.cache, w.cache_len, w.scale, idx=w.idx, idx_len=w.idx_len)
+    assert_parity(o, ref, f"{name} o_lat, all {o.shape[0] * o.shape[1] * o.shape[2]} rows")
+    # the worst row measured against its own largest value, for the record
+    row_err = np.abs(o - ref).max(axis=-1) / np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    print(f"{name}: worst row max|err| / max|ref row| = {float(row_err.max()):.3e}", flush=True)
+    lerr = float(np.abs(lse - lse_ref).max())
+    print(f"{name}: max|lse err| = {lerr:.3e}", flush=True)
+    assert lerr <= 1e-3
+
+
+def poisoned_index_rows(w):
+    """The workload's index rows, with every slot past idx_len naming a cached position that is not
+    in the row's set (the first ones), so that reading a slot past the listed ones changes the
+    probe's counts."""
+    idx = w.idx.copy()
+    B, Q, K = idx.shape
+    for b in range(B):
+        for i in range(Q):
+            n = int(w.idx_len[b, i])
+            if n < K:
+                outside = np.setdiff1d(np.arange(K + n, dtype=np.int32), idx[b, i, :n])[: K - n]
+                idx[b, i, n:] = outside
+    return idx
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_selection_probe(name):
+    w = wl.make_workload(name)
+    B, Q = w.q.shape[:2]
+    Lmax = int(w.cache.shape[1])
+    assert Lmax <= 1 << pi.N_POS_BITS
+    splits = split_count(w)
+    print(f"{name}: probe at {B} x {Q} x {Lmax}, {splits} splits", flush=True)
+    cache = pi.coded_cache(B, Lmax, 512, w.cache_len)
+    q_abs = np.zeros((B, Q, 64, 512), np.uint16)
+    if w.idx is not None:
+        w.idx = poisoned_index_rows(w)
+    o, lse = attend(w, q_abs, cache)
+    assert np.isfinite(o).all(), "a row past cache_len was read (NaN poison)"
+    bad = 0
+    for b in range(B):
+        for i in range(Q):
+            if w.idx is None:
+                sel = oracle.dense_visible_positions(int(w.cache_len[b]), Q, i)
+            else:
+                sel = w.idx[b, i, : w.idx_len[b, i]]
+            expect = pi.expected_counts(sel)
+            for h in range(64):
+                got, n = pi.decoded_counts(o[b, i, h], lse[b, i, h])
+                if n != expect[-1] or not np.array_equal(got, expect) or pi.decode_error(o[b, i, h], n) >= 0.05:
+                    bad += 1
+                    if bad <= 5:
+                        print(f"{name}: b{b} i{i} h{h}: n {n} vs {expect[-1]}, counts {got[:6]} vs {expect[:6]}",
+                              flush=True)
+    print(f"{name}: {B * Q * 64 - bad} of {B * Q * 64} rows select exactly their set", flush=True)
+    assert bad == 0
