@@ -57,7 +57,9 @@ enum mla_status {
   MLA_ERR_ARG = -3,       /* another argument out of range (stride, num_splits, K_max, scale) */
   MLA_ERR_WORKSPACE = -4, /* workspace smaller than mla_latent_attn_workspace_size() */
   MLA_ERR_HIP = -5,       /* a HIP runtime call or kernel launch failed */
-  MLA_ERR_DEVICE = -6     /* the current device is not a gfx950 GPU */
+  MLA_ERR_DEVICE = -6,    /* the current device is not a gfx950 GPU */
+  MLA_ERR_SCRATCH = -7    /* the call needs more than the fixed scratch of the no-allocation entry
+                             point (MLA_NOALLOC_SCRATCH_BYTES) */
 };
 
 /* Human-readable text for a status code (static storage; never NULL). */
@@ -339,6 +341,31 @@ enum mla_bad_input {
 };
 int mla_check_attn_inputs(const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t B,
                           int32_t Q, int32_t K_max, int32_t max_cache_len, int32_t* flags, void* stream);
+
+/*
+ * mla_latent_attn_up_v for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments, kernels,
+ * split count and bits as mla_latent_attn_up_v, minus the workspace: the split partials live
+ * in a scratch buffer of MLA_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * per GPU, until the process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); the caller passes every input and output.
+ *   - The first call on a device resolves that device's buffer address (with that device
+ *     current); make it outside graph capture.
+ *   - A call whose workspace would exceed the buffer (mla_latent_attn_up_v_workspace_size() >
+ *     MLA_NOALLOC_SCRATCH_BYTES) is refused with MLA_ERR_SCRATCH before anything is enqueued.
+ *     The four full-size workloads of this library need at most about 63 MB.
+ *   - Every call on one GPU shares that GPU's buffer and leaves the last call's partials in it
+ *     (nothing in it needs clearing: each call writes every partial it reads).  Calls that
+ *     overlap on one GPU, on different streams or from different threads, RACE and give wrong
+ *     results: serialise them (one stream, or events between streams).
+ * Errors: those of mla_latent_attn_up_v except MLA_ERR_WORKSPACE, plus MLA_ERR_SCRATCH.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int mla_latent_attn_up_v_noalloc(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
+                                 const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len,
+                                 int32_t K_max, int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len,
+                                 float scale, int32_t num_splits, const uint16_t* w_v, int32_t D, float* out,
+                                 float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,11 +22,14 @@ MLA_ERR_ARG = -3
 MLA_ERR_WORKSPACE = -4
 MLA_ERR_HIP = -5
 MLA_ERR_DEVICE = -6
+MLA_ERR_SCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("mla_status_string", "mla_absorb_q", "mla_latent_attn_num_splits", "mla_latent_attn_workspace_size",
            "mla_latent_attn", "mla_latent_attn_indexed", "mla_up_v", "mla_kpool_keys", "mla_indexer_scores",
            "mla_indexer_select", "mla_latent_append", "mla_expand_kv", "mla_naive_attn",
-           "mla_latent_attn_up_v_workspace_size", "mla_latent_attn_up_v", "mla_check_attn_inputs")
+           "mla_latent_attn_up_v_workspace_size", "mla_latent_attn_up_v", "mla_check_attn_inputs",
+           "mla_latent_attn_up_v_noalloc")
 
 
 class MlaError(RuntimeError):
@@ -64,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.mla_latent_attn_up_v.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32,
                                            vp, vp, vp, sz, vp]
         L.mla_latent_attn_up_v.restype = ctypes.c_int
+        L.mla_latent_attn_up_v_noalloc.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                                   vp, i32, vp, vp, vp]
+        L.mla_latent_attn_up_v_noalloc.restype = ctypes.c_int
         L.mla_check_attn_inputs.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
         L.mla_check_attn_inputs.restype = ctypes.c_int
         L.mla_up_v.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
@@ -373,6 +379,33 @@ def mla_latent_attn_up_v(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: to
                                       int(num_splits), _ptr(w_v), D, _ptr(out), _ptr(lse), _ptr(workspace),
                                       _nbytes(workspace), _stream(stream)),
            "mla_latent_attn_up_v")
+    return out, lse
+
+
+def mla_latent_attn_up_v_noalloc(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor,
+                                 max_cache_len: int, scale: float, w_v: torch.Tensor, out: torch.Tensor,
+                                 lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                                 idx_len: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None):
+    """mla_latent_attn_up_v with the split partials in the library's fixed device scratch: neither
+    the library nor this wrapper allocates (the caller passes out, and lse or None).  Calls that
+    overlap on one GPU race on that scratch.  Returns (out, lse)."""
+    B, Q, H, R, K_max = _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx, idx_len)
+    _need(w_v, torch.bfloat16, "w_v")
+    if w_v.dim() != 3 or w_v.shape[0] != H or w_v.shape[2] != R:
+        raise ValueError(f"w_v must be [H={H}, D, R={R}], got {tuple(w_v.shape)}")
+    D = w_v.shape[1]
+    if out is None:
+        raise ValueError("out must be given: this call allocates nothing")
+    _need(out, torch.float32, "out")
+    _shape(out, (B, Q, H, D), "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+        _shape(lse, (B, Q, H), "lse")
+    _gpu(q_abs, cache, cache_len, w_v, idx, idx_len, out, lse)
+    _check(lib().mla_latent_attn_up_v_noalloc(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len),
+                                              _ptr(idx), _ptr(idx_len), K_max, B, Q, H, R, int(max_cache_len),
+                                              float(scale), int(num_splits), _ptr(w_v), D, _ptr(out), _ptr(lse),
+                                              _stream(stream)), "mla_latent_attn_up_v_noalloc")
     return out, lse
 
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "mla_absorb.h"
 #include "mla_internal.h"
@@ -98,6 +99,31 @@ size_t fused_workspace_bytes_for(int32_t B, int32_t Q, int32_t H, int32_t s) {
   return s > 1 ? workspace_bytes_for(B, Q, H, s) : (size_t)B * Q * H * 512 * sizeof(float);
 }
 
+// ---- fixed scratch of the no-allocation entry point (mla_latent_attn_up_v_noalloc)
+// The array's name is a host-side stand-in in host code, not a device address: host code uses only
+// the per-device address hipGetSymbolAddress returns (each GPU holds its own copy of the array).
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// the current device's copy of `scratch`, resolved once per device with that device current
+int scratch_for_current_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MLA_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return MLA_OK;
+}
+
 int device_cus_or_default() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
@@ -112,8 +138,9 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
                 const int32_t* idx, const int32_t* idx_len, int32_t K_max, bool indexed, int32_t B, int32_t Q,
                 int32_t H, int32_t R, int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat,
                 float* lse, void* workspace, size_t workspace_bytes, void* stream, const uint16_t* w_v = nullptr,
-                float* out = nullptr) {
-  // w_v != null: the up-projection follows, fused with the split merge, and writes `out`
+                float* out = nullptr, bool fixed_scratch = false) {
+  // w_v != null: the up-projection follows, fused with the split merge, and writes `out`;
+  // fixed_scratch: the partials go to the library's own scratch (workspace arguments ignored)
   const bool fused = w_v != nullptr;
   if (!q_abs || !cache || !cache_len || (fused ? !out : !o_lat)) return MLA_ERR_NULL;
   if (indexed && (!idx || !idx_len)) return MLA_ERR_NULL;
@@ -130,6 +157,12 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   const int s = resolve_splits(B, Q, H, max_positions, num_splits, cus, indexed);
   if (s < 1) return s;
   const size_t need = fused ? fused_workspace_bytes_for(B, Q, H, s) : workspace_bytes_for(B, Q, H, s);
+  if (fixed_scratch) {
+    if (need > kScratchBytes) return MLA_ERR_SCRATCH;
+    const int sst = scratch_for_current_device(&workspace);
+    if (sst != MLA_OK) return sst;
+    workspace_bytes = kScratchBytes;
+  }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
   const int64_t total = (int64_t)B * mla::query_units(indexed, Q) * (H / 64) * s;
   if (total > 0x7fffffff || (int64_t)B * Q * H > 0x7fffffff) return MLA_ERR_SHAPE;
@@ -189,6 +222,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_WORKSPACE: return "workspace too small";
     case MLA_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case MLA_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    case MLA_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point holds (64 MiB)";
     default: return "unknown status";
   }
 }
@@ -251,6 +285,18 @@ int mla_latent_attn_up_v(const uint16_t* q_abs, const uint16_t* cache, int64_t c
   if (!supported(H, D, R)) return MLA_ERR_SHAPE;
   return attn_common(q_abs, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, idx != nullptr, B, Q, H, R,
                      max_cache_len, scale, num_splits, nullptr, lse, workspace, workspace_bytes, stream, w_v, out);
+}
+
+int mla_latent_attn_up_v_noalloc(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
+                                 const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len,
+                                 int32_t K_max, int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len,
+                                 float scale, int32_t num_splits, const uint16_t* w_v, int32_t D, float* out,
+                                 float* lse, void* stream) {
+  if (!w_v) return MLA_ERR_NULL;
+  if ((idx == nullptr) != (idx_len == nullptr)) return MLA_ERR_NULL;
+  if (!supported(H, D, R)) return MLA_ERR_SHAPE;
+  return attn_common(q_abs, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, idx != nullptr, B, Q, H, R,
+                     max_cache_len, scale, num_splits, nullptr, lse, nullptr, 0, stream, w_v, out, true);
 }
 
 int mla_check_attn_inputs(const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t B,

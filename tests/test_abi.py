@@ -37,8 +37,8 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings(L):
-    for s in (0, -1, -2, -3, -4, -5, -6):
-        assert binding.status_string(s)
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert binding.status_string(s) and binding.status_string(s) != "unknown status"
     assert "workspace" in binding.status_string(binding.MLA_ERR_WORKSPACE)
 
 
@@ -172,6 +172,42 @@ def test_fused_up_projection_host_validation(L):
         binding.mla_latent_attn_workspace_size(32, 1, 64, 512, 8192, 0) == s * 32 * 64 * 514 * 4
     assert binding.mla_latent_attn_up_v_workspace_size(2, 3, 64, 512, 256, 1) == 2 * 3 * 64 * 512 * 4
     assert binding.mla_latent_attn_up_v_workspace_size(2, 3, 64, 256, 256, 1) == 0
+
+
+def test_noalloc_host_validation(L):
+    fake = ctypes.c_void_p(0x1000)
+    f = L.mla_latent_attn_up_v_noalloc
+    # args: q_abs cache stride cache_len idx idx_len K_max B Q H R max_len scale splits w_v D out lse stream
+    ok = [fake, fake, 51200, fake, None, None, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake, 256, fake, None, None]
+    names = ["q", "c", "st", "cl", "idx", "idx_len", "K", "B", "Q", "H", "R", "L", "scale", "s", "w_v", "D", "out",
+             "lse", "stream"]
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    # every host-side error comes before the device is touched (no GPU here)
+    assert call(w_v=None) == binding.MLA_ERR_NULL
+    assert call(out=None) == binding.MLA_ERR_NULL
+    assert call(q=None) == binding.MLA_ERR_NULL
+    assert call(idx=fake) == binding.MLA_ERR_NULL
+    assert call(D=128) == binding.MLA_ERR_SHAPE
+    assert call(R=256) == binding.MLA_ERR_SHAPE
+    assert call(scale=float("inf")) == binding.MLA_ERR_ARG
+    assert call(st=512 * 99) == binding.MLA_ERR_ARG
+    assert call(s=-1) == binding.MLA_ERR_ARG
+    # the four full-size workloads fit the fixed scratch
+    for B, Q, Lmax, ind in ((32, 1, 8192, False), (16, 6, 32768, False), (4, 1, 131072, False),
+                            (32, 4, 2052, True)):
+        assert binding.mla_latent_attn_up_v_workspace_size(B, Q, 64, 512, Lmax, 0, ind) <= \
+            binding.NOALLOC_SCRATCH_BYTES
+    # the binding allocates nothing for it: out is required
+    import torch
+    with pytest.raises(ValueError):
+        binding.mla_latent_attn_up_v_noalloc(_bf(1, 1, 64, 512), _bf(1, 40, 512), _i32(1), 40, 0.0625,
+                                             _bf(64, 256, 512), None)
 
 
 def test_input_check_host_validation(L):
