@@ -29,7 +29,10 @@ def unwaited_barriers(asm: str):
     """(kernel, line) of every s_barrier some path reaches with an LDS write not yet waited for."""
     lines = asm.split("\n")
     found = []
-    starts = [i for i, l in enumerate(lines) if re.match(r"^_Z\S+:\s*(;.*)?$", l)]
+    # functions only (a file may also define device variables, whose labels look alike)
+    funcs = set(re.findall(r"\.type\s+(\S+),\s*@function", asm))
+    starts = [i for i, l in enumerate(lines)
+              if re.match(r"^_Z\S+:\s*(;.*)?$", l) and l.split(":")[0] in funcs]
     for st in starts:
         name = lines[st].split(":")[0]
         en = next(i for i in range(st, len(lines)) if lines[i].strip().startswith(".Lfunc_end"))
@@ -62,10 +65,12 @@ def unwaited_barriers(asm: str):
 
 def test_checker_flags_a_missing_wait():
     # a loop whose back edge carries an LDS write to the barrier, and the same with the wait
-    bad = "\n".join(["_Zk:", "  s_nop 0", ".LBB0_1:", "  s_barrier", "  ds_write_b32 v0, v1",
+    bad = "\n".join(["\t.type _Zk,@function", "_Zk:", "  s_nop 0", ".LBB0_1:", "  s_barrier", "  ds_write_b32 v0, v1",
                      "  s_cbranch_scc1 .LBB0_1", "  s_endpgm", ".Lfunc_end0:"])
     good = bad.replace("  s_cbranch_scc1", "  s_waitcnt lgkmcnt(0)\n  s_cbranch_scc1")
     assert unwaited_barriers(bad) == [("_Zk", 3)]
+    # a device variable's label is not a kernel
+    assert unwaited_barriers(bad + "\n_ZN12_GLOBAL__N_17scratchE:\n\t.zero 256") == [("_Zk", 3)]
     assert unwaited_barriers(good) == []
 
 
