@@ -101,7 +101,8 @@ int32_t mla_latent_attn_num_splits(int32_t B, int32_t Q, int32_t H, int32_t max_
 
 /*
  * Workspace bytes a latent-attention call needs (0 when it uses one split): the split
- * partials, [splits][B*Q][H][R] fp32 plus two [splits][B*Q][H] fp32 arrays.  Same
+ * partials, [splits][B*Q][H][R] fp16 (each split's weighted sum of latents divided by its own
+ * softmax sum) plus [splits][B*Q][H][2] fp32 (running maximum, sum).  Same
  * arguments as mla_latent_attn_num_splits plus R.  Returns 0 on bad sizes as well; the
  * attention calls reject a workspace that is too small.
  */
@@ -128,7 +129,9 @@ size_t mla_latent_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R
  * visible set is empty (cache_len[b] < Q) gets o_lat = NaN and lse = -inf.
  * Results are deterministic for a fixed num_splits (no atomics in any reduction), and for the
  * same split count equal bit for bit those of mla_latent_attn_indexed given every causal
- * position.
+ * position.  With several splits each split's normalised partial is kept in fp16 between the
+ * two kernels (2^-11 relative; a convex combination of cached latents, so the cache's values
+ * must stay below 65,504 in magnitude); maxima, sums and lse stay fp32.
  */
 int mla_latent_attn(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
                     const int32_t* cache_len, int32_t B, int32_t Q, int32_t H, int32_t R,

@@ -148,7 +148,8 @@ __device__ __forceinline__ TrOffsets transpose_offsets(int lane, int lq) {
 
 // A value wave's result for one head column hv of row bq: lane holds latents 128lq + 32mb + 8ii
 // + 4hf + j.  With one split, o_lat = o / l and lse = (m + log2 l) ln 2 are final; otherwise the
-// unnormalised partial and its (m, l) go to the split's slot for the merge.
+// normalised partial o / l (fp16; zero for a split that saw nothing) and its (m, l) go to the
+// split's slot for the merge.
 __device__ __forceinline__ void store_value_rows(const AttnArgs& a, int split, int bq, int hv, int lq, int hf,
                                                  float m_fin, float l_fin, const f32x16 (&o)[4]) {
   if (a.num_splits == 1) {
@@ -165,13 +166,15 @@ __device__ __forceinline__ void store_value_rows(const AttnArgs& a, int split, i
       a.lse[(size_t)bq * a.H + hv] = (m_fin + __builtin_amdgcn_logf(l_fin)) * 0.69314718055994531f;
   } else {
     const size_t prow_idx = ((size_t)split * a.B * a.Q + bq) * a.H + hv;
-    float* orow = a.part_o + prow_idx * kLatent + 128 * lq + 4 * hf;
+    uint16_t* orow = a.part_o + prow_idx * kLatent + 128 * lq + 4 * hf;
+    const float inv_l = l_fin > 0.f ? 1.0f / l_fin : 0.f;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
-        *(f32x4*)(orow + 32 * mb + 8 * ii) =
-            (f32x4){o[mb][4 * ii], o[mb][4 * ii + 1], o[mb][4 * ii + 2], o[mb][4 * ii + 3]};
+        *(f16x4*)(orow + 32 * mb + 8 * ii) =
+            __builtin_convertvector((f32x4){o[mb][4 * ii] * inv_l, o[mb][4 * ii + 1] * inv_l,
+                                            o[mb][4 * ii + 2] * inv_l, o[mb][4 * ii + 3] * inv_l}, f16x4);
     if (hf == 0 && lq == 0) {
       a.part_ml[2 * prow_idx] = m_fin;
       a.part_ml[2 * prow_idx + 1] = l_fin;
@@ -698,7 +701,7 @@ __global__ __launch_bounds__(1024) void combine_wide_kernel(AttnArgs a) {
   const size_t rows = (size_t)a.B * a.Q * a.H;
   const int S = a.num_splits;
   const int ngroups = (S + 7) / 8;
-  const float* po = a.part_o + row * kLatent + 4 * t;
+  const uint16_t* po = a.part_o + row * kLatent + 4 * t;
   const float* pml = a.part_ml + 2 * row;
   float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};

@@ -38,8 +38,8 @@ int check_device(int* cus) {
 // even Q (mla::query_units); the positions of each unit are cut into `s` contiguous splits of
 // whole tiles, one workgroup per CU.  The estimate charges the rounds of resident workgroups
 // times the tiles of one split, plus the partial results each extra split writes and the
-// merge reads back (a 128 KiB partial per query is worth four 32 KiB tiles each way) and a
-// fixed cost for the merge launch.
+// merge reads back (priced as four 32 KiB tiles each way per query; measured sweeps of the
+// split count agree with this weight) and a fixed cost for the merge launch.
 int32_t choose_splits(int64_t units, int32_t max_positions, int cus) {
   const int64_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
   const int64_t slots = cus > 0 ? cus : 256;
@@ -88,10 +88,11 @@ int resolve_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions, int32
   return (max_positions + len - 1) / len;
 }
 
+// split partials: fp16 normalised latents, then fp32 (m, l) per row
 size_t workspace_bytes_for(int32_t B, int32_t Q, int32_t H, int32_t s) {
   if (s <= 1) return 0;
   const size_t rows = (size_t)s * B * Q * H;
-  return rows * 512 * sizeof(float) + rows * 2 * sizeof(float);
+  return rows * 512 * sizeof(uint16_t) + rows * 2 * sizeof(float);
 }
 
 // with the up-projection fused: the partials, or for one split the accumulated latents
@@ -187,8 +188,8 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   a.o_lat = fused ? (s > 1 ? nullptr : (float*)workspace) : o_lat;
   a.lse = lse;
   const size_t rows = (size_t)s * B * Q * H;
-  a.part_o = s > 1 ? (float*)workspace : nullptr;
-  a.part_ml = s > 1 ? (float*)workspace + rows * 512 : nullptr;
+  a.part_o = s > 1 ? (uint16_t*)workspace : nullptr;
+  a.part_ml = s > 1 ? (float*)((uint8_t*)workspace + rows * 512 * sizeof(uint16_t)) : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   if (mla::launch_latent_attn(a, indexed, st) != hipSuccess) return MLA_ERR_HIP;

@@ -19,6 +19,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kLatent = 512;        // R
@@ -160,9 +161,11 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Log-sum-exp merge of split-K attention partials.  A split's partial is (m, l, o): m a running
-// maximum in log2 units, l = sum 2^(score - m) and o the unnormalised weighted sum of its latents;
-// the merged row is sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  The splits
+// Log-sum-exp merge of split-K attention partials.  A split's partial is (m, l, u): m a running
+// maximum in log2 units, l = sum 2^(score - m) and u = o / l its normalised weighted sum of latents
+// (o the unnormalised sum), stored in fp16: u is a convex combination of cached latents, so its
+// magnitude is at most theirs, and fp16 keeps it to 2^-11 relative; 0 when the split saw nothing.
+// The merged row is sum_s 2^(m_s - M) l_s u_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  The splits
 // are taken in groups of eight, every load of a group issued together.  A group is first reduced
 // on its own, relative to its own maximum Mg (splits that saw no position, l = 0, weigh nothing),
 // and the group results are then folded in order into a running (M, L, o), rescaling what was
@@ -178,11 +181,11 @@ struct MergePartial {
   f32x4 acc;
 };
 
-// part_o: the row's four latents (of this thread) in split 0; part_ml: the row's (m, l) in
-// split 0; split s lies o_step (ml_step) floats further on
+// part_o: the row's four latents (of this thread, fp16) in split 0; part_ml: the row's (m, l) in
+// split 0; split s lies o_step (ml_step) elements further on
 // slots past the last split are not loaded: they hold a neutral partial (no maximum, zero sum,
 // zero latents), which merge_group weighs by zero like any split that saw no position
-__device__ __forceinline__ void merge_load(MergeGroup& g, const float* part_o, const float* part_ml, size_t o_step,
+__device__ __forceinline__ void merge_load(MergeGroup& g, const uint16_t* part_o, const float* part_ml, size_t o_step,
                                            size_t ml_step, int S, int s0) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -190,7 +193,7 @@ __device__ __forceinline__ void merge_load(MergeGroup& g, const float* part_o, c
     if (s < S) {
       g.mm[k] = part_ml[s * ml_step];
       g.ll[k] = part_ml[s * ml_step + 1];
-      g.v[k] = *(const f32x4*)(part_o + s * o_step);
+      g.v[k] = __builtin_convertvector(*(const f16x4*)(part_o + s * o_step), f32x4);
     } else {
       g.mm[k] = -INFINITY;
       g.ll[k] = 0.f;
@@ -211,9 +214,10 @@ __device__ __forceinline__ bool merge_group(const MergeGroup& g, int S, int s0, 
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const float w = (s0 + k < S && g.ll[k] > 0.f) ? __builtin_amdgcn_exp2f(g.mm[k] - Mg) : 0.f;
+    const float wl = w * g.ll[k];  // the split's weight: its sum rescaled to the group's maximum
     L = __builtin_fmaf(w, g.ll[k], L);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, g.v[k][e], acc[e]);
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wl, g.v[k][e], acc[e]);
   }
   r.M = Mg;
   r.L = L;
@@ -234,7 +238,7 @@ __device__ __forceinline__ void merge_fold(float& M, float& L, f32x4& acc, const
 }
 
 // the whole merge for the four latents a thread owns; *lse2 = M + log2(L) (log2 units)
-__device__ __forceinline__ f32x4 merge_splits(const float* part_o, const float* part_ml, size_t o_step,
+__device__ __forceinline__ f32x4 merge_splits(const uint16_t* part_o, const float* part_ml, size_t o_step,
                                               size_t ml_step, int S, float* lse2) {
   float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};

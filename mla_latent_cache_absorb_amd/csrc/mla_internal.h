@@ -24,7 +24,7 @@ struct AttnArgs {
   int32_t total_wg;
   float* o_lat;                   // [B][Q][H][R] fp32 (written directly when num_splits == 1)
   float* lse;                     // [B][Q][H] or null
-  float* part_o;                  // [S][B*Q][H][R] fp32 unnormalised partial sums
+  uint16_t* part_o;               // [S][B*Q][H][R] fp16 bits: the split's normalised partial o / l
   float* part_ml;                 // [S][B*Q][H][2] fp32 (running max in log2 units, sum)
 };
 
@@ -123,7 +123,7 @@ hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int 
 
 // split-K partials merged straight into the up-projection
 struct MergeUpArgs {
-  const float* part_o;     // [S][rows][H][R] fp32 unnormalised partial sums
+  const uint16_t* part_o;  // [S][rows][H][R] fp16 bits: normalised partials o / l
   const float* part_ml;    // [S][rows][H][2] fp32 (running max in log2 units, sum)
   int32_t num_splits;
   int32_t rows, H;         // rows = B * Q

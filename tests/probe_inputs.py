@@ -49,6 +49,53 @@ def coded_cache(B: int, L_max: int, R: int, cache_len) -> np.ndarray:
     return out
 
 
+# ------------------------------------------------------------------ read through the log-sum-exp
+# The count probe above reads the counts out of o_lat, which needs the accumulated latents exact
+# to the last unit; a library that keeps its split partials in fp16 rounds them.  This form reads
+# the same 35 integers out of lse instead, which the attention computes from the fp32 running
+# maxima and sums only.  Head 0 has a zero query: every score is 0, every weight exactly 1, so
+# lse = ln(n).  Head 1 + c (c < 34) scores K * (c_j[c] - c_j[34]): 0 for a position whose code
+# bit c is set and -K otherwise, so with K = 512 (exact in bf16; scale * K = 32) the clear
+# positions weigh exp(-32) and lse = ln(number of positions with bit c set) up to 1e-9 relative.
+# Heads 35..63 repeat head 0.  Every product and sum that reaches lse is then exact (scores 0 or
+# -K, weights 1, sums of ones below 2^24); only the final logarithm rounds, by a few parts in 1e7,
+# so the counts are recovered exactly while they stay below about 2^19.
+PROBE_K = 512.0
+
+
+def lse_probe_query(R: int = 512, heads: int = 64) -> np.ndarray:
+    """[heads, R] bf16 bits of the absorbed query for the log-sum-exp form of the probe."""
+    assert heads >= ONE_CHANNEL + 1 and R >= ONE_CHANNEL + 1
+    q = np.zeros((heads, R), np.float32)
+    for c in range(ONE_CHANNEL):
+        q[1 + c, c] = PROBE_K
+        q[1 + c, ONE_CHANNEL] = -PROBE_K
+    b = (q.view(np.uint32) >> 16).astype(np.uint16)  # the values are exact in bf16
+    assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), q)
+    return b
+
+
+def expected_lse_counts(positions: np.ndarray, heads: int = 64) -> np.ndarray:
+    """The integers the log-sum-exp probe must recover per head for a selected set."""
+    c = expected_counts(positions)  # 34 bit counts, then n
+    n = c[-1]
+    out = np.full(heads, n, np.int64)
+    out[1:1 + ONE_CHANNEL] = c[:ONE_CHANNEL]
+    return out
+
+
+LN2_F32 = float(np.float32(0.69314718055994531))  # the fp32 constant a library multiplies by
+
+
+def decoded_lse_counts(lse_row: np.ndarray) -> tuple[np.ndarray, float]:
+    """Per head: round(exp(lse)), and the largest distance of exp(lse) from an integer.  lse is
+    divided by the fp32 value of ln 2 so that a base-2 logarithm times that constant inverts
+    exactly but for the logarithm's own rounding."""
+    v = np.exp2(np.asarray(lse_row, np.float64) / LN2_F32)
+    n = np.rint(v)
+    return n.astype(np.int64), float(np.max(np.abs(v - n)))
+
+
 def expected_counts(positions: np.ndarray) -> np.ndarray:
     """The 35 integers the probe must recover for a selected set."""
     p = np.asarray(positions, dtype=np.int64)

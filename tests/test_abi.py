@@ -77,7 +77,8 @@ def test_split_sizing(L):
         s = binding.mla_latent_attn_num_splits(B, Q, 64, Lmax, 0)
         assert 1 <= s <= max(1, (Lmax + 31) // 32)
         ws = binding.mla_latent_attn_workspace_size(B, Q, 64, 512, Lmax, 0)
-        assert ws == (0 if s == 1 else s * B * Q * 64 * (512 + 2) * 4)
+        # fp16 normalised partials, then fp32 (m, l) per row
+        assert ws == (0 if s == 1 else s * B * Q * 64 * (512 * 2 + 2 * 4))
     # splits hold whole 32-position tiles and none is left empty
     assert binding.mla_latent_attn_num_splits(1, 1, 64, 256, 8) == 8
     assert binding.mla_latent_attn_num_splits(1, 1, 64, 256, 5) == 4   # 8 tiles as 2+2+2+2
@@ -110,7 +111,7 @@ def test_split_choice_counts_query_pairs(L):
     assert binding.mla_latent_attn_num_splits(16, 2, 64, 32768, 0) == 16
     assert binding.mla_latent_attn_num_splits(16, 8, 64, 32768, 0) == 4
     assert binding.mla_latent_attn_num_splits(32, 4, 64, 2052, 0, indexed=True) == 2
-    assert binding.mla_latent_attn_workspace_size(32, 4, 64, 512, 2052, 0, indexed=True) == 2 * 128 * 64 * 514 * 4
+    assert binding.mla_latent_attn_workspace_size(32, 4, 64, 512, 2052, 0, indexed=True) == 2 * 128 * 64 * 1032
 
 
 def test_indexer_host_validation(L):
@@ -169,7 +170,7 @@ def test_fused_up_projection_host_validation(L):
     # workspace: the split partials, or the accumulated latents when there is one split
     s = binding.mla_latent_attn_num_splits(32, 1, 64, 8192, 0)
     assert binding.mla_latent_attn_up_v_workspace_size(32, 1, 64, 512, 8192, 0) == \
-        binding.mla_latent_attn_workspace_size(32, 1, 64, 512, 8192, 0) == s * 32 * 64 * 514 * 4
+        binding.mla_latent_attn_workspace_size(32, 1, 64, 512, 8192, 0) == s * 32 * 64 * 1032
     assert binding.mla_latent_attn_up_v_workspace_size(2, 3, 64, 512, 256, 1) == 2 * 3 * 64 * 512 * 4
     assert binding.mla_latent_attn_up_v_workspace_size(2, 3, 64, 256, 256, 1) == 0
 

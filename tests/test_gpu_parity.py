@@ -265,10 +265,23 @@ def test_full_size_sampled(name, bs, qs, hs):
 
 
 # ------------------------------------------------------------------ selection probes
+# Position-coded latents and a query per head that counts the visible positions with one code bit
+# set; the counts are read from lse (tests/probe_inputs.py), which the library computes in fp32
+# from the running maxima and sums only.
+def probe_query(B, Q):
+    return bf16(np.ascontiguousarray(np.broadcast_to(pi.lse_probe_query(), (B, Q, 64, 512))))
+
+
+def assert_probe_counts(lse_row, positions, what):
+    got, dist = pi.decoded_lse_counts(lse_row)
+    want = pi.expected_lse_counts(positions)
+    assert dist < 0.3, f"{what}: lse {dist:.3f} from an integer count"
+    np.testing.assert_array_equal(got, want, err_msg=what)
+
+
 def _probe_dense(B, Q, L_max, lens, splits):
     cache = pi.coded_cache(B, L_max, 512, np.array(lens))
-    q_abs = torch.zeros((B, Q, 64, 512), dtype=torch.bfloat16, device=DEV)
-    o_lat, lse = binding.mla_latent_attn(q_abs, bf16(cache), i32(lens), L_max, 1.0 / 16, splits)
+    o_lat, lse = binding.mla_latent_attn(probe_query(B, Q), bf16(cache), i32(lens), L_max, 1.0 / 16, splits)
     torch.cuda.synchronize()
     return o_lat.cpu().numpy(), lse.cpu().numpy()
 
@@ -281,12 +294,7 @@ def test_probe_dense_selects_exact_causal_sets(splits):
     assert np.isfinite(o_lat).all(), "a row past cache_len was read (NaN poison)"
     for b in range(B):
         for i in range(Q):
-            expect = pi.expected_counts(oracle.dense_visible_positions(lens[b], Q, i))
-            for h in (0, 37, 63):
-                got, n = pi.decoded_counts(o_lat[b, i, h], lse[b, i, h])
-                assert pi.decode_error(o_lat[b, i, h], n) < 0.05
-                assert n == expect[-1], (b, i, h, n, expect[-1])
-                np.testing.assert_array_equal(got, expect, err_msg=f"b{b} i{i} h{h}")
+            assert_probe_counts(lse[b, i], oracle.dense_visible_positions(lens[b], Q, i), f"b{b} i{i}")
 
 
 def test_probe_indexed_reads_only_listed_slots():
@@ -308,17 +316,15 @@ def test_probe_indexed_reads_only_listed_slots():
             idx[b, i, sel.size:sel.size + rest.size] = rest
             sets[(b, i)] = sel
     cache = pi.coded_cache(B, L_max, 512, lens)
-    q_abs = torch.zeros((B, Q, 64, 512), dtype=torch.bfloat16, device=DEV)
+    q_abs = probe_query(B, Q)
     for splits in (0, 1, 4):
         o_lat, lse = binding.mla_latent_attn_indexed(q_abs, bf16(cache), i32(lens), i32(idx), i32(idx_len), L_max,
                                                      1.0 / 16, splits)
         torch.cuda.synchronize()
         o_lat, lse = o_lat.cpu().numpy(), lse.cpu().numpy()
+        assert np.isfinite(o_lat).all()
         for (b, i), sel in sets.items():
-            expect = pi.expected_counts(sel)
-            got, n = pi.decoded_counts(o_lat[b, i, 5], lse[b, i, 5])
-            assert n == sel.size
-            np.testing.assert_array_equal(got, expect, err_msg=f"b{b} i{i} s{splits}")
+            assert_probe_counts(lse[b, i], sel, f"b{b} i{i} s{splits}")
 
 
 def test_spike_at_first_masked_position_does_not_leak():

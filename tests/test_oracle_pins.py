@@ -349,6 +349,36 @@ def test_probe_recovers_selected_sets_exactly():
             np.testing.assert_array_equal(got, expect)
 
 
+def _lse_probe_ok(lse, cache_len, Q, batches):
+    """Whether the log-sum-exp form of the probe recovers every query's exact causal counts."""
+    ok = True
+    for b in batches:
+        for i in range(Q):
+            expect = pi.expected_lse_counts(np.arange(int(cache_len[b]) - Q + i + 1))
+            got, dist = pi.decoded_lse_counts(lse[b, i])
+            ok &= bool(np.array_equal(got, expect)) and dist < 0.01
+    return ok
+
+
+def test_lse_probe_recovers_selected_sets_exactly():
+    # the probe's log-sum-exp form (a query per head that scores 0 on positions with one code bit
+    # set and -K elsewhere) on the oracle: every head's lse gives its count exactly
+    cache, cache_len, _ = _probe_case()
+    q_abs = np.broadcast_to(oracle.bf16_bits_to_f64(pi.lse_probe_query()), (2, 6, 64, 512))
+    _, lse = oracle.latent_attention(q_abs, cache, cache_len, 1.0 / 16)
+    assert _lse_probe_ok(lse, cache_len, 6, range(2))
+    # and for an indexed set
+    sel = np.array([3, 17, 64, 65, 200, 250], np.int64)
+    idx = np.full((2, 6, 8), -1, np.int32)
+    idx_len = np.ones((2, 6), np.int32)
+    idx[:, :, 0] = 0
+    idx[0, 5, :6] = sel
+    idx_len[0, 5] = 6
+    _, lse = oracle.latent_attention(q_abs, cache, cache_len, 1.0 / 16, idx=idx, idx_len=idx_len)
+    got, _ = pi.decoded_lse_counts(lse[0, 5])
+    np.testing.assert_array_equal(got, pi.expected_lse_counts(sel))
+
+
 # ---------------------------------------------------------------- planted mistakes
 MISTAKES = {
     "causal_bound_plus_one": ("dense_visible_positions",
@@ -385,4 +415,8 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
             got, n = pi.decoded_counts(olat[0, i, 0], lse[0, i, 0])
             probe_ok &= bool(np.array_equal(got, expect))
         assert not probe_ok, "selection probe missed a shifted causal bound"
+        # and so must its log-sum-exp form
+        q_lse = np.broadcast_to(oracle.bf16_bits_to_f64(pi.lse_probe_query()), (1, 3, 64, 512))
+        _, lse = mla_oracle.latent_attention(q_lse, cache, cache_len, 1.0 / 16)
+        assert not _lse_probe_ok(lse, cache_len, 3, [0]), "log-sum-exp probe missed a shifted causal bound"
     assert caught, f"pins missed planted mistake {name}"
