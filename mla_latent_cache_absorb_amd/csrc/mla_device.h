@@ -183,22 +183,19 @@ struct MergePartial {
 
 // part_o: the row's four latents (of this thread, fp16) in split 0; part_ml: the row's (m, l) in
 // split 0; split s lies o_step (ml_step) elements further on
-// slots past the last split are not loaded: they hold a neutral partial (no maximum, zero sum,
-// zero latents), which merge_group weighs by zero like any split that saw no position
+// Every slot is loaded, unconditionally, so that the group's loads all issue before the first
+// one is waited for (one memory round trip; a conditional load per slot makes the compiler wait
+// before each branch).  A slot past the last split reloads the last split (in bounds, a cache
+// hit); merge_group weighs such slots by zero, as it does a split that saw no position.
 __device__ __forceinline__ void merge_load(MergeGroup& g, const uint16_t* part_o, const float* part_ml, size_t o_step,
                                            size_t ml_step, int S, int s0) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int s = s0 + k;
-    if (s < S) {
-      g.mm[k] = part_ml[s * ml_step];
-      g.ll[k] = part_ml[s * ml_step + 1];
-      g.v[k] = __builtin_convertvector(*(const f16x4*)(part_o + s * o_step), f32x4);
-    } else {
-      g.mm[k] = -INFINITY;
-      g.ll[k] = 0.f;
-      g.v[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
+    const size_t s = (size_t)min(s0 + k, S - 1);
+    const float2 ml = *(const float2*)(part_ml + s * ml_step);
+    g.mm[k] = ml.x;
+    g.ll[k] = ml.y;
+    g.v[k] = __builtin_convertvector(*(const f16x4*)(part_o + s * o_step), f32x4);
   }
 }
 

@@ -62,18 +62,25 @@ __global__ __launch_bounds__(kThreads) void up_v_kernel(const float* __restrict_
   for (int pass = blockIdx.y; pass < npass; pass += gridDim.y) {
     const int row0 = pass * kUpRows;
     __syncthreads();  // the previous pass's reads are done
-    // stage rows row0 .. row0+31: task t = 8 consecutive latents (chunk t % 64) of row t / 64
+    // stage rows row0 .. row0+31: task t = 8 consecutive latents (chunk t % 64) of row t / 64.
+    // Every load is issued before any is used (rows past the end reload the last row and are
+    // zeroed after), so the staging is one memory round trip.
+    constexpr int kTasks = kUpRows * 64 / kThreads;
+    f32x4 xs[kTasks][2];
 #pragma unroll
-    for (int k = 0; k < kUpRows * 64 / kThreads; ++k) {
+    for (int k = 0; k < kTasks; ++k) {
+      const int task = threadIdx.x + kThreads * k;
+      const int row = min(row0 + (task >> 6), rows - 1);
+      const float* src = o_lat + ((size_t)row * H + h) * kLatent + 8 * (task & 63);
+      xs[k][0] = *(const f32x4*)src;
+      xs[k][1] = *(const f32x4*)(src + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < kTasks; ++k) {
       const int task = threadIdx.x + kThreads * k;
       const int r = task >> 6, c = task & 63;
-      const int row = row0 + r;
-      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-      if (row < rows) {
-        const float* src = o_lat + ((size_t)row * H + h) * kLatent + 8 * c;
-        x0 = *(const f32x4*)src;
-        x1 = *(const f32x4*)(src + 4);
-      }
+      f32x4 x0 = xs[k][0], x1 = xs[k][1];
+      if (row0 + r >= rows) x0 = x1 = (f32x4){0.f, 0.f, 0.f, 0.f};
       bf16x8 vh, vl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -90,12 +97,20 @@ __global__ __launch_bounds__(kThreads) void up_v_kernel(const float* __restrict_
 #pragma unroll
     for (int rb = 0; rb < kUpRows / 16; ++rb) {
       const int r = 16 * rb + ql;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // every operand of the block read from LDS before the first product (one LDS round trip)
+      bf16x8 bh[16], bl[16];
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int off = r * kRowBytes + 16 * up_slot(r, 4 * s + g);
-        acc = mfma16x16(wa[s], *(const bf16x8*)(hi_t + off), acc);
-        acc = mfma16x16(wa[s], *(const bf16x8*)(lo_t + off), acc);
+        bh[s] = *(const bf16x8*)(hi_t + off);
+        bl[s] = *(const bf16x8*)(lo_t + off);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        acc = mfma16x16(wa[s], bh[s], acc);
+        acc = mfma16x16(wa[s], bl[s], acc);
       }
       // lane holds row row0 + r, output dims d0 + 4g .. +3
       const int row = row0 + r;
@@ -162,12 +177,26 @@ __global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a)
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const uint8_t* wrow = wv_t + (d0 + ql) * (kRowBytes / 2);
+  // operands read from LDS kAhead k-steps ahead of the products that use them
+  constexpr int kAhead = 4;
+  bf16x8 ow[kAhead + 1], oh[kAhead + 1], ol[kAhead + 1];
+  auto rd = [&](int s, int slot) {
+    if (s < 8) ow[slot] = *(const bf16x8*)(wrow + 16 * ((4 * s + g) ^ ql));
+    const int off = ql * kRowBytes + 16 * up_slot(ql, 4 * s + g);
+    oh[slot] = *(const bf16x8*)(hi_t + off);
+    ol[slot] = *(const bf16x8*)(lo_t + off);
+  };
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s) rd(s, s);
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
-    const bf16x8 w = s < 8 ? *(const bf16x8*)(wrow + 16 * ((4 * s + g) ^ ql)) : wa[s - 8];
-    const int off = ql * kRowBytes + 16 * up_slot(ql, 4 * s + g);
-    acc = mfma16x16(w, *(const bf16x8*)(hi_t + off), acc);
-    acc = mfma16x16(w, *(const bf16x8*)(lo_t + off), acc);
+    if (s + kAhead < 16) rd(s + kAhead, (s + kAhead) % (kAhead + 1));
+    const int k = s % (kAhead + 1);
+    const bf16x8 w = s < 8 ? ow[k] : wa[s - 8];
+    __builtin_amdgcn_sched_barrier(0);
+    acc = mfma16x16(w, oh[k], acc);
+    acc = mfma16x16(w, ol[k], acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // lane holds row row0 + ql, output dims d0 + 4g .. +3
   const int row = row0 + ql;
