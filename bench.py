@@ -301,6 +301,51 @@ def time_latency(name: str = "decode_b1_l256", samples: int = 200):
     return res
 
 
+def time_read_ceiling(mib: int = 256, nsets: int = 3, calls: int = 30):
+    """The device's plain streaming-read rate (mla_stream_read): `calls` reads of `mib` MiB, the
+    `nsets` buffers rotating so that the 256 MB Infinity Cache cannot serve them, launched back to
+    back between two HIP events on the launch stream (as the attention calls are timed), and the
+    spread of single calls, each between its own events behind a short GPU spin so that the events
+    bracket the kernel rather than the host's launch.  The ceiling beside the published 8 TB/s
+    against which the cache streams of the attention kernels are read."""
+    import torch
+    from mla_latent_cache_absorb_amd import binding
+
+    dev = torch.device("cuda:0")
+    bufs = [torch.full((mib << 20,), s + 1, dtype=torch.uint8, device=dev) for s in range(nsets)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for k in range(4 * nsets):
+        binding.mla_stream_read(bufs[k % nsets], sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(calls):
+        binding.mla_stream_read(bufs[k % nsets], sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    avg = e0.elapsed_time(e1) / calls
+    spin = getattr(torch.cuda, "_sleep", None)
+    per = []
+    for k in range(calls):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if spin is not None:
+            spin(20000)
+        a.record(stream)
+        binding.mla_stream_read(bufs[k % nsets], sink)
+        b.record(stream)
+        b.synchronize()
+        per.append(a.elapsed_time(b))
+    per.sort()
+    nbytes = mib << 20
+    gbs = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"kernel": "stream_read_kernel", "bytes_per_call": nbytes, "buffers_rotated": nsets,
+            "avg_launch_ms": round(avg, 6), "GB/s": gbs(avg), "frac_of_peak": round(gbs(avg) / HBM_PEAK_GBS, 4),
+            "single_call_ms_p10_p50_p90": [round(per[int(f * (calls - 1) + 0.5)], 6) for f in (0.1, 0.5, 0.9)]}
+
+
 def time_indexer(name: str, steps: int, warmup: int):
     """The k-pooled indexer on the sequences of `name`: pooled keys (a full build, and a decode
     step's build of each sequence's newest pool), pool scores for all queries, top-k selection
@@ -692,6 +737,9 @@ def main():
     ap.add_argument("--no-qlen-sweep", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true")
+    ap.add_argument("--read-ceiling-only", action="store_true",
+                    help="time only the plain streaming read of 256 MiB (the device's read ceiling)")
     ap.add_argument("--latency-only", action="store_true",
                     help="time only the batch-1 decode latency (256 positions), for profiling it on its own")
     ap.add_argument("--other-configs-only", action="store_true",
@@ -732,6 +780,9 @@ def main():
         log(f"[bench] copied {args.calibrate_copy} MiB three times")
         del src, dst
         torch.cuda.empty_cache()
+    if args.read_ceiling_only:
+        print(json.dumps({"read_ceiling": time_read_ceiling()}), flush=True)
+        return
     if args.latency_only:
         print(json.dumps({"latency_b1": time_latency()}), flush=True)
         return
@@ -815,6 +866,10 @@ def main():
             "launch_ms_p10_p50_p90": [round(x, 6) for x in s["stage_pct_ms"]["latent_attn"]],
             "fused_attn_up_v": {"value": round(tf_fused, 2), "unit": "TFLOP/s",
                                 "frac": round(tf_fused / BF16_PEAK_TFLOPS, 4), "flops": fused_flops}}
+    if not args.no_read_ceiling:
+        log("[bench] timing the plain streaming read (read ceiling)")
+        result["read_ceiling"] = time_read_ceiling()
+        result["roofline"]["frac_of_read_ceiling"] = round(achieved / result["read_ceiling"]["GB/s"], 4)
     if not args.no_latency:
         log("[bench] timing the batch-1 decode latency")
         result["latency_b1"] = time_latency()

@@ -346,6 +346,21 @@ int mla_check_attn_inputs(const int32_t* cache_len, const int32_t* idx, const in
                           int32_t Q, int32_t K_max, int32_t max_cache_len, int32_t* flags, void* stream);
 
 /*
+ * Measurement helper, not a step of the attention path: reads `bytes` of device memory at src
+ * once, in 32 KiB chunks spread over the GPU, as a plain streaming read.  Its rate is the
+ * device's achievable streaming-read bandwidth, the ceiling beside the published peak against
+ * which the attention kernels' cache streams are measured (page "Module 05", section 5: decode is
+ * bandwidth-bound, and a workload's regime is measured rather than counted).
+ *   src    device memory, 16-byte aligned, bytes readable
+ *   bytes  a positive multiple of 32768
+ *   never  a value the folded bytes (XOR of every 32-bit word each lane reads) will not equal
+ *   sink   one uint32 (device): OR-ed with 1 only if some lane's folded value equals never, so
+ *          that the loads cannot be dropped; practically never written
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (bytes), MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_stream_read(const void* src, size_t bytes, uint32_t never, uint32_t* sink, void* stream);
+
+/*
  * mla_latent_attn_up_v for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  Same arguments, kernels,
  * split count and bits as mla_latent_attn_up_v, minus the workspace: the split partials live

@@ -29,7 +29,7 @@ EXPORTS = ("mla_status_string", "mla_absorb_q", "mla_latent_attn_num_splits", "m
            "mla_latent_attn", "mla_latent_attn_indexed", "mla_up_v", "mla_kpool_keys", "mla_indexer_scores",
            "mla_indexer_select", "mla_latent_append", "mla_expand_kv", "mla_naive_attn",
            "mla_latent_attn_up_v_workspace_size", "mla_latent_attn_up_v", "mla_check_attn_inputs",
-           "mla_latent_attn_up_v_noalloc")
+           "mla_latent_attn_up_v_noalloc", "mla_stream_read")
 
 
 class MlaError(RuntimeError):
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.mla_latent_attn_up_v_noalloc.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
                                                    vp, i32, vp, vp, vp]
         L.mla_latent_attn_up_v_noalloc.restype = ctypes.c_int
+        L.mla_stream_read.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
+        L.mla_stream_read.restype = ctypes.c_int
         L.mla_check_attn_inputs.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
         L.mla_check_attn_inputs.restype = ctypes.c_int
         L.mla_up_v.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
@@ -407,6 +409,21 @@ def mla_latent_attn_up_v_noalloc(q_abs: torch.Tensor, cache: torch.Tensor, cache
                                               float(scale), int(num_splits), _ptr(w_v), D, _ptr(out), _ptr(lse),
                                               _stream(stream)), "mla_latent_attn_up_v_noalloc")
     return out, lse
+
+
+def mla_stream_read(src: torch.Tensor, sink: torch.Tensor, never: int = 0x7BADF00D, stream=None) -> None:
+    """Measurement helper: read every byte of src (contiguous, a multiple of 32 KiB) once as a plain
+    streaming read; sink is one int32 on the same GPU, practically never written."""
+    if not isinstance(src, torch.Tensor) or not src.is_contiguous():
+        raise ValueError("src must be a contiguous tensor")
+    if not isinstance(sink, torch.Tensor) or sink.dtype != torch.int32 or sink.numel() < 1:
+        raise TypeError("sink must be an int32 tensor")
+    nbytes = _nbytes(src)
+    if nbytes < 32768 or nbytes % 32768:
+        raise ValueError("src must hold a positive multiple of 32 KiB")
+    _gpu(src, sink)
+    _check(lib().mla_stream_read(_ptr(src), nbytes, int(never) & 0xFFFFFFFF, _ptr(sink), _stream(stream)),
+           "mla_stream_read")
 
 
 # ------------------------------------------------------------------ down-projection and append

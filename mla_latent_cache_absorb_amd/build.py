@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["mla_api.hip", "latent_attn.hip", "absorb_q.hip", "up_v.hip", "kpool_indexer.hip",
-           "latent_down.hip", "naive_attn.hip", "check_inputs.hip"]
+           "latent_down.hip", "naive_attn.hip", "check_inputs.hip", "stream_probe.hip"]
 LIB_NAME = "libmla_absorb.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")

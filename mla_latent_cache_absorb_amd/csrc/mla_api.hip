@@ -300,6 +300,14 @@ int mla_latent_attn_up_v_noalloc(const uint16_t* q_abs, const uint16_t* cache, i
                      max_cache_len, scale, num_splits, nullptr, lse, nullptr, 0, stream, w_v, out, true);
 }
 
+int mla_stream_read(const void* src, size_t bytes, uint32_t never, uint32_t* sink, void* stream) {
+  if (!src || !sink) return MLA_ERR_NULL;
+  if (bytes < mla::kStreamChunkBytes || bytes % mla::kStreamChunkBytes != 0) return MLA_ERR_SHAPE;
+  const int dst = check_device(nullptr);
+  if (dst != MLA_OK) return dst;
+  return mla::launch_stream_read(src, bytes, never, sink, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_check_attn_inputs(const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t B,
                           int32_t Q, int32_t K_max, int32_t max_cache_len, int32_t* flags, void* stream) {
   static_assert(mla::kBadCacheLenShort == MLA_BAD_CACHE_LEN_SHORT && mla::kBadCacheLenLong == MLA_BAD_CACHE_LEN_LONG &&

@@ -147,4 +147,8 @@ struct CheckArgs {
 };
 hipError_t launch_check_inputs(const CheckArgs& a, hipStream_t stream);
 
+// ---- streaming-read measurement
+constexpr size_t kStreamChunkBytes = 32768;  // bytes one workgroup reads per turn (256 lanes x 8 x 16 B)
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t never, uint32_t* sink, hipStream_t stream);
+
 }  // namespace mla

@@ -211,6 +211,17 @@ def test_noalloc_host_validation(L):
                                              _bf(64, 256, 512), None)
 
 
+def test_stream_read_host_validation(L):
+    fake = ctypes.c_void_p(0x1000)
+    f = L.mla_stream_read
+    assert f(None, 32768, 0, fake, None) == binding.MLA_ERR_NULL
+    assert f(fake, 32768, 0, None, None) == binding.MLA_ERR_NULL
+    assert f(fake, 0, 0, fake, None) == binding.MLA_ERR_SHAPE
+    assert f(fake, 32768 + 16, 0, fake, None) == binding.MLA_ERR_SHAPE
+    with pytest.raises(ValueError):
+        binding.mla_stream_read(_bf(100), _i32(1))
+
+
 def test_input_check_host_validation(L):
     fake = ctypes.c_void_p(0x1000)
     f = L.mla_check_attn_inputs
