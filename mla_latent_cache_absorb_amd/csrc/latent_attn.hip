@@ -66,16 +66,6 @@ __device__ __forceinline__ float quad_sum(float x) {
   return half_swap_sum(x);
 }
 
-// Merge of row `row`'s split partials (merge_splits); thread t owns latents 4t .. 4t+3.
-__device__ __forceinline__ void merge_row(const AttnArgs& a, size_t row, int t) {
-  const size_t rows = (size_t)a.B * a.Q * a.H;
-  float lse2;
-  const f32x4 o = merge_splits(a.part_o + row * kLatent + 4 * t, a.part_ml + 2 * row, rows * kLatent, 2 * rows,
-                               a.num_splits, &lse2);
-  *(f32x4*)(a.o_lat + row * kLatent + 4 * t) = o;
-  if (a.lse != nullptr && t == 0) a.lse[row] = lse2 * 0.69314718055994531f;
-}
-
 // Largest of this lane's eight scores of a tile and those of the other three lanes of its head
 // (one column of the two 16x16 score blocks), times scale * log2(e).
 __device__ __forceinline__ float tile_max(const float (&v)[8], float c2) {
@@ -684,8 +674,23 @@ void latent_attn_pair_kernel(AttnArgs a) {
   }
 }
 
-// Merge of the split partials: one workgroup of 128 threads per (b, i, head).
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) { merge_row(a, blockIdx.x, threadIdx.x); }
+// Merge of the split partials (up to eight splits): four (b, i, head) rows per workgroup of 256
+// threads, 64 threads per row, thread t owning latents 8t .. 8t+7 (16-byte loads, 32-byte stores).
+constexpr int kCombineRows = 4;
+__global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(AttnArgs a) {
+  const size_t rows = (size_t)a.B * a.Q * a.H;
+  const size_t row = (size_t)blockIdx.x * kCombineRows + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int t = threadIdx.x & 63;
+  float lse2;
+  f32x4 o[2];
+  merge_splits8(a.part_o + row * kLatent + 8 * t, a.part_ml + 2 * row, rows * kLatent, 2 * rows, a.num_splits, &lse2,
+                o);
+  float* dst = a.o_lat + row * kLatent + 8 * t;
+  *(f32x4*)dst = o[0];
+  *(f32x4*)(dst + 4) = o[1];
+  if (a.lse != nullptr && t == 0) a.lse[row] = lse2 * 0.69314718055994531f;
+}
 
 // Merge of more than eight splits: G = min(8, groups of eight splits) thread groups of 128 per
 // (b, i, head).  Thread group q reduces group r0 + q of a round of G groups, all the round's loads
@@ -749,7 +754,8 @@ hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
     const dim3 block(128 * (groups < 8 ? groups : 8));
     return hipLaunchKernel((const void*)&combine_wide_kernel, grid, block, args, 0, stream);
   }
-  return hipLaunchKernel((const void*)&combine_kernel, grid, dim3(128), args, 0, stream);
+  const dim3 cgrid((unsigned)(((size_t)a.B * a.Q * a.H + kCombineRows - 1) / kCombineRows));
+  return hipLaunchKernel((const void*)&combine_kernel, cgrid, dim3(64 * kCombineRows), args, 0, stream);
 }
 
 }  // namespace mla

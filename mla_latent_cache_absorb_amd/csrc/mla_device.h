@@ -20,6 +20,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kLatent = 512;        // R
@@ -248,6 +249,38 @@ __device__ __forceinline__ f32x4 merge_splits(const uint16_t* part_o, const floa
   // __builtin_amdgcn_logf is the hardware base-2 logarithm
   *lse2 = M + __builtin_amdgcn_logf(L);
   return acc * (1.0f / L);
+}
+
+// merge_splits for eight adjacent latents (two blocks of four, one 16-byte load per split and
+// group slot): each block goes through the same steps as in merge_splits, so the bits are the same
+__device__ __forceinline__ void merge_splits8(const uint16_t* part_o, const float* part_ml, size_t o_step,
+                                              size_t ml_step, int S, float* lse2, f32x4 (&out)[2]) {
+  float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    MergeGroup g[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // every slot loaded, as in merge_load
+      const size_t s = (size_t)min(s0 + k, S - 1);
+      const float2 ml = *(const float2*)(part_ml + s * ml_step);
+      const f16x8 x = *(const f16x8*)(part_o + s * o_step);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        g[h].mm[k] = ml.x;
+        g[h].ll[k] = ml.y;
+        g[h].v[k] = __builtin_convertvector((f16x4){x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]}, f32x4);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      MergePartial r;
+      if (merge_group(g[h], S, s0, r)) merge_fold(M[h], L[h], acc[h], r);
+    }
+  }
+  // __builtin_amdgcn_logf is the hardware base-2 logarithm
+  *lse2 = M[0] + __builtin_amdgcn_logf(L[0]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) out[h] = acc[h] * (1.0f / L[h]);
 }
 
 // Map the hardware workgroup id to a logical id so that consecutive logical ids run on the
