@@ -136,40 +136,54 @@ __device__ __forceinline__ TrOffsets transpose_offsets(int lane, int lq) {
           row1 * kRowBytes + 256 * lq + ((x ^ ((row1 >> 2) & 3)) << 4) + ((tq & 1) << 3), te};
 }
 
-// A value wave's result for one head column hv of row bq: lane holds latents 128lq + 32mb + 8ii
-// + 4hf + j.  With one split, o_lat = o / l and lse = (m + log2 l) ln 2 are final; otherwise the
-// normalised partial o / l (fp16; zero for a split that saw nothing) and its (m, l) go to the
-// split's slot for the merge.
-__device__ __forceinline__ void store_value_rows(const AttnArgs& a, int split, int bq, int hv, int lq, int hf,
-                                                 float m_fin, float l_fin, const f32x16 (&o)[4]) {
-  if (a.num_splits == 1) {
-    const float inv_l = 1.0f / l_fin;
-    float* orow = a.o_lat + ((size_t)bq * a.H + hv) * kLatent + 128 * lq + 4 * hf;
+// A value wave's result for one head column hv of row bq with one split: o_lat = o / l and
+// lse = (m + log2 l) ln 2 are final.  The lane holds latents 128lq + 32mb + 8ii + 4hf + j.
+__device__ __forceinline__ void store_value_rows(const AttnArgs& a, int bq, int hv, int lq, int hf, float m_fin,
+                                                 float l_fin, const f32x16 (&o)[4]) {
+  const float inv_l = 1.0f / l_fin;
+  float* orow = a.o_lat + ((size_t)bq * a.H + hv) * kLatent + 128 * lq + 4 * hf;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        *(f32x4*)(orow + 32 * mb + 8 * ii) = (f32x4){o[mb][4 * ii] * inv_l, o[mb][4 * ii + 1] * inv_l,
-                                                    o[mb][4 * ii + 2] * inv_l, o[mb][4 * ii + 3] * inv_l};
-    // __builtin_amdgcn_logf is the hardware base-2 logarithm
-    if (a.lse != nullptr && hf == 0 && lq == 0)
-      a.lse[(size_t)bq * a.H + hv] = (m_fin + __builtin_amdgcn_logf(l_fin)) * 0.69314718055994531f;
-  } else {
-    const size_t prow_idx = ((size_t)split * a.B * a.Q + bq) * a.H + hv;
-    uint16_t* orow = a.part_o + prow_idx * kLatent + 128 * lq + 4 * hf;
-    const float inv_l = l_fin > 0.f ? 1.0f / l_fin : 0.f;
+    for (int ii = 0; ii < 4; ++ii)
+      *(f32x4*)(orow + 32 * mb + 8 * ii) = (f32x4){o[mb][4 * ii] * inv_l, o[mb][4 * ii + 1] * inv_l,
+                                                  o[mb][4 * ii + 2] * inv_l, o[mb][4 * ii + 3] * inv_l};
+  // __builtin_amdgcn_logf is the hardware base-2 logarithm
+  if (a.lse != nullptr && hf == 0 && lq == 0)
+    a.lse[(size_t)bq * a.H + hv] = (m_fin + __builtin_amdgcn_logf(l_fin)) * 0.69314718055994531f;
+}
+
+// A workgroup's split partial (several splits): the value waves stage the normalised fp16 rows
+// (64 per query) in LDS, in the tile ring, idle once the loop is over; then every thread copies
+// them out as 16-byte chunks, each wave instruction one contiguous KiB, since the 64 heads of a
+// query are 64 consecutive rows of part_o.  Written straight from the accumulators, each store
+// instruction would put 16 bytes into each of 32 rows.  Staged rows are 1 KiB apart, chunk c of
+// row r at chunk position c ^ (r & 63): the staging writes of the 32 rows a wave holds then fall
+// in different banks, and a row read back stays one KiB.
+__device__ __forceinline__ void stage_value_rows(uint8_t* stage, int srow, int lq, int hf, float l_fin,
+                                                 const f32x16 (&o)[4]) {
+  const float inv_l = l_fin > 0.f ? 1.0f / l_fin : 0.f;
+  uint8_t* rowp = stage + srow * kRowBytes + 8 * hf;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        *(f16x4*)(orow + 32 * mb + 8 * ii) =
-            __builtin_convertvector((f32x4){o[mb][4 * ii] * inv_l, o[mb][4 * ii + 1] * inv_l,
-                                            o[mb][4 * ii + 2] * inv_l, o[mb][4 * ii + 3] * inv_l}, f16x4);
-    if (hf == 0 && lq == 0) {
-      a.part_ml[2 * prow_idx] = m_fin;
-      a.part_ml[2 * prow_idx + 1] = l_fin;
+    for (int ii = 0; ii < 4; ++ii) {
+      const int chunk = 16 * lq + 4 * mb + ii;  // latents 8 chunk .. +7; this lane's four at + 4 hf
+      *(f16x4*)(rowp + 16 * (chunk ^ (srow & 63))) =
+          __builtin_convertvector((f32x4){o[mb][4 * ii] * inv_l, o[mb][4 * ii + 1] * inv_l,
+                                          o[mb][4 * ii + 2] * inv_l, o[mb][4 * ii + 3] * inv_l}, f16x4);
     }
+}
+// every thread of the workgroup, after the staging writes and a barrier: staged rows srow0 ..
+// srow0 + 63 to part_o rows first .., and their (m, l) from m_row / l_row
+__device__ __forceinline__ void copy_partial_block(const AttnArgs& a, size_t first, const uint8_t* stage, int srow0,
+                                                   const float* m_row, const float* l_row) {
+  uint16_t* dst = a.part_o + first * kLatent;
+  for (int c = threadIdx.x; c < 64 * 64; c += kThreads) {
+    const int h = c >> 6, k = c & 63, r = srow0 + h;
+    *(int4*)(dst + h * kLatent + 8 * k) = *(const int4*)(stage + r * kRowBytes + 16 * (k ^ (r & 63)));
   }
+  if (threadIdx.x < 64) *(float2*)(a.part_ml + 2 * (first + threadIdx.x)) = float2{m_row[threadIdx.x], l_row[threadIdx.x]};
 }
 
 template <bool INDEXED>
@@ -429,8 +443,16 @@ void latent_attn_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();  // (m, l) are posted
-    store_value_rows(a, split, bq, hv, lq, hf, mlbuf[0][32 * vh + hl], mlbuf[1][32 * vh + hl], o);
+    __syncthreads();  // (m, l) are posted; every read of the tile ring is done
+    if (a.num_splits == 1)
+      store_value_rows(a, bq, hv, lq, hf, mlbuf[0][32 * vh + hl], mlbuf[1][32 * vh + hl], o);
+    else
+      stage_value_rows(&smem[0][0], 32 * vh + hl, lq, hf, mlbuf[1][32 * vh + hl], o);
+  }
+  if (a.num_splits > 1) {
+    __syncthreads();  // the partial is staged
+    copy_partial_block(a, ((size_t)split * a.B * a.Q + bq) * a.H + (size_t)hg * 64, &smem[0][0], 0, mlbuf[0],
+                       mlbuf[1]);
   }
 }
 
@@ -663,13 +685,27 @@ void latent_attn_pair_kernel(AttnArgs a) {
           for (int nb = 0; nb < 2; ++nb) pf[nb] = *(const bf16x8*)(pb + 32 * nb * kPStride + 32);
       }
     }
-    __syncthreads();  // (m, l) are posted
+    __syncthreads();  // (m, l) are posted; every read of the tile ring is done
     const int iq = qq == 0 ? i0 : i1;
     if (iq >= 0) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        store_value_rows(a, split, b * a.Q + iq, hg * 64 + 32 * nb + hl, lq, hf, mlbuf[0][prow0 + 32 * nb],
-                         mlbuf[1][prow0 + 32 * nb], o[nb]);
+      for (int nb = 0; nb < 2; ++nb) {
+        if (a.num_splits == 1)
+          store_value_rows(a, b * a.Q + iq, hg * 64 + 32 * nb + hl, lq, hf, mlbuf[0][prow0 + 32 * nb],
+                           mlbuf[1][prow0 + 32 * nb], o[nb]);
+        else
+          stage_value_rows(&smem[0][0], prow0 + 32 * nb, lq, hf, mlbuf[1][prow0 + 32 * nb], o[nb]);
+      }
+    }
+  }
+  if (a.num_splits > 1) {
+    __syncthreads();  // the partials are staged: rows 64 qq + head of query qq of the pair
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int iq = qq == 0 ? i0 : i1;
+      if (iq >= 0)
+        copy_partial_block(a, ((size_t)split * a.B * a.Q + b * a.Q + iq) * a.H + (size_t)hg * 64, &smem[0][0],
+                           64 * qq, mlbuf[0] + 64 * qq, mlbuf[1] + 64 * qq);
     }
   }
 }
@@ -692,46 +728,52 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(AttnArgs a) 
   if (a.lse != nullptr && t == 0) a.lse[row] = lse2 * 0.69314718055994531f;
 }
 
-// Merge of more than eight splits: G = min(8, groups of eight splits) thread groups of 128 per
-// (b, i, head).  Thread group q reduces group r0 + q of a round of G groups, all the round's loads
-// in flight together, and thread group 0 folds the round's results in group order (the order
-// merge_splits uses, so the bits are the same): one memory round trip per G groups instead of
-// one per group.
-__global__ __launch_bounds__(1024) void combine_wide_kernel(AttnArgs a) {
-  __shared__ f32x4 gacc[8][128];
-  __shared__ float gM[8][128], gL[8][128];
+// Merge of more than eight splits: G = min(8, groups of eight splits) thread groups of 64 per
+// (b, i, head), thread t owning latents 8t .. 8t+7.  Thread group q reduces group r0 + q of a round
+// of G groups, all the round's loads in flight together, and thread group 0 folds the round's
+// results in group order (the order merge_splits uses, so the bits are the same): one memory round
+// trip per G groups instead of one per group.
+__global__ __launch_bounds__(512) void combine_wide_kernel(AttnArgs a) {
+  __shared__ f32x4 gacc[8][2][64];
+  __shared__ float gM[8][64], gL[8][64];  // the same for both blocks of four latents
   const size_t row = blockIdx.x;
-  const int t = threadIdx.x & 127, q = threadIdx.x >> 7;
-  const int G = blockDim.x >> 7;  // thread groups, 2 .. 8
+  const int t = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int G = blockDim.x >> 6;  // thread groups, 2 .. 8
   const size_t rows = (size_t)a.B * a.Q * a.H;
   const int S = a.num_splits;
   const int ngroups = (S + 7) / 8;
-  const uint16_t* po = a.part_o + row * kLatent + 4 * t;
+  const uint16_t* po = a.part_o + row * kLatent + 8 * t;
   const float* pml = a.part_ml + 2 * row;
-  float M = -INFINITY, L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   for (int r0 = 0; r0 < ngroups; r0 += G) {
     const int g = r0 + q;
-    MergePartial p;
+    MergePartial p[2];
     bool ok = false;
     if (g < ngroups) {
-      MergeGroup grp;
-      merge_load(grp, po, pml, rows * kLatent, 2 * rows, S, 8 * g);
-      ok = merge_group(grp, S, 8 * g, p);
+      MergeGroup grp[2];
+      merge_load8(grp, po, pml, rows * kLatent, 2 * rows, S, 8 * g);
+      ok = merge_group(grp[0], S, 8 * g, p[0]);
+      merge_group(grp[1], S, 8 * g, p[1]);  // same weights: ok alike
     }
-    gM[q][t] = ok ? p.M : -INFINITY;
-    gL[q][t] = ok ? p.L : 0.f;
-    gacc[q][t] = ok ? p.acc : f32x4{0.f, 0.f, 0.f, 0.f};
+    gM[q][t] = ok ? p[0].M : -INFINITY;
+    gL[q][t] = ok ? p[0].L : 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) gacc[q][h][t] = ok ? p[h].acc : f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
     if (q == 0)
       for (int k = 0; k < G && r0 + k < ngroups; ++k)
-        if (gM[k][t] != -INFINITY) merge_fold(M, L, acc, MergePartial{gM[k][t], gL[k][t], gacc[k][t]});
+        if (gM[k][t] != -INFINITY)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) merge_fold(M[h], L[h], acc[h], MergePartial{gM[k][t], gL[k][t], gacc[k][h][t]});
     __syncthreads();  // the round's slots are rewritten by the next round
   }
   if (q == 0) {
-    *(f32x4*)(a.o_lat + row * kLatent + 4 * t) = acc * (1.0f / L);
+    float* dst = a.o_lat + row * kLatent + 8 * t;
+    *(f32x4*)dst = acc[0] * (1.0f / L[0]);
+    *(f32x4*)(dst + 4) = acc[1] * (1.0f / L[1]);
     // __builtin_amdgcn_logf is the hardware base-2 logarithm
-    if (a.lse != nullptr && t == 0) a.lse[row] = (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f;
+    if (a.lse != nullptr && t == 0) a.lse[row] = (M[0] + __builtin_amdgcn_logf(L[0])) * 0.69314718055994531f;
   }
 }
 
@@ -751,7 +793,7 @@ hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(a.B * a.Q * a.H);
   if (a.num_splits > 8) {
     const int groups = (a.num_splits + 7) / 8;
-    const dim3 block(128 * (groups < 8 ? groups : 8));
+    const dim3 block(64 * (groups < 8 ? groups : 8));
     return hipLaunchKernel((const void*)&combine_wide_kernel, grid, block, args, 0, stream);
   }
   const dim3 cgrid((unsigned)(((size_t)a.B * a.Q * a.H + kCombineRows - 1) / kCombineRows));

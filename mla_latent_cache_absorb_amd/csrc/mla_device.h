@@ -251,26 +251,32 @@ __device__ __forceinline__ f32x4 merge_splits(const uint16_t* part_o, const floa
   return acc * (1.0f / L);
 }
 
-// merge_splits for eight adjacent latents (two blocks of four, one 16-byte load per split and
-// group slot): each block goes through the same steps as in merge_splits, so the bits are the same
+// merge_load for eight adjacent latents: two blocks of four, one 16-byte load per split slot
+__device__ __forceinline__ void merge_load8(MergeGroup (&g)[2], const uint16_t* part_o, const float* part_ml,
+                                            size_t o_step, size_t ml_step, int S, int s0) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {  // every slot loaded, as in merge_load
+    const size_t s = (size_t)min(s0 + k, S - 1);
+    const float2 ml = *(const float2*)(part_ml + s * ml_step);
+    const f16x8 x = *(const f16x8*)(part_o + s * o_step);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      g[h].mm[k] = ml.x;
+      g[h].ll[k] = ml.y;
+      g[h].v[k] = __builtin_convertvector((f16x4){x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]}, f32x4);
+    }
+  }
+}
+
+// merge_splits for eight adjacent latents (two blocks of four): each block goes through the same
+// steps as in merge_splits, so the bits are the same
 __device__ __forceinline__ void merge_splits8(const uint16_t* part_o, const float* part_ml, size_t o_step,
                                               size_t ml_step, int S, float* lse2, f32x4 (&out)[2]) {
   float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
   f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   for (int s0 = 0; s0 < S; s0 += 8) {
     MergeGroup g[2];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {  // every slot loaded, as in merge_load
-      const size_t s = (size_t)min(s0 + k, S - 1);
-      const float2 ml = *(const float2*)(part_ml + s * ml_step);
-      const f16x8 x = *(const f16x8*)(part_o + s * o_step);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        g[h].mm[k] = ml.x;
-        g[h].ll[k] = ml.y;
-        g[h].v[k] = __builtin_convertvector((f16x4){x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]}, f32x4);
-      }
-    }
+    merge_load8(g, part_o, part_ml, o_step, ml_step, S, s0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       MergePartial r;
