@@ -20,6 +20,7 @@ against the bf16 matrix-core peak.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -159,6 +160,9 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
     for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
+    # no collector pauses inside the timed regions (it runs now, and again after them)
+    gc.collect()
+    gc.disable()
     # whole steps, back to back
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -190,19 +194,30 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
         else:
             binding.mla_up_v(o_lat, d["w_v"], out=out)
 
-    stage, pct = {}, {}
+    stage, pct, stage_all = {}, {}, {}
     for k in ("absorb_q", "latent_attn_up_v", "latent_attn", "up_v"):
         if k.startswith("latent_attn"):
             for s in range(3):
                 one_stage(k, s)
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for s in range(steps):
-                one_stage(k, s)
-            e1.record(stream)
+            # the calls launched back to back in five chunks, an event between chunks (which does not
+            # stop the stream): the per-call average is that of the median chunk, so that one stall
+            # of the host or the device during the run does not set the figure; the average over
+            # every call is kept beside it
+            nchunk = 5 if steps >= 10 else 1
+            sizes = [steps // nchunk + (1 if c < steps % nchunk else 0) for c in range(nchunk)]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(nchunk + 1)]
+            ev[0].record(stream)
+            done = 0
+            for c in range(nchunk):
+                for s in range(sizes[c]):
+                    one_stage(k, done + s)
+                done += sizes[c]
+                ev[c + 1].record(stream)
             torch.cuda.synchronize()
-            stage[k] = e0.elapsed_time(e1) / steps
+            chunk = sorted(ev[c].elapsed_time(ev[c + 1]) / sizes[c] for c in range(nchunk))
+            stage[k] = chunk[nchunk // 2]
+            stage_all[k] = ev[0].elapsed_time(ev[nchunk]) / steps
             # the spread: each call between its own pair of events
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
             ev[0].record(stream)
@@ -226,9 +241,11 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
         torch.cuda.synchronize()
         stage[k] = e0.elapsed_time(e1) / steps
         del graph
+    gc.enable()
     del sets
     torch.cuda.empty_cache()
-    return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, stage_pct_ms=pct, splits=splits, workload=w0)
+    return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, stage_all_ms=stage_all, stage_pct_ms=pct, splits=splits,
+                workload=w0)
 
 
 def time_latency(name: str = "decode_b1_l256", samples: int = 200):
@@ -835,9 +852,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic / (attn_ms * 1e-3) / 1e9, 2),
                      "algorithmic_bytes_per_launch": latent_bytes, "avg_launch_ms": round(attn_ms, 6),
+                     "avg_launch_ms_all_calls": round(r["stage_all_ms"]["latent_attn"], 6),
                      "launch_ms_p10_p50_p90": [round(x, 6) for x in r["stage_pct_ms"]["latent_attn"]]},
         "fused_attn_up_v": {"call": "mla_latent_attn_up_v (split kernel + merge fused into the up-projection)",
                             "avg_launch_ms": round(fused_ms, 6),
+                            "avg_launch_ms_all_calls": round(r["stage_all_ms"]["latent_attn_up_v"], 6),
                             "launch_ms_p10_p50_p90": [round(x, 6) for x in r["stage_pct_ms"]["latent_attn_up_v"]],
                             "algorithmic_bytes_per_launch": fused_bytes,
                             "achieved": round(fused_gbs, 2), "unit": "GB/s",
