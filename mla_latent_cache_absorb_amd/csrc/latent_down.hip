@@ -105,8 +105,9 @@ __global__ __launch_bounds__(kDownThreads) void latent_down_kernel(DownArgs a) {
 // ---------------------------------------------------------------------- long passes (prefill)
 // A tiled product for passes of many tokens: a workgroup owns 64 tokens x 128 channels, four
 // waves of 32 channels x 64 tokens, and streams the hidden dimension through LDS 64 at a time
-// (double-buffered, one copy instruction per 8 rows x 128 bytes, chunk c of row r at slot
-// c ^ ((r >> 1) & 7)).  The sum keeps latent_down_kernel's order exactly: per K-slice of 256 a
+// (a ring of four stages, three in flight while one is multiplied: with one stage in flight the
+// copies' latency set the pace; one copy instruction per 8 rows x 128 bytes, chunk c of row r at
+// slot c ^ ((r >> 1) & 7)).  The sum keeps latent_down_kernel's order exactly: per K-slice of 256 a
 // partial from zero over the same eight MFMA 16x16x32 k-steps, the partials added to the total in
 // slice order, so a token gets the same bits in either kernel.  The operands are swapped (W rows
 // as A, tokens as B), so each lane holds four consecutive channels of one token and stores them
@@ -117,13 +118,15 @@ constexpr int kGemmK = 64;                          // hidden per stage
 constexpr int kGemmRowBytes = kGemmK * 2;           // 128 bytes: 8 chunks of 16
 constexpr int kGemmStages = kHidden / kGemmK;       // 64
 constexpr int kStagesPerSlice = kSlice / kGemmK;    // 4
+constexpr int kGemmRing = 4;                        // stages held in LDS: three in flight, one in use
+constexpr int kGemmCopies = 6;                      // copy instructions per wave per stage
 static_assert(kSlice % kGemmK == 0 && kGemmK % 32 == 0, "a stage holds whole k-steps of one slice");
 
 __device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
 
 __global__ __launch_bounds__(256) void down_gemm_kernel(DownArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ldsW[2][kGemmN * kGemmRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ldsH[2][kGemmM * kGemmRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ldsW[kGemmRing][kGemmN * kGemmRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ldsH[kGemmRing][kGemmM * kGemmRowBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * kGemmN;  // channels
@@ -156,12 +159,16 @@ __global__ __launch_bounds__(256) void down_gemm_kernel(DownArgs a) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) total[x][y] = part[x][y] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
+  for (int st = 0; st < kGemmRing - 1; ++st) issue(st, st);
   for (int st = 0; st < kGemmStages; ++st) {
-    const int buf = st & 1;
-    wait_vmcnt<0>();
-    __syncthreads();  // stage st landed for every wave; every wave is done reading the other buffer
-    if (st + 1 < kGemmStages) issue(st + 1, buf ^ 1);
+    const int buf = st % kGemmRing;
+    // stage st has landed once at most the stages issued after it are in flight
+    if (st + 2 < kGemmStages) wait_vmcnt<2 * kGemmCopies>();
+    else if (st + 1 < kGemmStages) wait_vmcnt<kGemmCopies>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // stage st landed for every wave; every wave is done reading stage st - 1
+    // into the buffer of stage st - 1, which every wave finished reading before the barrier
+    if (st + kGemmRing - 1 < kGemmStages) issue(st + kGemmRing - 1, (st + kGemmRing - 1) % kGemmRing);
     if (st % kStagesPerSlice == 0) {
 #pragma unroll
       for (int x = 0; x < 2; ++x)
