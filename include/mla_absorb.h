@@ -25,8 +25,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work
  *     on it: it never synchronises, never allocates and keeps no state between calls, so
  *     calls on different streams may run concurrently.
- *   - Supported shapes: R == 512, D == 256, H a positive multiple of 64 (the checkpoint
- *     has H = 64).  Other shapes return MLA_ERR_SHAPE.
+ *   - Supported shapes: R == 512, D == 256, H a positive multiple of 16 (the checkpoint
+ *     has H = 64; the attention kernels take heads in groups of 64, the last group of other
+ *     counts partial).  Other shapes return MLA_ERR_SHAPE.
  *   - On any error the call returns a negative status BEFORE enqueuing anything, so no
  *     output is written.  MLA_ERR_HIP means a launch failed after validation.
  *   - The current HIP device must be a gfx950 GPU (MLA_ERR_DEVICE otherwise).

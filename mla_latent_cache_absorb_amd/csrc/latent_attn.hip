@@ -175,15 +175,17 @@ __device__ __forceinline__ void stage_value_rows(uint8_t* stage, int srow, int l
     }
 }
 // every thread of the workgroup, after the staging writes and a barrier: staged rows srow0 ..
-// srow0 + 63 to part_o rows first .., and their (m, l) from m_row / l_row
-__device__ __forceinline__ void copy_partial_block(const AttnArgs& a, size_t first, const uint8_t* stage, int srow0,
-                                                   const float* m_row, const float* l_row) {
+// srow0 + nrows - 1 (the group's heads, fewer than 64 in a last partial group) to part_o rows
+// first .., and their (m, l) from m_row / l_row
+__device__ __forceinline__ void copy_partial_block(const AttnArgs& a, size_t first, int nrows, const uint8_t* stage,
+                                                   int srow0, const float* m_row, const float* l_row) {
   uint16_t* dst = a.part_o + first * kLatent;
-  for (int c = threadIdx.x; c < 64 * 64; c += kThreads) {
+  for (int c = threadIdx.x; c < nrows * 64; c += kThreads) {
     const int h = c >> 6, k = c & 63, r = srow0 + h;
     *(int4*)(dst + h * kLatent + 8 * k) = *(const int4*)(stage + r * kRowBytes + 16 * (k ^ (r & 63)));
   }
-  if (threadIdx.x < 64) *(float2*)(a.part_ml + 2 * (first + threadIdx.x)) = float2{m_row[threadIdx.x], l_row[threadIdx.x]};
+  if ((int)threadIdx.x < nrows)
+    *(float2*)(a.part_ml + 2 * (first + threadIdx.x)) = float2{m_row[threadIdx.x], l_row[threadIdx.x]};
 }
 
 template <bool INDEXED>
@@ -232,7 +234,7 @@ void latent_attn_kernel(AttnArgs a) {
     // ======================= score waves =======================
     const int s = wave;
     const int c = lane & 15, G = lane >> 4;  // head 16s + c; k / row group G
-    const int h = hg * 64 + 16 * s + c;
+    const int h = min(hg * 64 + 16 * s + c, a.H - 1);  // a partial group's missing heads reuse the last
     const float c2 = a.scale_log2;
     // absorbed query as the B operand: latents 32ks + 8G .. +7
     bf16x8 qf[16];
@@ -444,15 +446,16 @@ void latent_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();  // (m, l) are posted; every read of the tile ring is done
-    if (a.num_splits == 1)
-      store_value_rows(a, bq, hv, lq, hf, mlbuf[0][32 * vh + hl], mlbuf[1][32 * vh + hl], o);
-    else
+    if (a.num_splits == 1) {
+      if (hv < a.H) store_value_rows(a, bq, hv, lq, hf, mlbuf[0][32 * vh + hl], mlbuf[1][32 * vh + hl], o);
+    } else {
       stage_value_rows(&smem[0][0], 32 * vh + hl, lq, hf, mlbuf[1][32 * vh + hl], o);
+    }
   }
   if (a.num_splits > 1) {
     __syncthreads();  // the partial is staged
-    copy_partial_block(a, ((size_t)split * a.B * a.Q + bq) * a.H + (size_t)hg * 64, &smem[0][0], 0, mlbuf[0],
-                       mlbuf[1]);
+    copy_partial_block(a, ((size_t)split * a.B * a.Q + bq) * a.H + (size_t)hg * 64, min(64, a.H - 64 * hg),
+                       &smem[0][0], 0, mlbuf[0], mlbuf[1]);
   }
 }
 
@@ -511,7 +514,7 @@ void latent_attn_pair_kernel(AttnArgs a) {
     // ======================= score waves =======================
     const int s = wave;
     const int c = lane & 15, G = lane >> 4;  // head 16s + c; k / row group G
-    const int h = hg * 64 + 16 * s + c;
+    const int h = min(hg * 64 + 16 * s + c, a.H - 1);  // a partial group's missing heads reuse the last
     const float c2 = a.scale_log2;
     // absorbed queries as B operands: latents 32ks + 8G .. +7 (a lone query is loaded twice)
     bf16x8 qf[2][16];
@@ -690,10 +693,11 @@ void latent_attn_pair_kernel(AttnArgs a) {
     if (iq >= 0) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        if (a.num_splits == 1)
-          store_value_rows(a, b * a.Q + iq, hg * 64 + 32 * nb + hl, lq, hf, mlbuf[0][prow0 + 32 * nb],
-                           mlbuf[1][prow0 + 32 * nb], o[nb]);
-        else
+        if (a.num_splits == 1) {
+          if (hg * 64 + 32 * nb + hl < a.H)
+            store_value_rows(a, b * a.Q + iq, hg * 64 + 32 * nb + hl, lq, hf, mlbuf[0][prow0 + 32 * nb],
+                             mlbuf[1][prow0 + 32 * nb], o[nb]);
+        } else
           stage_value_rows(&smem[0][0], prow0 + 32 * nb, lq, hf, mlbuf[1][prow0 + 32 * nb], o[nb]);
       }
     }
@@ -704,8 +708,8 @@ void latent_attn_pair_kernel(AttnArgs a) {
     for (int qq = 0; qq < 2; ++qq) {
       const int iq = qq == 0 ? i0 : i1;
       if (iq >= 0)
-        copy_partial_block(a, ((size_t)split * a.B * a.Q + b * a.Q + iq) * a.H + (size_t)hg * 64, &smem[0][0],
-                           64 * qq, mlbuf[0] + 64 * qq, mlbuf[1] + 64 * qq);
+        copy_partial_block(a, ((size_t)split * a.B * a.Q + b * a.Q + iq) * a.H + (size_t)hg * 64,
+                           min(64, a.H - 64 * hg), &smem[0][0], 64 * qq, mlbuf[0] + 64 * qq, mlbuf[1] + 64 * qq);
     }
   }
 }

@@ -67,18 +67,21 @@ int32_t split_length(int32_t max_positions, int32_t s) {
   return per * mla::kTilePositions;
 }
 
-bool supported(int32_t H, int32_t D, int32_t R) { return R == 512 && D == 256 && H > 0 && H % 64 == 0; }
+bool supported(int32_t H, int32_t D, int32_t R) { return R == 512 && D == 256 && H > 0 && H % 16 == 0; }
+
+// head groups of the attention kernels: 64 heads each, the last one possibly partial
+int32_t head_groups(int32_t H) { return (H + 63) / 64; }
 
 // the choice depends on the workgroup count per split (one per sequence, 64-head group and query,
 // or pair of queries for dense calls with two or more) and the tiles only
 int resolve_splits(int32_t B, int32_t Q, int32_t H, int32_t max_positions, int32_t num_splits, int cus,
                    bool indexed) {
-  if (B < 1 || Q < 1 || H < 64 || H % 64 != 0 || max_positions < 1) return MLA_ERR_SHAPE;
+  if (B < 1 || Q < 1 || H < 16 || H % 16 != 0 || max_positions < 1) return MLA_ERR_SHAPE;
   if (num_splits < 0) return MLA_ERR_ARG;
   const int32_t tiles = (max_positions + mla::kTilePositions - 1) / mla::kTilePositions;
   int32_t s;
   if (num_splits == 0) {
-    s = choose_splits((int64_t)B * mla::query_units(indexed, Q) * (H / 64), max_positions, cus);
+    s = choose_splits((int64_t)B * mla::query_units(indexed, Q) * head_groups(H), max_positions, cus);
   } else {
     s = num_splits > mla::kMaxSplits ? mla::kMaxSplits : num_splits;
     if (s > tiles) s = tiles;
@@ -165,7 +168,7 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
     workspace_bytes = kScratchBytes;
   }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
-  const int64_t total = (int64_t)B * mla::query_units(indexed, Q) * (H / 64) * s;
+  const int64_t total = (int64_t)B * mla::query_units(indexed, Q) * head_groups(H) * s;
   if (total > 0x7fffffff || (int64_t)B * Q * H > 0x7fffffff) return MLA_ERR_SHAPE;
 
   mla::AttnArgs a;
@@ -179,7 +182,7 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
   a.B = B;
   a.Q = Q;
   a.H = H;
-  a.HG = H / 64;
+  a.HG = head_groups(H);
   a.max_cache_len = max_cache_len;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_splits = s;
@@ -218,7 +221,7 @@ const char* mla_status_string(int status) {
   switch (status) {
     case MLA_OK: return "ok";
     case MLA_ERR_NULL: return "a required pointer is NULL";
-    case MLA_ERR_SHAPE: return "unsupported shape (need R == 512, D == 256, H a positive multiple of 64, sizes >= 1)";
+    case MLA_ERR_SHAPE: return "unsupported shape (need R == 512, D == 256, H a positive multiple of 16, sizes >= 1)";
     case MLA_ERR_ARG: return "argument out of range";
     case MLA_ERR_WORKSPACE: return "workspace too small";
     case MLA_ERR_HIP: return "HIP runtime call or kernel launch failed";

@@ -17,7 +17,7 @@ struct AttnArgs {
   const int32_t* idx;             // [B][Q][K_max] (indexed only)
   const int32_t* idx_len;         // [B][Q]        (indexed only)
   int32_t K_max;
-  int32_t B, Q, H, HG;            // HG = H / 64 head groups
+  int32_t B, Q, H, HG;            // HG = ceil(H / 64) head groups (H a multiple of 16)
   int32_t max_cache_len;
   float scale_log2;               // softmax scale * log2(e)
   int32_t num_splits, split_len;  // split_len: positions (or index slots) per split, multiple of the tile

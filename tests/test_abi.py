@@ -48,7 +48,7 @@ def test_host_validation_without_device(L):
     # null pointers and shapes are rejected before any device call
     assert L.mla_absorb_q(None, fake, fake, 1, 64, 256, 512, 1.0, None) == binding.MLA_ERR_NULL
     assert L.mla_absorb_q(fake, fake, fake, 1, 64, 128, 512, 1.0, None) == binding.MLA_ERR_SHAPE
-    assert L.mla_absorb_q(fake, fake, fake, 1, 48, 256, 512, 1.0, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_absorb_q(fake, fake, fake, 1, 40, 256, 512, 1.0, None) == binding.MLA_ERR_SHAPE  # H % 16 != 0
     assert L.mla_absorb_q(fake, fake, fake, 0, 64, 256, 512, 1.0, None) == binding.MLA_ERR_SHAPE
     assert L.mla_absorb_q(fake, fake, fake, 1, 64, 256, 512, float("nan"), None) == binding.MLA_ERR_ARG
     assert L.mla_up_v(fake, None, fake, 1, 64, 256, 512, None) == binding.MLA_ERR_NULL
@@ -163,7 +163,7 @@ def test_fused_up_projection_host_validation(L):
     assert call(idx=fake) == binding.MLA_ERR_NULL          # idx without idx_len
     assert call(idx_len=fake) == binding.MLA_ERR_NULL      # idx_len without idx
     assert call(D=128) == binding.MLA_ERR_SHAPE
-    assert call(H=96) == binding.MLA_ERR_SHAPE
+    assert call(H=40) == binding.MLA_ERR_SHAPE  # not a multiple of 16
     assert call(scale=0.0) == binding.MLA_ERR_ARG
     assert call(st=512 * 99) == binding.MLA_ERR_ARG
     assert call(idx=fake, idx_len=fake, K=0) == binding.MLA_ERR_ARG
@@ -343,3 +343,14 @@ def test_naive_and_indexer_wrappers_check_every_extent(L):
     _expect(TypeError, binding.mla_indexer_select, **se)
     for b in (dict(cache_len=_i32(3)), dict(idx=_i32(2, 3, 11)), dict(idx_len=_i32(2, 3))):
         _expect(ValueError, binding.mla_indexer_select, **{**se, **b})
+
+
+def test_head_counts_multiple_of_16(L):
+    # H a multiple of 16: the attention kernels take heads in groups of 64, the last partial
+    for H in (16, 48, 80, 112):
+        s = binding.mla_latent_attn_num_splits(2, 1, H, 4096, 0)
+        assert s >= 1
+        assert binding.mla_latent_attn_workspace_size(2, 1, H, 512, 4096, 0) == (0 if s == 1 else s * 2 * H * 1032)
+    for H in (8, 24, 40, 72):
+        assert L.mla_latent_attn_num_splits(2, 1, H, 4096, 0, 0) == binding.MLA_ERR_SHAPE
+        assert L.mla_latent_attn_workspace_size(2, 1, H, 512, 4096, 0, 0) == 0

@@ -1,0 +1,81 @@
+"""Head counts that are multiples of 16 but not of 64 (GPU): the attention kernels take heads in
+groups of 64, and the last group of such a call is partial.
+
+* Latent attention (dense single-query, dense query pairs, odd Q, indexed; one split, the
+  automatic count, three splits) against the fp64 oracle's latent-space attention (page "Module 05
+  -- MLA: Compressing Per-Token History", section 3), with o_lat and lse written into views of
+  larger buffers whose tails hold a sentinel: nothing may be written past the last head's row.
+* The whole path (absorb, attention, up-projection) and the fused call: bit-equal to each other,
+  and sampled against the oracle's expanded form (sections 1 and 4).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_cache_absorb_amd import binding, workloads as wl
+from tests.gpu_util import DEV, assert_parity, bf16, i32
+
+pytestmark = pytest.mark.gpu
+
+F = oracle.bf16_bits_to_f64
+SENTINEL = 12345.0
+
+CASES = [
+    # (H, B, Q, L, n_index)
+    (16, 2, 1, 700, 0),
+    (48, 3, 1, 900, 0),
+    (80, 2, 2, 800, 0),    # query pairs, one full and one partial group
+    (112, 2, 3, 600, 0),   # odd Q
+    (48, 2, 2, 900, 200),  # indexed
+    (16, 1, 4, 300, 0),
+]
+
+
+def views_with_tail(shape, tail):
+    """A contiguous tensor of `shape` at the start of a larger buffer whose last `tail` values hold
+    the sentinel."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + tail,), SENTINEL, dtype=torch.float32, device=DEV)
+    return buf[:n].view(*shape), buf
+
+
+@pytest.mark.parametrize("H,B,Q,L,n_index", CASES)
+@pytest.mark.parametrize("splits", [1, 0, 3])
+def test_partial_head_group_matches_oracle(H, B, Q, L, n_index, splits):
+    spec = wl.make_spec(B, Q, L, min_cache_len=L // 2, n_index=n_index, heads=H, workload_id=2600 + H + Q + B)
+    w = wl.make_workload(spec)
+    qa = wl.latent_query_bits(spec)
+    print(f"H={H} B={B} Q={Q} L={L} indexed={n_index > 0} splits={splits}", flush=True)
+    o_lat, o_buf = views_with_tail((B, Q, H, 512), 64 * 512)
+    lse, l_buf = views_with_tail((B, Q, H), 64)
+    q_abs, c, cl = bf16(qa), bf16(w.cache), i32(w.cache_len)
+    if n_index:
+        binding.mla_latent_attn_indexed(q_abs, c, cl, i32(w.idx), i32(w.idx_len), L, w.scale, splits, o_lat=o_lat,
+                                        lse=lse)
+    else:
+        binding.mla_latent_attn(q_abs, c, cl, L, w.scale, splits, o_lat=o_lat, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((o_buf[o_lat.numel():] == SENTINEL).all()), "o_lat written past the last head's row"
+    assert bool((l_buf[lse.numel():] == SENTINEL).all()), "lse written past the last head's row"
+    ref, lse_ref = oracle.latent_attention(F(qa), w.cache, w.cache_len, w.scale, idx=w.idx, idx_len=w.idx_len)
+    assert_parity(o_lat.cpu().numpy(), ref, f"o_lat H{H}")
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=1e-3)
+
+
+@pytest.mark.parametrize("H,B,Q,L,n_index", CASES[:4])
+def test_partial_head_group_whole_path(H, B, Q, L, n_index):
+    spec = wl.make_spec(B, Q, L, min_cache_len=L // 2, n_index=n_index, heads=H, workload_id=2700 + H + Q + B)
+    w = wl.make_workload(spec)
+    q, c, wk, wv, cl = bf16(w.q), bf16(w.cache), bf16(w.w_k), bf16(w.w_v), i32(w.cache_len)
+    print(f"whole path H={H} B={B} Q={Q} L={L}", flush=True)
+    q_abs = binding.mla_absorb_q(q, wk)
+    o_lat, lse_s = binding.mla_latent_attn(q_abs, c, cl, L, w.scale, 0)
+    out_s = binding.mla_up_v(o_lat, wv)
+    out_f, lse_f = binding.mla_latent_attn_up_v(q_abs, c, cl, L, w.scale, wv)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f.view(torch.int32), out_s.view(torch.int32)), "fused and separate calls differ"
+    assert torch.equal(lse_f.view(torch.int32), lse_s.view(torch.int32))
+    hs = sorted({0, H // 2, H - 1})
+    ref, _ = oracle.mla_reference(w.q, w.cache, w.w_k, w.w_v, w.cache_len, w.scale, heads=hs)
+    assert_parity(out_f.cpu().numpy()[:, :, hs], ref, f"out H{H}")
