@@ -76,6 +76,38 @@ def read_traffic(workload: str):
         return None
 
 
+def chunked_ms(call, steps: int, stream=None, nchunk: int = 5):
+    """`steps` calls of call(k) launched back to back in `nchunk` chunks, an event between chunks
+    (an event does not stop the stream).  Returns (average over every call, per-call average of the
+    median chunk).  The first is the figure reported; the second, beside it, shows whether one
+    stall of the host or the device set it.  The collector is off meanwhile."""
+    import torch
+    nchunk = nchunk if steps >= 2 * nchunk else 1
+    sizes = [steps // nchunk + (1 if c < steps % nchunk else 0) for c in range(nchunk)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nchunk + 1)]
+    gc.collect()
+    gc.disable()
+    try:
+        if stream is None:
+            ev[0].record()
+        else:
+            ev[0].record(stream)
+        done = 0
+        for c in range(nchunk):
+            for k in range(sizes[c]):
+                call(done + k)
+            done += sizes[c]
+            if stream is None:
+                ev[c + 1].record()
+            else:
+                ev[c + 1].record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
+    chunk = sorted(ev[c].elapsed_time(ev[c + 1]) / sizes[c] for c in range(nchunk))
+    return ev[0].elapsed_time(ev[nchunk]) / steps, chunk[nchunk // 2]
+
+
 def visible_rows(w) -> int:
     """Latent rows the attention reads: every visible position of every query (dense), or every
     listed position (indexed).  Queries of one sequence share rows in the dense case."""
@@ -194,30 +226,15 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
         else:
             binding.mla_up_v(o_lat, d["w_v"], out=out)
 
-    stage, pct, stage_all = {}, {}, {}
+    stage, pct, stage_med = {}, {}, {}
     for k in ("absorb_q", "latent_attn_up_v", "latent_attn", "up_v"):
         if k.startswith("latent_attn"):
             for s in range(3):
                 one_stage(k, s)
             torch.cuda.synchronize()
-            # the calls launched back to back in five chunks, an event between chunks (which does not
-            # stop the stream): the per-call average is that of the median chunk, so that one stall
-            # of the host or the device during the run does not set the figure; the average over
-            # every call is kept beside it
-            nchunk = 5 if steps >= 10 else 1
-            sizes = [steps // nchunk + (1 if c < steps % nchunk else 0) for c in range(nchunk)]
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(nchunk + 1)]
-            ev[0].record(stream)
-            done = 0
-            for c in range(nchunk):
-                for s in range(sizes[c]):
-                    one_stage(k, done + s)
-                done += sizes[c]
-                ev[c + 1].record(stream)
-            torch.cuda.synchronize()
-            chunk = sorted(ev[c].elapsed_time(ev[c + 1]) / sizes[c] for c in range(nchunk))
-            stage[k] = chunk[nchunk // 2]
-            stage_all[k] = ev[0].elapsed_time(ev[nchunk]) / steps
+            # back to back: the average over every call, and beside it the median chunk's (chunked_ms)
+            stage[k], stage_med[k] = chunked_ms(lambda s: one_stage(k, s), steps, stream)
+            gc.disable()
             # the spread: each call between its own pair of events
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
             ev[0].record(stream)
@@ -244,8 +261,8 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
     gc.enable()
     del sets
     torch.cuda.empty_cache()
-    return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, stage_all_ms=stage_all, stage_pct_ms=pct, splits=splits,
-                workload=w0)
+    return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, stage_median_chunk_ms=stage_med, stage_pct_ms=pct,
+                splits=splits, workload=w0)
 
 
 def time_latency(name: str = "decode_b1_l256", samples: int = 200):
@@ -562,12 +579,12 @@ def time_crossover(reps: int = 3):
 QLEN_SWEEP = (16, 32768, (1, 2, 3, 4, 5, 6, 7, 8))   # batch, cache length, query counts
 
 
-def time_qlen_sweep(steps: int = 10, warmup: int = 20):
+def time_qlen_sweep(steps: int = 20, warmup: int = 20):
     """The latent attention (mla_latent_attn, split kernel + merge) at one to eight query
     positions per pass (draft depths 0..7) on 16 sequences of 32,768 positions.  Intensity is
     128 Q FLOP/B: HBM-bound at Q = 1 and 2, matrix-core-bound from Q = 3 on (the ridge is
-    2.5e15 / 8e12 = 312 FLOP/B).  Each depth is timed over `steps` back-to-back calls between
-    HIP events, two caches alternating.  Inputs: torch.randn on the GPU with the workloads'
+    2.5e15 / 8e12 = 312 FLOP/B).  Each depth is timed over `steps` back-to-back calls (the
+    median of five chunks, chunked_ms), two caches alternating.  Inputs: torch.randn on the GPU with the workloads'
     distributions (timing only)."""
     import torch
     from mla_latent_cache_absorb_amd import binding, workloads as wl
@@ -592,13 +609,7 @@ def time_qlen_sweep(steps: int = 10, warmup: int = 20):
         for k in range(warmup):
             call(k)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for k in range(steps):
-            call(k)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        ms, _ = chunked_ms(call, steps)
         visible = B * (Q * (L - Q) + Q * (Q + 1) // 2)
         flops = 4 * H * R * visible
         lat_bytes = B * L * R * 2
@@ -621,7 +632,7 @@ def time_other_configs(steps: int = 20, warmup: int = 20):
     uniform in [4096, 65536]) over 2,048 positions drawn per query from the committed prefix plus
     the causal tail.  Inputs are drawn on the GPU with those shapes and structures (timing only;
     the parity tests use the seeded CPU workloads).  Two input sets alternate; each call is timed
-    over `steps` back-to-back calls between HIP events."""
+    over `steps` back-to-back calls (the median of five chunks, chunked_ms)."""
     import torch
     from mla_latent_cache_absorb_amd import binding, workloads as wl
 
@@ -635,13 +646,7 @@ def time_other_configs(steps: int = 20, warmup: int = 20):
         for k in range(warmup):
             call(k % nsets)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for k in range(steps):
-            call(k % nsets)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+        return chunked_ms(lambda k: call(k % nsets), steps)
 
     # decode, 4 x 131072, spiked
     B, Q, L = 4, 1, 131072
@@ -658,11 +663,12 @@ def time_other_configs(steps: int = 20, warmup: int = 20):
     o = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
     ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, L, 0), 1), dtype=torch.uint8, device=dev)
-    ms = run(lambda k: binding.mla_latent_attn(sets[k][1], sets[k][0], cl, L, wl.SCALE, 0, o_lat=o, lse=lse,
-                                               workspace=ws), 2)
+    ms, ms_med = run(lambda k: binding.mla_latent_attn(sets[k][1], sets[k][0], cl, L, wl.SCALE, 0, o_lat=o, lse=lse,
+                                                       workspace=ws), 2)
     lat = B * L * R * 2
     gbs = lat / (ms * 1e-3) / 1e9
     out.append({"workload": "decode_b4_l131072_spiked", "call": "mla_latent_attn", "ms": round(ms, 5),
+                "median_chunk_ms": round(ms_med, 5),
                 "splits": binding.mla_latent_attn_num_splits(B, Q, H, L, 0), "latent_bytes": lat,
                 "GB/s": round(gbs, 2), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
     del sets, o, lse, ws
@@ -690,14 +696,15 @@ def time_other_configs(steps: int = 20, warmup: int = 20):
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
     ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, K, 0, indexed=True), 1),
                      dtype=torch.uint8, device=dev)
-    ms = run(lambda k: binding.mla_latent_attn_indexed(sets[k][1], sets[k][0], cl, idx, idx_len, Lmax, wl.SCALE, 0,
-                                                       o_lat=o, lse=lse, workspace=ws), 2)
+    ms, ms_med = run(lambda k: binding.mla_latent_attn_indexed(sets[k][1], sets[k][0], cl, idx, idx_len, Lmax,
+                                                               wl.SCALE, 0, o_lat=o, lse=lse, workspace=ws), 2)
     rows = int(idx_len.sum())
     lat = rows * R * 2
     flops = 4 * H * R * rows
     gbs = lat / (ms * 1e-3) / 1e9
     tf = flops / (ms * 1e-3) / 1e12
     out.append({"workload": "indexed_verify_b32_q4_ragged", "call": "mla_latent_attn_indexed", "ms": round(ms, 5),
+                "median_chunk_ms": round(ms_med, 5),
                 "splits": binding.mla_latent_attn_num_splits(B, Q, H, K, 0, indexed=True), "latent_bytes": lat,
                 "index_bytes": B * Q * K * 4, "GB/s": round(gbs, 2), "bound": "hbm",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOP/s": round(tf, 2),
@@ -852,11 +859,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic / (attn_ms * 1e-3) / 1e9, 2),
                      "algorithmic_bytes_per_launch": latent_bytes, "avg_launch_ms": round(attn_ms, 6),
-                     "avg_launch_ms_all_calls": round(r["stage_all_ms"]["latent_attn"], 6),
+                     "median_chunk_ms": round(r["stage_median_chunk_ms"]["latent_attn"], 6),
                      "launch_ms_p10_p50_p90": [round(x, 6) for x in r["stage_pct_ms"]["latent_attn"]]},
         "fused_attn_up_v": {"call": "mla_latent_attn_up_v (split kernel + merge fused into the up-projection)",
                             "avg_launch_ms": round(fused_ms, 6),
-                            "avg_launch_ms_all_calls": round(r["stage_all_ms"]["latent_attn_up_v"], 6),
+                            "median_chunk_ms": round(r["stage_median_chunk_ms"]["latent_attn_up_v"], 6),
                             "launch_ms_p10_p50_p90": [round(x, 6) for x in r["stage_pct_ms"]["latent_attn_up_v"]],
                             "algorithmic_bytes_per_launch": fused_bytes,
                             "achieved": round(fused_gbs, 2), "unit": "GB/s",

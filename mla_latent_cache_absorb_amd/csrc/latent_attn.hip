@@ -20,7 +20,10 @@
 // halves of the computation while either role waits on LDS, and no wave holds both the
 // query registers and the accumulators.  One latent row serves all 64 heads: the cache is read
 // once per (query, split); the queries of one split are placed on one XCD and share the tiles
-// through its L2.
+// through its L2.  With several splits, each workgroup ends by staging its normalised partial in
+// the idle tile ring and storing it as whole contiguous KiB (stage_value_rows,
+// copy_partial_block).  Head counts that are not a multiple of 64 leave the last group partial:
+// its missing heads reuse the last head's query and nothing of theirs is stored.
 //
 // Indexed calls gather the listed rows instead of a run of positions: each value wave stages its
 // rows' index slots in LDS ahead of use (copied like the tiles, so no load waits on memory inside
@@ -30,9 +33,10 @@
 // the same twelve waves take two adjacent queries over one run of tiles, so that each LDS read of
 // a tile feeds twice the matrix work (the single-query form is bound by its LDS traffic).
 //
-// The split partials (m, l, o) are merged by log-sum-exp (merge_splits): combine_kernel for up to
-// eight splits, combine_wide_kernel above that (one thread group per group of eight splits), or
-// the fused merge and up-projection of mla_latent_attn_up_v; all three give the same bits.
+// The split partials (m, l, u = o / l) are merged by log-sum-exp (merge_splits): combine_kernel
+// for up to eight splits, combine_wide_kernel above that (one thread group per group of eight
+// splits), or the fused merge and up-projection of mla_latent_attn_up_v; all three give the same
+// bits.
 #include "mla_device.h"
 #include "mla_internal.h"
 
