@@ -293,15 +293,10 @@ void latent_attn_kernel(AttnArgs a) {
         const int nvalid = s_end - base;
         uint32_t valid = nvalid >= kTile ? 0xffffffffu : ((1u << nvalid) - 1u);
         if constexpr (INDEXED) {
-          // row validity posted by the value waves when they copied this tile (two steps ago)
-          const uint32_t* vb = (const uint32_t*)vrow[t % kRing];
-#pragma unroll
-          for (int w = 0; w < kTile / 4; ++w) {
-            const uint32_t x = vb[w];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (((x >> (8 * j)) & 0xffu) == 0) valid &= ~(1u << (4 * w + j));
-          }
+          // row validity posted by the value waves when they copied this tile (two steps ago): lane
+          // l reads row l & 31's byte, and the wave's ballot is the tile's mask (bit r = row r)
+          const bool ok = vrow[t % kRing][lane & 31] != 0;
+          valid &= (uint32_t)__builtin_amdgcn_ballot_w64(ok);
         }
         if (valid != 0xffffffffu) {
 #pragma unroll
