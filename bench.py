@@ -80,12 +80,14 @@ def chunked_ms(call, steps: int, stream=None, nchunk: int = 5):
     """`steps` calls of call(k) launched back to back in `nchunk` chunks, an event between chunks
     (an event does not stop the stream).  Returns (average over every call, per-call average of the
     median chunk).  The first is the figure reported; the second, beside it, shows whether one
-    stall of the host or the device set it.  The collector is off meanwhile."""
+    stall of the host or the device set it.  The collector is off meanwhile; it is not run here:
+    the device would idle meanwhile and the timed calls would start below the steady clock (the
+    callers run it before their warm-up calls)."""
     import torch
     nchunk = nchunk if steps >= 2 * nchunk else 1
     sizes = [steps // nchunk + (1 if c < steps % nchunk else 0) for c in range(nchunk)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nchunk + 1)]
-    gc.collect()
+    was_enabled = gc.isenabled()
     gc.disable()
     try:
         if stream is None:
@@ -103,7 +105,8 @@ def chunked_ms(call, steps: int, stream=None, nchunk: int = 5):
                 ev[c + 1].record(stream)
         torch.cuda.synchronize()
     finally:
-        gc.enable()
+        if was_enabled:
+            gc.enable()
     chunk = sorted(ev[c].elapsed_time(ev[c + 1]) / sizes[c] for c in range(nchunk))
     return ev[0].elapsed_time(ev[nchunk]) / steps, chunk[nchunk // 2]
 
@@ -189,12 +192,14 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
         binding.mla_absorb_q(d["q"], d["w_k"], q_abs=q_abs)
         attn_up_v(d)
 
+    # no collector pauses inside the timed regions: it runs now, before the warm-up (run between the
+    # warm-up and the timing, it would leave the device idle and the first timed steps below the
+    # steady clock), and again after them
+    gc.collect()
+    gc.disable()
     for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
-    # no collector pauses inside the timed regions (it runs now, and again after them)
-    gc.collect()
-    gc.disable()
     # whole steps, back to back
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -234,7 +239,6 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
             torch.cuda.synchronize()
             # back to back: the average over every call, and beside it the median chunk's (chunked_ms)
             stage[k], stage_med[k] = chunked_ms(lambda s: one_stage(k, s), steps, stream)
-            gc.disable()
             # the spread: each call between its own pair of events
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
             ev[0].record(stream)
@@ -606,6 +610,7 @@ def time_qlen_sweep(steps: int = 20, warmup: int = 20):
                          device=dev)
         call = lambda k: binding.mla_latent_attn(q_abs, caches[k & 1], cl, L, wl.SCALE, 0, o_lat=o, lse=lse,
                                                  workspace=ws)
+        gc.collect()
         for k in range(warmup):
             call(k)
         torch.cuda.synchronize()
@@ -643,6 +648,7 @@ def time_other_configs(steps: int = 20, warmup: int = 20):
     out = []
 
     def run(call, nsets):
+        gc.collect()
         for k in range(warmup):
             call(k % nsets)
         torch.cuda.synchronize()
