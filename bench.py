@@ -76,6 +76,25 @@ def read_traffic(workload: str):
         return None
 
 
+def warm_up(call, min_calls: int, min_ms: float = 20.0) -> int:
+    """Untimed calls of call(k), in batches of at least `min_calls`, until about `min_ms` of wall
+    time has passed with the device busy: an idle device drops its clock, and work issued right
+    after an idle spell runs below the steady clock for a few milliseconds (a 4 x 131,072 decode
+    call measured 124-136 us after 20 warm-up calls against 112-117 us after 100).  The collector
+    runs first, before the device is busy.  Returns the number of calls made."""
+    import torch
+    gc.collect()
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        for _ in range(max(1, min_calls)):
+            call(k)
+            k += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            return k
+
+
 def chunked_ms(call, steps: int, stream=None, nchunk: int = 5):
     """`steps` calls of call(k) launched back to back in `nchunk` chunks, an event between chunks
     (an event does not stop the stream).  Returns (average over every call, per-call average of the
@@ -234,9 +253,7 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
     stage, pct, stage_med = {}, {}, {}
     for k in ("absorb_q", "latent_attn_up_v", "latent_attn", "up_v"):
         if k.startswith("latent_attn"):
-            for s in range(3):
-                one_stage(k, s)
-            torch.cuda.synchronize()
+            warm_up(lambda s: one_stage(k, s), 3)
             # back to back: the average over every call, and beside it the median chunk's (chunked_ms)
             stage[k], stage_med[k] = chunked_ms(lambda s: one_stage(k, s), steps, stream)
             # the spread: each call between its own pair of events
@@ -253,8 +270,7 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
         with torch.cuda.graph(graph):
             for s in range(steps):
                 one_stage(k, s)
-        graph.replay()  # once untimed
-        torch.cuda.synchronize()
+        warm_up(lambda s: graph.replay(), 1)  # untimed replays (the capture left the device idle)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         graph.replay()
@@ -353,9 +369,7 @@ def time_read_ceiling(mib: int = 256, nsets: int = 3, calls: int = 30):
     bufs = [torch.full((mib << 20,), s + 1, dtype=torch.uint8, device=dev) for s in range(nsets)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
-    for k in range(4 * nsets):
-        binding.mla_stream_read(bufs[k % nsets], sink)
-    torch.cuda.synchronize()
+    warm_up(lambda k: binding.mla_stream_read(bufs[k % nsets], sink), 4 * nsets)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for k in range(calls):
@@ -426,9 +440,7 @@ def time_indexer(name: str, steps: int, warmup: int):
         if ev is not None:
             ev[4].record(stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(lambda k: step(), warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for s in range(steps):
         step(evs[s])
@@ -484,9 +496,7 @@ def time_append(steps: int, warmup: int):
         L = 8192 if rows is None else rows
         cache = torch.zeros((B, L, wl.LATENT), dtype=torch.bfloat16, device=dev)
         cl = torch.full((B,), L, dtype=torch.int32, device=dev)
-        for _ in range(warmup):
-            binding.mla_latent_append(h, w, cache, cl, L)
-        torch.cuda.synchronize()
+        warm_up(lambda k: binding.mla_latent_append(h, w, cache, cl, L), warmup)
         # a call takes a few microseconds on the GPU, less than the Python call that launches it:
         # the timed calls are captured in a HIP graph and replayed, so the events see GPU time
         graph = torch.cuda.CUDAGraph()
@@ -610,10 +620,7 @@ def time_qlen_sweep(steps: int = 20, warmup: int = 20):
                          device=dev)
         call = lambda k: binding.mla_latent_attn(q_abs, caches[k & 1], cl, L, wl.SCALE, 0, o_lat=o, lse=lse,
                                                  workspace=ws)
-        gc.collect()
-        for k in range(warmup):
-            call(k)
-        torch.cuda.synchronize()
+        warm_up(call, warmup)
         ms, _ = chunked_ms(call, steps)
         visible = B * (Q * (L - Q) + Q * (Q + 1) // 2)
         flops = 4 * H * R * visible
@@ -648,10 +655,7 @@ def time_other_configs(steps: int = 20, warmup: int = 20):
     out = []
 
     def run(call, nsets):
-        gc.collect()
-        for k in range(warmup):
-            call(k % nsets)
-        torch.cuda.synchronize()
+        warm_up(lambda k: call(k % nsets), warmup)
         return chunked_ms(lambda k: call(k % nsets), steps)
 
     # decode, 4 x 131072, spiked
