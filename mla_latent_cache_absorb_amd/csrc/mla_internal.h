@@ -130,9 +130,8 @@ struct MergeUpArgs {
   const uint16_t* w_v;     // [H][D][R] bf16
   float* out;              // [rows][H][D] fp32
   float* lse;              // [rows][H] fp32 or null
-  int32_t rows_per_group, groups, total_wg;  // set by the launcher
+  int32_t rows_per_pass, passes, groups, total_wg;  // set by the launcher
 };
-int merge_up_v_rows_per_group(int rows, int H, int cus);
 hipError_t launch_merge_up_v(MergeUpArgs a, int cus, hipStream_t stream);
 
 // ---- device-side precondition check (bits of the flag word, as in the public header)

@@ -10,13 +10,13 @@
 // bits of o_lat.  Bound by reading U^V (16 MiB) at decode sizes.
 //
 // merge_up_v_kernel fuses the log-sum-exp merge of split-K attention partials into the same
-// product: a workgroup owns one head, all 256 output dims (sixteen waves of 16) and a group of
-// rows.  It merges its rows' partials straight into the hi / lo LDS staging, so the merged
-// latents never travel through HBM, and writes each row's log-sum-exp.  The groups of one head
-// run on one XCD and share U_h^V through its L2.  Half of U_h^V (latents 0..255) is copied
-// straight into LDS and half is held in registers; both copies are issued before the merge's
-// loads, so the whole workgroup has one memory round trip.  Its time is set by the bytes each CU
-// pulls in (256 KiB of U_h^V, the partials of its rows), not by HBM.
+// product: a workgroup owns one head, half of its 256 output dims (eight waves of 16, their U_h^V
+// rows in registers as above) and a group of up to 16 rows.  It merges its rows' partials straight
+// into the hi / lo LDS staging, so the merged latents never travel through HBM, and the half-0
+// workgroup writes each row's log-sum-exp.  The workgroups of one head run on one XCD.  Its time
+// is set by the bytes each CU pulls in, not by HBM: half of U_h^V (128 KiB) and the partials of 16
+// rows, 256 KiB at decode sizes, where one workgroup per (head, eight rows) covering all 256 dims
+// pulled 256 KiB of U_h^V and 64 KiB of partials.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -119,89 +119,169 @@ __global__ __launch_bounds__(kThreads) void up_v_kernel(const float* __restrict_
   }
 }
 
-constexpr int kFuseWaves = kHeadDim / 16;  // one wave per 16 output dims
+constexpr int kFuseWaves = 8;                // 16 output channels each: half of a head's 256
 constexpr int kFuseThreads = 64 * kFuseWaves;
-constexpr int kFuseMaxRows = 16;             // rows per group: the MFMA's 16 B columns
+constexpr int kFuseRows = 16;                // rows per group: the MFMA's 16 B columns
+constexpr int kFuseHalf = 16 * kFuseWaves;   // output channels per workgroup
+constexpr int kMaxFusePasses = 16;           // row passes per workgroup
 
+// The partials of two chunks of eight latents of one row when there are at most eight splits (one
+// group of merge slots): every slot loaded, slots past the last split reloading it, as in
+// merge_load8.  Held as loaded, so the next pass's loads can be in flight during this pass's
+// products.
+struct FuseRaw {
+  f16x8 v[2][8];
+  float2 ml[8];
+};
+
+__device__ __forceinline__ void fuse_load(FuseRaw& f, const uint16_t* po0, const uint16_t* po1, const float* pml,
+                                          size_t o_step, size_t ml_step, int S) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const size_t s = (size_t)min(k, S - 1);
+    f.ml[k] = *(const float2*)(pml + s * ml_step);
+    f.v[0][k] = *(const f16x8*)(po0 + s * o_step);
+    f.v[1][k] = *(const f16x8*)(po1 + s * o_step);
+  }
+}
+
+// merge_splits8's steps for each chunk of a FuseRaw (one group: a single merge_group and fold), so
+// the bits are those of merge_splits8 and merge_splits
+__device__ __forceinline__ void fuse_merge(const FuseRaw& f, int S, float* lse2, f32x4 (&out)[2][2]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    MergeGroup g[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        g[h].mm[k] = f.ml[k].x;
+        g[h].ll[k] = f.ml[k].y;
+        g[h].v[k] = __builtin_convertvector(
+            (f16x4){f.v[c][k][4 * h], f.v[c][k][4 * h + 1], f.v[c][k][4 * h + 2], f.v[c][k][4 * h + 3]}, f32x4);
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float M = -INFINITY, L = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      MergePartial r;
+      if (merge_group(g[h], S, 0, r)) merge_fold(M, L, acc, r);
+      // __builtin_amdgcn_logf is the hardware base-2 logarithm
+      if (c == 0 && h == 0) *lse2 = M + __builtin_amdgcn_logf(L);
+      out[c][h] = acc * (1.0f / L);
+    }
+  }
+}
+
+// AHEAD: passes of 16 rows and at most eight splits, the next pass's partials loaded during this
+// pass's products; otherwise the general merge, passes of 16 or 8 rows
+template <bool AHEAD>
 __global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t hi_t[kFuseMaxRows * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lo_t[kFuseMaxRows * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t wv_t[kHeadDim * kRowBytes / 2];  // U_h^V, latents 0..255
+  // two staging buffers: pass p writes buffer p & 1, so one barrier a pass suffices
+  __shared__ __attribute__((aligned(1024))) uint8_t hi_t[2][kFuseRows * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lo_t[2][kFuseRows * kRowBytes];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wg = xcd_remap(blockIdx.x, a.total_wg);
-  const int h = wg / a.groups;  // the groups of one head are adjacent: one XCD, one L2 copy of U_h^V
-  const int row0 = (wg % a.groups) * a.rows_per_group;
-  const int d0 = 16 * wave;
+  // logical order (head, row group, half): the workgroups of one head are adjacent, on one XCD,
+  // and the two halves of a row group read the same partials through its L2
+  const int half = wg & 1;
+  const int grp = (wg >> 1) % a.groups;
+  const int h = (wg >> 1) / a.groups;
+  const int rpp = a.rows_per_pass;
+  const int row0 = grp * rpp * a.passes;
+  const int d0 = half * kFuseHalf + 16 * wave;
   const int ql = lane & 15, g = lane >> 4;
-  const uint16_t* wh = a.w_v + ((size_t)h * kHeadDim + d0) * kLatent;
 
-  // U_h^V rows d0 .. d0+15 of this wave, latents 0..255, copied to LDS 1 KiB per instruction
-  // (two half rows); slot p of local row r holds the 16-byte chunk p ^ (r & 15), so that the
-  // operand reads below (16 rows at one chunk) fall in sixteen different bank groups
+  // A operand: U_h^V row d0 + ql, latents 32s + 8g .. +7, in registers for the whole kernel
+  bf16x8 wa[16];
+  {
+    const uint16_t* wrow = a.w_v + ((size_t)h * kHeadDim + d0 + ql) * kLatent + 8 * g;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 2 * j + (lane >> 5), p = lane & 31;
-    copy16_to_lds(wh + (size_t)r * kLatent + 8 * (p ^ (r & 15)), lds_addr(wv_t + (d0 + 2 * j) * (kRowBytes / 2)));
+    for (int s = 0; s < 16; ++s) wa[s] = *(const bf16x8*)(wrow + 32 * s);
   }
-  // latents 256..511 as the A operand in registers: row d0 + ql, latents 256 + 32s + 8g .. +7
-  bf16x8 wa[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) wa[s] = *(const bf16x8*)(wh + (size_t)ql * kLatent + 256 + 32 * s + 8 * g);
 
-  // merge: task = (row r of the group, latents 4t .. 4t+3), 128 tasks per row
-  const size_t prow_count = (size_t)a.rows * a.H;  // partial rows per split
-  for (int task = threadIdx.x; task < kFuseMaxRows * 128; task += kFuseThreads) {
-    const int r = task >> 7, t = task & 127;
-    const int row = row0 + r;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (r < a.rows_per_group && row < a.rows) {
-      const size_t prow = (size_t)row * a.H + h;
-      float lse2;
-      x = merge_splits(a.part_o + prow * kLatent + 4 * t, a.part_ml + 2 * prow, prow_count * kLatent,
-                       2 * prow_count, a.num_splits, &lse2);
-      if (a.lse != nullptr && t == 0) a.lse[prow] = lse2 * 0.69314718055994531f;
-    }
-    s16x4 vh, vl;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const __bf16 bh = (__bf16)x[e];
-      vh[e] = __builtin_bit_cast(short, bh);
-      vl[e] = __builtin_bit_cast(short, (__bf16)(x[e] - (float)bh));
-    }
-    const int off = r * kRowBytes + 16 * up_slot(r, t >> 1) + 8 * (t & 1);
-    *(s16x4*)(hi_t + off) = vh;
-    *(s16x4*)(lo_t + off) = vl;
-  }
-  wait_vmcnt<0>();  // the U^V copies have landed
-  __syncthreads();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const uint8_t* wrow = wv_t + (d0 + ql) * (kRowBytes / 2);
-  // operands read from LDS kAhead k-steps ahead of the products that use them
-  constexpr int kAhead = 4;
-  bf16x8 ow[kAhead + 1], oh[kAhead + 1], ol[kAhead + 1];
-  auto rd = [&](int s, int slot) {
-    if (s < 8) ow[slot] = *(const bf16x8*)(wrow + 16 * ((4 * s + g) ^ ql));
-    const int off = ql * kRowBytes + 16 * up_slot(ql, 4 * s + g);
-    oh[slot] = *(const bf16x8*)(hi_t + off);
-    ol[slot] = *(const bf16x8*)(lo_t + off);
+  // merge: with 16 rows a pass, thread t takes row t / 32 and its chunks of eight latents c and
+  // c + 32 (c = t % 32); with 8 rows a pass (a single pass), row t / 64 and chunk t % 64.  With 16
+  // rows and at most eight splits the loads of the next pass are issued before this pass's
+  // products (rows past the end reload the last row; their results are dropped).
+  const size_t prows = (size_t)a.rows * a.H;  // partial rows per split
+  const size_t o_step = prows * kLatent, ml_step = 2 * prows;
+  const bool two = AHEAD || rpp == kFuseRows;
+  const int r = two ? threadIdx.x >> 5 : threadIdx.x >> 6;
+  const int c = two ? threadIdx.x & 31 : threadIdx.x & 63;
+  FuseRaw f;
+  auto issue = [&](int p) {
+    const size_t prow = (size_t)min(row0 + p * rpp + r, a.rows - 1) * a.H + h;
+    const uint16_t* po = a.part_o + prow * kLatent;
+    fuse_load(f, po + 8 * c, po + 8 * (c + 32), a.part_ml + 2 * prow, o_step, ml_step, a.num_splits);
   };
+  if constexpr (AHEAD) issue(0);
+
+  for (int p = 0; p < a.passes; ++p) {
+    const int prow0 = row0 + p * rpp;
+    if (prow0 >= a.rows) break;  // the same for the whole workgroup
+    const int row = prow0 + r;
+    const size_t prow = (size_t)row * a.H + h;
+    f32x4 x[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+    float lse2 = 0.f;
+    if constexpr (AHEAD) {
+      fuse_merge(f, a.num_splits, &lse2, x);
+      __builtin_amdgcn_sched_barrier(0);  // this pass's partials consumed before the next ones land
+      if (p + 1 < a.passes) issue(p + 1);
+    } else if (row < a.rows) {  // the general merge
+      const uint16_t* po = a.part_o + prow * kLatent;
+      const float* pml = a.part_ml + 2 * prow;
+      merge_splits8(po + 8 * c, pml, o_step, ml_step, a.num_splits, &lse2, x[0]);
+      if (two) {
+        float unused;
+        merge_splits8(po + 8 * (c + 32), pml, o_step, ml_step, a.num_splits, &unused, x[1]);
+      }
+    }
+    if (row < a.rows && a.lse != nullptr && half == 0 && c == 0) a.lse[prow] = lse2 * 0.69314718055994531f;
+    // the merged latents as hi / lo bf16 terms; chunk cc of row r at slot cc ^ (r & 15); rows
+    // past the end are zero
+    uint8_t* hb = hi_t[p & 1];
+    uint8_t* lb = lo_t[p & 1];
 #pragma unroll
-  for (int s = 0; s < kAhead; ++s) rd(s, s);
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1 && !two) break;
+      bf16x8 vh, vl;
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    if (s + kAhead < 16) rd(s + kAhead, (s + kAhead) % (kAhead + 1));
-    const int k = s % (kAhead + 1);
-    const bf16x8 w = s < 8 ? ow[k] : wa[s - 8];
-    __builtin_amdgcn_sched_barrier(0);
-    acc = mfma16x16(w, oh[k], acc);
-    acc = mfma16x16(w, ol[k], acc);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < 8; ++e) {
+        const float v = row < a.rows ? x[k][e >> 2][e & 3] : 0.f;
+        const __bf16 bh = (__bf16)v;
+        vh[e] = bh;
+        vl[e] = (__bf16)(v - (float)bh);
+      }
+      const int off = r * kRowBytes + 16 * up_slot(r, c + 32 * k);  // k = 1 only with c < 32
+      *(bf16x8*)(hb + off) = vh;
+      *(bf16x8*)(lb + off) = vl;
+    }
+    __syncthreads();
+    // the operands read from LDS in two halves of eight k-steps (registers hold the next pass's
+    // partials meanwhile)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s0 = 0; s0 < 16; s0 += 8) {
+      bf16x8 bh[8], bl[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int off = ql * kRowBytes + 16 * up_slot(ql, 4 * (s0 + s) + g);
+        bh[s] = *(const bf16x8*)(hb + off);
+        bl[s] = *(const bf16x8*)(lb + off);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        acc = mfma16x16(wa[s0 + s], bh[s], acc);
+        acc = mfma16x16(wa[s0 + s], bl[s], acc);
+      }
+    }
+    // lane holds row prow0 + ql, output dims d0 + 4g .. +3 (with 8 rows a pass, rows 8..15 of the
+    // staging were not written: those columns are dropped)
+    const int orow = prow0 + ql;
+    if (orow < a.rows && ql < rpp) *(f32x4*)(a.out + ((size_t)orow * a.H + h) * kHeadDim + d0 + 4 * g) = acc;
   }
-  // lane holds row row0 + ql, output dims d0 + 4g .. +3
-  const int row = row0 + ql;
-  if (ql < a.rows_per_group && row < a.rows)
-    *(f32x4*)(a.out + ((size_t)row * a.H + h) * kHeadDim + d0 + 4 * g) = acc;
 }
 
 }  // namespace
@@ -214,19 +294,27 @@ hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int 
   return hipLaunchKernel((const void*)&up_v_kernel, grid, block, args, 0, stream);
 }
 
-int merge_up_v_rows_per_group(int rows, int H, int cus) {
-  // the largest group (at most 16 rows) that still gives every CU a workgroup
-  int rg = kFuseMaxRows;
-  while (rg > 4 && (int64_t)H * ((rows + rg - 1) / rg) < cus) rg >>= 1;
-  return rg;
-}
-
 hipError_t launch_merge_up_v(MergeUpArgs a, int cus, hipStream_t stream) {
-  a.rows_per_group = merge_up_v_rows_per_group(a.rows, a.H, cus);
-  a.groups = (a.rows + a.rows_per_group - 1) / a.rows_per_group;
-  a.total_wg = a.H * a.groups;
+  // passes of 16 rows, spread evenly over just enough row groups to give every CU a workgroup
+  // (each pass after the first reuses the U_h^V half in registers); passes of 8 rows, one each,
+  // where a single pass of 16 would already leave CUs idle
+  const int p16 = (a.rows + kFuseRows - 1) / kFuseRows;
+  if (2 * a.H * p16 >= cus) {
+    const int want = (cus + 2 * a.H - 1) / (2 * a.H);  // row groups that fill the CUs
+    const int n = (p16 + want - 1) / want;
+    a.rows_per_pass = kFuseRows;
+    a.passes = n < kMaxFusePasses ? n : kMaxFusePasses;
+  } else {
+    a.rows_per_pass = kFuseRows / 2;
+    a.passes = 1;
+  }
+  const int per = a.rows_per_pass * a.passes;
+  a.groups = (a.rows + per - 1) / per;
+  a.total_wg = a.H * a.groups * 2;
   void* args[] = {(void*)&a};
-  return hipLaunchKernel((const void*)&merge_up_v_kernel, dim3(a.total_wg), dim3(kFuseThreads), args, 0, stream);
+  const void* fn = a.rows_per_pass == kFuseRows && a.num_splits <= 8 ? (const void*)&merge_up_v_kernel<true>
+                                                                      : (const void*)&merge_up_v_kernel<false>;
+  return hipLaunchKernel(fn, dim3(a.total_wg), dim3(kFuseThreads), args, 0, stream);
 }
 
 }  // namespace mla

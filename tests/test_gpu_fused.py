@@ -45,15 +45,19 @@ def assert_same_bits(a, b, what):
 
 
 CASES = [
-    # (B, Q, L, min_len, n_index, heads, splits)  rows = B*Q; 64 heads give groups of 16 / 8 / 4
-    (10, 5, 300, 120, 0, 64, 4),    # 50 rows: groups of 16, last holds 2
-    (32, 1, 500, 200, 0, 64, 0),    # 32 rows: groups of 8, automatic split count
-    (5, 1, 900, 300, 0, 64, 7),     # 5 rows: groups of 4, last holds 1
+    # (B, Q, L, min_len, n_index, heads, splits)  rows = B*Q; the merge takes rows in passes of 16,
+    # spread over just enough row groups to fill the CUs, or in single passes of 8 where one pass
+    # of 16 would already leave CUs idle (64 heads: 16 rows or fewer)
+    (10, 5, 300, 120, 0, 64, 4),    # 50 rows: two groups of two passes, the last pass holds 2
+    (32, 1, 500, 200, 0, 64, 0),    # 32 rows: two groups of one pass, automatic split count
+    (5, 1, 900, 300, 0, 64, 7),     # 5 rows: one pass of 8 holding 5
     (3, 6, 700, 200, 0, 64, 1),     # one split: no merge
     (2, 4, 600, 300, 100, 64, 3),   # indexed
     (2, 3, 400, 150, 0, 128, 2),    # two head groups
     (2, 2, 333, 100, 0, 192, 0),    # three head groups, a length bound that is not a whole tile
     (3, 2, 1500, 600, 0, 64, 12),   # more than eight splits: the wide merge, one round of groups
+    (9, 2, 1500, 600, 0, 64, 10),   # 18 rows in passes of 16, more than eight splits
+    (16, 4, 1500, 600, 0, 64, 9),   # 64 rows: two passes a group with the general merge
     (2, 1, 5000, 4000, 0, 64, 70),  # nine groups of splits: two rounds of the wide merge
 ]
 
