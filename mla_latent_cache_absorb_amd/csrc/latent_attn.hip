@@ -33,7 +33,7 @@
 // the same twelve waves take two adjacent queries over one run of tiles, so that each LDS read of
 // a tile feeds twice the matrix work (the single-query form is bound by its LDS traffic).
 //
-// The split partials (m, l, u = o / l) are merged by log-sum-exp (merge_splits): combine_kernel
+// The split partials (m, l, u = o / l) are merged by log-sum-exp (merge_splits8): combine_kernel
 // for up to eight splits, combine_wide_kernel above that (one thread group per group of eight
 // splits), or the fused merge and up-projection of mla_latent_attn_up_v; all three give the same
 // bits.
@@ -715,7 +715,9 @@ void latent_attn_pair_kernel(AttnArgs a) {
 
 // Merge of the split partials (up to eight splits): four (b, i, head) rows per workgroup of 256
 // threads, 64 threads per row, thread t owning latents 8t .. 8t+7 (16-byte loads, 32-byte stores).
+// NS split slots loaded (merge_slots).
 constexpr int kCombineRows = 4;
+template <int NS>
 __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(AttnArgs a) {
   const size_t rows = (size_t)a.B * a.Q * a.H;
   const size_t row = (size_t)blockIdx.x * kCombineRows + (threadIdx.x >> 6);
@@ -723,8 +725,8 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(AttnArgs a) 
   const int t = threadIdx.x & 63;
   float lse2;
   f32x4 o[2];
-  merge_splits8(a.part_o + row * kLatent + 8 * t, a.part_ml + 2 * row, rows * kLatent, 2 * rows, a.num_splits, &lse2,
-                o);
+  merge_splits8<NS>(a.part_o + row * kLatent + 8 * t, a.part_ml + 2 * row, rows * kLatent, 2 * rows, a.num_splits,
+                    &lse2, o);
   float* dst = a.o_lat + row * kLatent + 8 * t;
   *(f32x4*)dst = o[0];
   *(f32x4*)(dst + 4) = o[1];
@@ -734,7 +736,7 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(AttnArgs a) 
 // Merge of more than eight splits: G = min(8, groups of eight splits) thread groups of 64 per
 // (b, i, head), thread t owning latents 8t .. 8t+7.  Thread group q reduces group r0 + q of a round
 // of G groups, all the round's loads in flight together, and thread group 0 folds the round's
-// results in group order (the order merge_splits uses, so the bits are the same): one memory round
+// results in group order (the order merge_splits8 uses, so the bits are the same): one memory round
 // trip per G groups instead of one per group.
 __global__ __launch_bounds__(512) void combine_wide_kernel(AttnArgs a) {
   __shared__ f32x4 gacc[8][2][64];
@@ -800,7 +802,11 @@ hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
     return hipLaunchKernel((const void*)&combine_wide_kernel, grid, block, args, 0, stream);
   }
   const dim3 cgrid((unsigned)(((size_t)a.B * a.Q * a.H + kCombineRows - 1) / kCombineRows));
-  return hipLaunchKernel((const void*)&combine_kernel, cgrid, dim3(64 * kCombineRows), args, 0, stream);
+  const int ns = merge_slots(a.num_splits);
+  const void* k = ns == 2 ? (const void*)&combine_kernel<2>
+                  : ns == 4 ? (const void*)&combine_kernel<4>
+                            : (const void*)&combine_kernel<8>;
+  return hipLaunchKernel(k, cgrid, dim3(64 * kCombineRows), args, 0, stream);
 }
 
 }  // namespace mla

@@ -171,8 +171,8 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // on its own, relative to its own maximum Mg (splits that saw no position, l = 0, weigh nothing),
 // and the group results are then folded in order into a running (M, L, o), rescaling what was
 // accumulated by 2^(M_old - M_new) and the group by 2^(Mg - M_new).  The sequential form below
-// and the wide merge kernel (groups reduced by different threads, folded in the same order) give
-// identical bits.  With one group the fold multiplies by one and adds zero, so it is exact.
+// (merge_splits8) and the wide merge kernel (groups reduced by different threads, folded in the
+// same order) give identical bits.  With one group the fold multiplies by one and adds zero, so it is exact.
 struct MergeGroup {
   float mm[8], ll[8];
   f32x4 v[8];
@@ -182,21 +182,43 @@ struct MergePartial {
   f32x4 acc;
 };
 
-// part_o: the row's four latents (of this thread, fp16) in split 0; part_ml: the row's (m, l) in
-// split 0; split s lies o_step (ml_step) elements further on
-// Every slot is loaded, unconditionally, so that the group's loads all issue before the first
-// one is waited for (one memory round trip; a conditional load per slot makes the compiler wait
-// before each branch).  A slot past the last split reloads the last split (in bounds, a cache
-// hit); merge_group weighs such slots by zero, as it does a split that saw no position.
-__device__ __forceinline__ void merge_load(MergeGroup& g, const uint16_t* part_o, const float* part_ml, size_t o_step,
-                                           size_t ml_step, int S, int s0) {
+// A slot past the last split weighs nothing: merge_group's condition skips it in the maximum, and
+// its weight is zero in the sums.  Its values only have to be finite; with them zero the sums take
+// exactly the same values as with any other finite values (an accumulator that starts at +0 and
+// gains a +0 or -0 term stays +0 under round-to-nearest, and a nonzero one is unchanged).
+__device__ __forceinline__ void merge_slot_empty(MergeGroup& g, int k) {
+  g.mm[k] = 0.f;
+  g.ll[k] = 0.f;
+  g.v[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
+// The partials of one group of splits, s0 .. s0 + 7, for eight adjacent latents (two blocks of
+// four): part_o holds the row's eight latents (of this thread, fp16) in split 0 and part_ml the
+// row's (m, l) in split 0; split s lies o_step (ml_step) elements further on.  NS (2, 4 or 8)
+// slots are loaded, unconditionally, so that the group's loads all issue before the first one is
+// waited for (one memory round trip; a conditional load per slot makes the compiler wait before
+// each branch).  Callers pick NS >= the splits left (NS < 8 only with a single group); a loaded
+// slot past the last split reloads the last split (in bounds, a cache hit), the others are filled
+// by merge_slot_empty.
+template <int NS = 8>
+__device__ __forceinline__ void merge_load8(MergeGroup (&g)[2], const uint16_t* part_o, const float* part_ml,
+                                            size_t o_step, size_t ml_step, int S, int s0) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
+    if (k >= NS) {
+      merge_slot_empty(g[0], k);
+      merge_slot_empty(g[1], k);
+      continue;
+    }
     const size_t s = (size_t)min(s0 + k, S - 1);
     const float2 ml = *(const float2*)(part_ml + s * ml_step);
-    g.mm[k] = ml.x;
-    g.ll[k] = ml.y;
-    g.v[k] = __builtin_convertvector(*(const f16x4*)(part_o + s * o_step), f32x4);
+    const f16x8 x = *(const f16x8*)(part_o + s * o_step);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      g[h].mm[k] = ml.x;
+      g[h].ll[k] = ml.y;
+      g[h].v[k] = __builtin_convertvector((f16x4){x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]}, f32x4);
+    }
   }
 }
 
@@ -235,48 +257,16 @@ __device__ __forceinline__ void merge_fold(float& M, float& L, f32x4& acc, const
   M = Mn;
 }
 
-// the whole merge for the four latents a thread owns; *lse2 = M + log2(L) (log2 units)
-__device__ __forceinline__ f32x4 merge_splits(const uint16_t* part_o, const float* part_ml, size_t o_step,
-                                              size_t ml_step, int S, float* lse2) {
-  float M = -INFINITY, L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    MergeGroup g;
-    merge_load(g, part_o, part_ml, o_step, ml_step, S, s0);
-    MergePartial r;
-    if (merge_group(g, S, s0, r)) merge_fold(M, L, acc, r);
-  }
-  // __builtin_amdgcn_logf is the hardware base-2 logarithm
-  *lse2 = M + __builtin_amdgcn_logf(L);
-  return acc * (1.0f / L);
-}
-
-// merge_load for eight adjacent latents: two blocks of four, one 16-byte load per split slot
-__device__ __forceinline__ void merge_load8(MergeGroup (&g)[2], const uint16_t* part_o, const float* part_ml,
-                                            size_t o_step, size_t ml_step, int S, int s0) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {  // every slot loaded, as in merge_load
-    const size_t s = (size_t)min(s0 + k, S - 1);
-    const float2 ml = *(const float2*)(part_ml + s * ml_step);
-    const f16x8 x = *(const f16x8*)(part_o + s * o_step);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      g[h].mm[k] = ml.x;
-      g[h].ll[k] = ml.y;
-      g[h].v[k] = __builtin_convertvector((f16x4){x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]}, f32x4);
-    }
-  }
-}
-
-// merge_splits for eight adjacent latents (two blocks of four): each block goes through the same
-// steps as in merge_splits, so the bits are the same
+// The whole merge for the eight latents a thread owns, as two blocks of four, each through its
+// own (M, L, o): *lse2 = M + log2(L) (log2 units).  NS as in merge_load8.
+template <int NS = 8>
 __device__ __forceinline__ void merge_splits8(const uint16_t* part_o, const float* part_ml, size_t o_step,
                                               size_t ml_step, int S, float* lse2, f32x4 (&out)[2]) {
   float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
   f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   for (int s0 = 0; s0 < S; s0 += 8) {
     MergeGroup g[2];
-    merge_load8(g, part_o, part_ml, o_step, ml_step, S, s0);
+    merge_load8<NS>(g, part_o, part_ml, o_step, ml_step, S, s0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       MergePartial r;
@@ -288,6 +278,9 @@ __device__ __forceinline__ void merge_splits8(const uint16_t* part_o, const floa
 #pragma unroll
   for (int h = 0; h < 2; ++h) out[h] = acc[h] * (1.0f / L[h]);
 }
+
+// merge slots to load for S splits in one group (2, 4 or 8)
+__host__ __device__ constexpr int merge_slots(int S) { return S <= 2 ? 2 : S <= 4 ? 4 : 8; }
 
 // Map the hardware workgroup id to a logical id so that consecutive logical ids run on the
 // same XCD: workgroups are dispatched round-robin over the 8 XCDs of an MI355X, so XCD x

@@ -126,18 +126,19 @@ constexpr int kFuseHalf = 16 * kFuseWaves;   // output channels per workgroup
 constexpr int kMaxFusePasses = 16;           // row passes per workgroup
 
 // The partials of two chunks of eight latents of one row when there are at most eight splits (one
-// group of merge slots): every slot loaded, slots past the last split reloading it, as in
-// merge_load8.  Held as loaded, so the next pass's loads can be in flight during this pass's
-// products.
+// group of merge slots): NS slots loaded as in merge_load8, slots past the last split reloading it.
+// Held as loaded, so the next pass's loads can be in flight during this pass's products.
+template <int NS>
 struct FuseRaw {
-  f16x8 v[2][8];
-  float2 ml[8];
+  f16x8 v[2][NS];
+  float2 ml[NS];
 };
 
-__device__ __forceinline__ void fuse_load(FuseRaw& f, const uint16_t* po0, const uint16_t* po1, const float* pml,
+template <int NS>
+__device__ __forceinline__ void fuse_load(FuseRaw<NS>& f, const uint16_t* po0, const uint16_t* po1, const float* pml,
                                           size_t o_step, size_t ml_step, int S) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < NS; ++k) {
     const size_t s = (size_t)min(k, S - 1);
     f.ml[k] = *(const float2*)(pml + s * ml_step);
     f.v[0][k] = *(const f16x8*)(po0 + s * o_step);
@@ -145,9 +146,10 @@ __device__ __forceinline__ void fuse_load(FuseRaw& f, const uint16_t* po0, const
   }
 }
 
-// merge_splits8's steps for each chunk of a FuseRaw (one group: a single merge_group and fold), so
-// the bits are those of merge_splits8 and merge_splits
-__device__ __forceinline__ void fuse_merge(const FuseRaw& f, int S, float* lse2, f32x4 (&out)[2][2]) {
+// merge_splits8's steps for each chunk of a FuseRaw (one group: a single merge_group and fold, the
+// slots not loaded filled as in merge_load8), so the bits are those of merge_splits8
+template <int NS>
+__device__ __forceinline__ void fuse_merge(const FuseRaw<NS>& f, int S, float* lse2, f32x4 (&out)[2][2]) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     MergeGroup g[2];
@@ -155,6 +157,10 @@ __device__ __forceinline__ void fuse_merge(const FuseRaw& f, int S, float* lse2,
     for (int k = 0; k < 8; ++k)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        if (k >= NS) {
+          merge_slot_empty(g[h], k);
+          continue;
+        }
         g[h].mm[k] = f.ml[k].x;
         g[h].ll[k] = f.ml[k].y;
         g[h].v[k] = __builtin_convertvector(
@@ -174,8 +180,9 @@ __device__ __forceinline__ void fuse_merge(const FuseRaw& f, int S, float* lse2,
 }
 
 // AHEAD: passes of 16 rows and at most eight splits, the next pass's partials loaded during this
-// pass's products; otherwise the general merge, passes of 16 or 8 rows
-template <bool AHEAD>
+// pass's products; otherwise the general merge, passes of 16 or 8 rows.  NS split slots loaded
+// (merge_slots).
+template <bool AHEAD, int NS>
 __global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a) {
   // two staging buffers: pass p writes buffer p & 1, so one barrier a pass suffices
   __shared__ __attribute__((aligned(1024))) uint8_t hi_t[2][kFuseRows * kRowBytes];
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a)
   const bool two = AHEAD || rpp == kFuseRows;
   const int r = two ? threadIdx.x >> 5 : threadIdx.x >> 6;
   const int c = two ? threadIdx.x & 31 : threadIdx.x & 63;
-  FuseRaw f;
+  FuseRaw<NS> f;
   auto issue = [&](int p) {
     const size_t prow = (size_t)min(row0 + p * rpp + r, a.rows - 1) * a.H + h;
     const uint16_t* po = a.part_o + prow * kLatent;
@@ -232,10 +239,10 @@ __global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a)
     } else if (row < a.rows) {  // the general merge
       const uint16_t* po = a.part_o + prow * kLatent;
       const float* pml = a.part_ml + 2 * prow;
-      merge_splits8(po + 8 * c, pml, o_step, ml_step, a.num_splits, &lse2, x[0]);
+      merge_splits8<NS>(po + 8 * c, pml, o_step, ml_step, a.num_splits, &lse2, x[0]);
       if (two) {
         float unused;
-        merge_splits8(po + 8 * (c + 32), pml, o_step, ml_step, a.num_splits, &unused, x[1]);
+        merge_splits8<NS>(po + 8 * (c + 32), pml, o_step, ml_step, a.num_splits, &unused, x[1]);
       }
     }
     if (row < a.rows && a.lse != nullptr && half == 0 && c == 0) a.lse[prow] = lse2 * 0.69314718055994531f;
@@ -312,8 +319,14 @@ hipError_t launch_merge_up_v(MergeUpArgs a, int cus, hipStream_t stream) {
   a.groups = (a.rows + per - 1) / per;
   a.total_wg = a.H * a.groups * 2;
   void* args[] = {(void*)&a};
-  const void* fn = a.rows_per_pass == kFuseRows && a.num_splits <= 8 ? (const void*)&merge_up_v_kernel<true>
-                                                                      : (const void*)&merge_up_v_kernel<false>;
+  const bool ahead = a.rows_per_pass == kFuseRows && a.num_splits <= 8;
+  const int ns = merge_slots(a.num_splits);
+  const void* fn = ahead ? (ns == 2   ? (const void*)&merge_up_v_kernel<true, 2>
+                            : ns == 4 ? (const void*)&merge_up_v_kernel<true, 4>
+                                      : (const void*)&merge_up_v_kernel<true, 8>)
+                         : (ns == 2   ? (const void*)&merge_up_v_kernel<false, 2>
+                            : ns == 4 ? (const void*)&merge_up_v_kernel<false, 4>
+                                      : (const void*)&merge_up_v_kernel<false, 8>);
   return hipLaunchKernel(fn, dim3(a.total_wg), dim3(kFuseThreads), args, 0, stream);
 }
 
