@@ -395,7 +395,50 @@ def time_read_ceiling(mib: int = 256, nsets: int = 3, calls: int = 30):
     torch.cuda.empty_cache()
     return {"kernel": "stream_read_kernel", "bytes_per_call": nbytes, "buffers_rotated": nsets,
             "avg_launch_ms": round(avg, 6), "GB/s": gbs(avg), "frac_of_peak": round(gbs(avg) / HBM_PEAK_GBS, 4),
-            "single_call_ms_p10_p50_p90": [round(per[int(f * (calls - 1) + 0.5)], 6) for f in (0.1, 0.5, 0.9)]}
+            "single_call_ms_p10_p50_p90": [round(per[int(f * (calls - 1) + 0.5)], 6) for f in (0.1, 0.5, 0.9)],
+            "small_reads": time_small_reads()}
+
+
+def time_small_reads(sizes_mib=(16, 32), rotate_mib: int = 384):
+    """The floor for a kernel that pulls one weight matrix from HBM: plain streaming reads
+    (mla_stream_read) of 16 and 32 MiB, captured back to back in one graph and replayed, over
+    enough buffers (`rotate_mib` in all) that none is still in the 256 MB Infinity Cache when it
+    is read again ("cold"), and of one buffer read again and again ("warm": served by the caches).
+    16 MiB is the size of W_k or W_v at 64 heads; the absorption reads W_k, the fused merge and
+    up-projection W_v and as much again of split partials at decode."""
+    import torch
+    from mla_latent_cache_absorb_amd import binding
+
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = []
+    for mib in sizes_mib:
+        nsets = max(2, -(-rotate_mib // mib))
+        bufs = [torch.full((mib << 20,), s + 1, dtype=torch.uint8, device=dev) for s in range(nsets)]
+        res = {"MiB": mib}
+        for kind, n, pick in (("cold", nsets, lambda k: bufs[k % nsets]), ("warm", 40, lambda k: bufs[0])):
+            g = torch.cuda.CUDAGraph()
+            binding.mla_stream_read(pick(0), sink)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for k in range(n):
+                    binding.mla_stream_read(pick(k), sink)
+            warm_up(lambda k: g.replay(), 2)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / (reps * n) * 1e3
+            res[f"{kind}_us"] = round(us, 3)
+            res[f"{kind}_GB/s"] = round((mib << 20) / (us * 1e-6) / 1e9, 1)
+            del g
+        out.append(res)
+        del bufs
+        torch.cuda.empty_cache()
+    return out
 
 
 def time_indexer(name: str, steps: int, warmup: int):
