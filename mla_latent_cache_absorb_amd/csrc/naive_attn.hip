@@ -5,7 +5,8 @@
 //
 // expand_kv_kernel   one GEMM per operand: [positions x 512] latents times the [H*D x 512]
 //                    weights (U_h stored [D][R] per head, so row h*D + d is U_h[d][:]), fp32
-//                    accumulation, nearest-even bf16 out.  Keys are written position-major,
+//                    accumulation, nearest-even bf16 out; 256 x 256 tiles, three stages of 32
+//                    latents in flight.  Keys are written position-major,
 //                    K[b][j][h][d]; values head-major and transposed, V^T[b][h][d][j], so that the
 //                    attention's value product reads them along positions.
 // naive_attn_kernel  flash attention with head dimension 256: per (sequence, head, 128 queries),
@@ -18,22 +19,32 @@ namespace mla {
 namespace {
 
 // ---------------------------------------------------------------------------------- expansion
-constexpr int kExpTile = 128;                    // positions and channels per workgroup
-constexpr int kExpK = 64;                        // latents per stage
-constexpr int kExpStages = kLatent / kExpK;      // 8
-constexpr int kExpRowBytes = kExpK * 2;          // 128 bytes: 8 chunks of 16
-constexpr int kExpTileBytes = kExpTile * kExpRowBytes;
+// A workgroup computes a 256 x 256 tile (channels h * D + d by positions) over the 512 latents in
+// 16 stages of 32, eight waves of 64 channels x 128 positions (2 x 4 MFMA 32x32x16 blocks).  The
+// stages pass through a ring of four LDS buffers, three in flight, so the products of one stage
+// run while the next ones are on their way (with one stage in flight the workgroup waited on
+// memory for every stage).
+constexpr int kExpTile = 256;                    // channels and positions per workgroup
+constexpr int kExpK = 32;                        // latents per stage
+constexpr int kExpStages = kLatent / kExpK;      // 16
+constexpr int kExpRing = 4;                      // stage buffers; three stages in flight
+constexpr int kExpRowBytes = kExpK * 2;          // 64 bytes: 4 chunks of 16
+constexpr int kExpTileBytes = kExpTile * kExpRowBytes;  // 16 KiB per operand
+constexpr int kExpCopies = 2 * kExpTileBytes / 1024 / 8;  // copy instructions per wave per stage (4)
+constexpr int kExpOutRows = kExpTile / 2;        // output rows staged per half
+constexpr int kExpOutStride = 2 * kExpTile + 16;  // bytes per staged output row
+static_assert(kExpOutRows * kExpOutStride <= kExpRing * 2 * kExpTileBytes, "output staged in the ring");
 
-// chunk c of tile row r sits at slot c ^ ((r >> 1) & 7): sixteen consecutive rows at one chunk
-// (an MFMA operand read) then fall in sixteen different 16-byte bank groups
-__device__ __forceinline__ int row128_swz(int r) { return (r >> 1) & 7; }
+// chunk c of tile row r sits at slot c ^ ((r >> 2) & 3): the sixteen rows read by one quarter of
+// an MFMA operand read (64-byte rows, four per 256 bytes) then fall in sixteen different 16-byte
+// bank groups
+__device__ __forceinline__ int row64_swz(int r) { return (r >> 2) & 3; }
 
-// VT = false: D[channel][position], each lane holds 4 consecutive channels of one position (keys,
-// position-major rows).  VT = true: D[position][channel], 4 consecutive positions of one channel
-// (values, transposed).
+// VT = false: keys, K[b][position][h * D + d], each output row a position.  VT = true: values
+// transposed, V^T[b][h * D + d][position], each output row a channel.
 template <bool VT>
-__global__ __launch_bounds__(256) void expand_kv_kernel(ExpandArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kExpTileBytes];  // [buffer][W, latents]
+__global__ __launch_bounds__(512) void expand_kv_kernel(ExpandArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kExpRing][2][kExpTileBytes];  // [stage][W, latents]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * kExpTile;          // weight rows (h*D + d)
@@ -44,96 +55,133 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(ExpandArgs a) {
   const uint16_t* w = (VT ? a.w_v : a.w_k) + (size_t)n0 * kLatent;
   const uint8_t* c = a.cache + (size_t)b * a.cache_bstride_bytes;
 
-  // each copy instruction moves 8 rows x 128 bytes; wave w moves rows 32w .. 32w+31 of both tiles
-  auto issue = [&](int st, int buf) {
+  // one copy instruction moves 16 rows x 64 bytes of one operand; wave v moves rows 32v .. 32v+31
+  // of both (lane l: row 16j + l / 4, slot l % 4, holding chunk (l % 4) ^ swz(row))
+  auto issue = [&](int st) {
     const int kb = st * kExpRowBytes;
+    uint8_t* buf = &lds[st % kExpRing][0][0];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = wave * 4 + u;
-      const int r = 8 * j + (lane >> 3);
-      const int chunk = (lane & 7) ^ row128_swz(r);
-      copy16_to_lds((const uint8_t*)(w + (size_t)r * kLatent) + kb + 16 * chunk, lds_addr(&lds[buf][0][1024 * j]));
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * wave + u;
+      const int r = 16 * j + (lane >> 2);
+      const int chunk = (lane & 3) ^ row64_swz(r);
+      copy16_to_lds((const uint8_t*)(w + (size_t)r * kLatent) + kb + 16 * chunk, lds_addr(buf + 1024 * j));
       const int pr = min(m0 + r, L - 1);
-      copy16_to_lds(c + (size_t)pr * kRowBytes + kb + 16 * chunk, lds_addr(&lds[buf][1][1024 * j]));
+      copy16_to_lds(c + (size_t)pr * kRowBytes + kb + 16 * chunk, lds_addr(buf + kExpTileBytes + 1024 * j));
     }
   };
+  static_assert(kExpCopies == 4, "two rows of copies per operand per wave");
 
-  const int wm = wave & 1, wn = wave >> 1;       // this wave: positions 64wm.., channels 64wn..
+  const int wn = wave & 3, wm = wave >> 2;       // this wave: channels 64wn .., positions 128wm ..
   const int r32 = lane & 31, kg = lane >> 5;
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];                              // [channel block][position block]
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < 4; ++y)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
 
-  issue(0, 0);
-  for (int st = 0; st < kExpStages; ++st) {
-    const int buf = st & 1;
-    wait_vmcnt<0>();
-    __syncthreads();  // stage st landed for every wave; every wave is done reading the other buffer
-    if (st + 1 < kExpStages) issue(st + 1, buf ^ 1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // k-steps of 16 latents: chunk 2s + kg
+  for (int st = 0; st < kExpRing - 1; ++st) issue(st);
+  for (int st = 0; st < kExpStages; ++st) {
+    // stage st has landed; the stages after it may stay in flight
+    if (st + 2 < kExpStages) wait_vmcnt<2 * kExpCopies>();
+    else if (st + 1 < kExpStages) wait_vmcnt<kExpCopies>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // stage st is in LDS for every wave; every wave is done with stage st - 1
+    if (st + kExpRing - 1 < kExpStages) issue(st + kExpRing - 1);  // into the buffer of stage st - 1
+    const uint8_t* wt = &lds[st % kExpRing][0][0];
+    const uint8_t* ct = &lds[st % kExpRing][1][0];
+#pragma unroll
+    for (int s = 0; s < kExpK / 16; ++s) {  // k-steps of 16 latents: chunk 2s + kg
       const int chunk = 2 * s + kg;
-      bf16x8 fw[2], fc[2];
+      bf16x8 fw[2], fc[4];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int rw = 64 * wn + 32 * x + r32;
-        const int rc = 64 * wm + 32 * x + r32;
-        fw[x] = *(const bf16x8*)&lds[buf][0][rw * kExpRowBytes + 16 * (chunk ^ row128_swz(rw))];
-        fc[x] = *(const bf16x8*)&lds[buf][1][rc * kExpRowBytes + 16 * (chunk ^ row128_swz(rc))];
+        fw[x] = *(const bf16x8*)(wt + rw * kExpRowBytes + 16 * (chunk ^ row64_swz(rw)));
+      }
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int rc = 128 * wm + 32 * y + r32;
+        fc[y] = *(const bf16x8*)(ct + rc * kExpRowBytes + 16 * (chunk ^ row64_swz(rc)));
       }
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
+        for (int y = 0; y < 4; ++y) {
           if constexpr (VT)
-            acc[x][y] = mfma32(fc[x], fw[y], acc[x][y]);  // [positions x][channels y]
+            acc[x][y] = mfma32(fc[y], fw[x], acc[x][y]);  // [positions][channels]
           else
-            acc[x][y] = mfma32(fw[x], fc[y], acc[x][y]);  // [channels x][positions y]
+            acc[x][y] = mfma32(fw[x], fc[y], acc[x][y]);  // [channels][positions]
         }
     }
   }
 
-  // D lane layout: column lane & 31, rows 8i + 4kg + j
+  // The tile leaves through LDS, half of its output rows at a time.  Every output row (a position
+  // of the keys, a channel of the transposed values) holds 256 values, 512 contiguous bytes in
+  // memory, written by 32 lanes with 16-byte stores; written straight from the accumulators, each
+  // store would put 8 bytes into each of 32 rows 16-32 KiB apart.  Staged rows are kExpOutStride
+  // bytes apart, so that the 8-byte writes of consecutive rows spread over the banks.
+  uint8_t* stage = &lds[0][0][0];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // every wave is done reading the ring, or the previous half is written out
+    // D lane layout: column lane & 31, rows 8i + 4kg + j.  VT: output rows are channels 64wn +
+    // 32x + r32, the lane's four values positions 128wm + 32y + 8i + 4kg ..; otherwise output rows
+    // are positions 128wm + 32y + r32 and the values channels 64wn + 32x + 8i + 4kg ..
+    const bool mine = VT ? (wn >> 1) == half : wm == half;
+    if (mine) {
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc[x][y][4 * i]) |
-                            ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * i + 1]) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc[x][y][4 * i + 2]) |
-                            ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * i + 3]) << 16);
-        const uint2 v = {lo, hi};
-        if constexpr (VT) {
-          // rows: positions 64wm + 32x + 8i + 4kg + j; column: channel 64wn + 32y + r32
-          const int m = m0 + 64 * wm + 32 * x + 8 * i + 4 * kg;
-          const int n = n0 + 64 * wn + 32 * y + r32;
-          const int h = n / kHeadDim, d = n % kHeadDim;
-          uint16_t* dst = a.v_out + (size_t)b * a.vt_bstride + ((size_t)h * kHeadDim + d) * a.vt_len + m;
-          // positions from L up to the next multiple of 64 get zeros: the attention reads whole
-          // 64-position spans and multiplies them by zero weights, which must not meet a NaN
-          const int pad_end = min((L + 63) & ~63, a.vt_len);
-          if (m + 3 < L) {
-            *(uint2*)dst = v;
-          } else if (m < pad_end) {
-            const uint64_t keep = m >= L ? 0ull : (~0ull >> (16 * (4 - (L - m))));
-            const uint64_t w64 = ((uint64_t)hi << 32 | lo) & keep;
-            *(uint2*)dst = uint2{(uint32_t)w64, (uint32_t)(w64 >> 32)};
+        for (int y = 0; y < 4; ++y)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc[x][y][4 * i]) |
+                                ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * i + 1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc[x][y][4 * i + 2]) |
+                                ((uint32_t)f32_to_bf16_bits(acc[x][y][4 * i + 3]) << 16);
+            const int row = VT ? 64 * wn + 32 * x + r32 : 128 * wm + 32 * y + r32;
+            const int col = VT ? 128 * wm + 32 * y + 8 * i + 4 * kg : 64 * wn + 32 * x + 8 * i + 4 * kg;
+            *(uint2*)(stage + (row - kExpOutRows * half) * kExpOutStride + 2 * col) = uint2{lo, hi};
           }
-        } else {
-          const int n = n0 + 64 * wn + 32 * x + 8 * i + 4 * kg;
-          const int m = m0 + 64 * wm + 32 * y + r32;
-          if (m < L) *(uint2*)(a.k_out + (size_t)b * a.k_bstride + (size_t)m * a.HD + n) = v;
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < kExpOutRows * 32; q += 512) {
+      const int row = q >> 5, ch = q & 31;
+      const int orow = kExpOutRows * half + row;
+      uint4 v = *(const uint4*)(stage + row * kExpOutStride + 16 * ch);
+      if constexpr (VT) {
+        // channel n0 + orow (= h * D + d), positions m .. m+7; positions from L up to the next
+        // multiple of 64 get zeros: the attention reads whole 64-position spans and multiplies
+        // them by zero weights, which must not meet a NaN
+        const int m = m0 + 8 * ch;
+        const int pad_end = min((L + 63) & ~63, a.vt_len);
+        uint16_t* dst = a.v_out + (size_t)b * a.vt_bstride + (size_t)(n0 + orow) * a.vt_len + m;
+        if (m + 7 < L) {
+          *(uint4*)dst = v;
+        } else if (m < pad_end) {
+          uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (m + e >= L) wd[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          *(uint4*)dst = uint4{wd[0], wd[1], wd[2], wd[3]};
         }
+      } else {
+        const int m = m0 + orow;
+        if (m < L) *(uint4*)(a.k_out + (size_t)b * a.k_bstride + (size_t)m * a.HD + n0 + 8 * ch) = v;
       }
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------ attention
+// chunk c of a 128-byte tile row r sits at slot c ^ ((r >> 1) & 7): sixteen consecutive rows at
+// one chunk (an MFMA operand read) then fall in sixteen different 16-byte bank groups
+__device__ __forceinline__ int row128_swz(int r) { return (r >> 1) & 7; }
+
 constexpr int kNaWaves = 8;
 constexpr int kNaQ = 16 * kNaWaves;        // queries per workgroup
 constexpr int kNaKeys = 64;                // keys per tile
@@ -302,7 +350,7 @@ __global__ __launch_bounds__(64 * kNaWaves) void naive_attn_kernel(NaiveArgs a) 
 
 hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<ExpandArgs*>(&a)};
-  const dim3 grid(a.HD / kExpTile, (a.max_cache_len + kExpTile - 1) / kExpTile, a.B), block(256);
+  const dim3 grid(a.HD / kExpTile, (a.max_cache_len + kExpTile - 1) / kExpTile, a.B), block(512);
   hipError_t e = hipLaunchKernel((const void*)&expand_kv_kernel<false>, grid, block, args, 0, stream);
   if (e != hipSuccess) return e;
   return hipLaunchKernel((const void*)&expand_kv_kernel<true>, grid, block, args, 0, stream);

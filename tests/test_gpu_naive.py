@@ -46,7 +46,7 @@ def expand(w, lens, Lmax):
     return k, vt
 
 
-@pytest.mark.parametrize("lens,Lmax", [([200, 77], 256), ([64, 1], 130), ([384], 384)])
+@pytest.mark.parametrize("lens,Lmax", [([200, 77], 256), ([64, 1], 130), ([384], 384), ([700, 513], 720)])
 def test_expansion_rounded_and_padded(lens, Lmax):
     spec = wl.make_spec(len(lens), 1, Lmax, workload_id=720 + Lmax)
     w = wl.make_workload(spec)
