@@ -279,6 +279,21 @@ __device__ __forceinline__ void merge_splits8(const uint16_t* part_o, const floa
   for (int h = 0; h < 2; ++h) out[h] = acc[h] * (1.0f / L[h]);
 }
 
+// merge_splits8's steps for one group of slots already loaded (at most eight splits), so the bits
+// are those of merge_splits8
+__device__ __forceinline__ void merge_one_group8(const MergeGroup (&g)[2], int S, float* lse2, f32x4 (&out)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    MergePartial r;
+    if (merge_group(g[h], S, 0, r)) merge_fold(M, L, acc, r);
+    // __builtin_amdgcn_logf is the hardware base-2 logarithm
+    if (h == 0) *lse2 = M + __builtin_amdgcn_logf(L);
+    out[h] = acc * (1.0f / L);
+  }
+}
+
 // merge slots to load for S splits in one group (2, 4 or 8)
 __host__ __device__ constexpr int merge_slots(int S) { return S <= 2 ? 2 : S <= 4 ? 4 : 8; }
 

@@ -146,8 +146,8 @@ __device__ __forceinline__ void fuse_load(FuseRaw<NS>& f, const uint16_t* po0, c
   }
 }
 
-// merge_splits8's steps for each chunk of a FuseRaw (one group: a single merge_group and fold, the
-// slots not loaded filled as in merge_load8), so the bits are those of merge_splits8
+// merge_splits8's steps for each chunk of a FuseRaw (one group, merge_one_group8; the slots not
+// loaded filled as in merge_load8), so the bits are those of merge_splits8
 template <int NS>
 __device__ __forceinline__ void fuse_merge(const FuseRaw<NS>& f, int S, float* lse2, f32x4 (&out)[2][2]) {
 #pragma unroll
@@ -166,16 +166,9 @@ __device__ __forceinline__ void fuse_merge(const FuseRaw<NS>& f, int S, float* l
         g[h].v[k] = __builtin_convertvector(
             (f16x4){f.v[c][k][4 * h], f.v[c][k][4 * h + 1], f.v[c][k][4 * h + 2], f.v[c][k][4 * h + 3]}, f32x4);
       }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float M = -INFINITY, L = 0.f;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      MergePartial r;
-      if (merge_group(g[h], S, 0, r)) merge_fold(M, L, acc, r);
-      // __builtin_amdgcn_logf is the hardware base-2 logarithm
-      if (c == 0 && h == 0) *lse2 = M + __builtin_amdgcn_logf(L);
-      out[c][h] = acc * (1.0f / L);
-    }
+    float chunk_lse2;  // the same for both chunks (it depends only on the splits' (m, l))
+    merge_one_group8(g, S, &chunk_lse2, out[c]);
+    if (c == 0) *lse2 = chunk_lse2;
   }
 }
 
