@@ -60,6 +60,8 @@ CASES = [
     (16, 4, 1500, 600, 0, 64, 9),   # 64 rows: two passes a group with the general merge
     (2, 1, 5000, 4000, 0, 64, 70),  # nine groups of splits: two rounds of the wide merge
     (64, 4, 300, 100, 0, 16, 3),    # 16 heads, 256 rows: eight groups of two passes
+    (9, 2, 700, 300, 0, 64, 2),     # two splits (two merge slots loaded), passes of 16 with loads ahead
+    (3, 1, 500, 200, 0, 64, 2),     # two splits, one pass of 8 rows: the general merge
     (16, 5, 400, 150, 0, 48, 5),    # 48 heads, 80 rows: three groups of two passes, the last group one
 ]
 
