@@ -200,7 +200,7 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
     if (s > 1 && mla::launch_combine(a, st) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
   }
-  if (s == 1) return mla::launch_up_v(a.o_lat, w_v, out, B * Q, H, st) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  if (s == 1) return mla::launch_up_v(a.o_lat, w_v, out, B * Q, H, cus, st) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   mla::MergeUpArgs m{};
   m.part_o = a.part_o;
   m.part_ml = a.part_ml;
@@ -421,9 +421,10 @@ int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, 
              void* stream) {
   if (!o_lat || !w_v || !out) return MLA_ERR_NULL;
   if (!supported(H, D, R) || rows < 1 || (int64_t)rows * H > 0x7fffffff) return MLA_ERR_SHAPE;
-  const int dst = check_device(nullptr);
+  int cus = 0;
+  const int dst = check_device(&cus);
   if (dst != MLA_OK) return dst;
-  if (mla::launch_up_v(o_lat, w_v, out, rows, H, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  if (mla::launch_up_v(o_lat, w_v, out, rows, H, cus, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
 

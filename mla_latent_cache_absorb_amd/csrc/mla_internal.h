@@ -118,11 +118,13 @@ hipError_t launch_naive_attn(const NaiveArgs& a, hipStream_t stream);
 
 hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int rows, int H,
                            float prescale, hipStream_t stream);
-hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H,
+hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H, int cus,
                        hipStream_t stream);
 
-// split-K partials merged straight into the up-projection
+// the up-projection's arguments: the latents given (o_lat), or split-K partials merged straight
+// into it (o_lat null)
 struct MergeUpArgs {
+  const float* o_lat;      // [rows][H][R] fp32, or null
   const uint16_t* part_o;  // [S][rows][H][R] fp16 bits: normalised partials o / l
   const float* part_ml;    // [S][rows][H][2] fp32 (running max in log2 units, sum)
   int32_t num_splits;

@@ -2,33 +2,27 @@
 // Per-Token History", section 3: U_h^V does not depend on the position, so it factors out of
 // the weighted sum and the accumulated latent is expanded once).
 //
-// Per head, out^T[D x rows] = U_h^V[D x R] . o_lat^T[R x rows].  A workgroup owns one head and 64
-// output dims, four waves of 16.  U^V rows are the A operand, loaded straight into registers (16
-// dims x 512 latents per wave, 64 VGPRs) and kept for every row.  The fp32 latents of 32 rows are
-// staged once per workgroup in LDS, each split into two bf16 terms (hi = bf16(x), lo = bf16(x -
-// hi)), and read as the B operand of two MFMA 16x16x32 per k-step, so the result keeps about 16
-// bits of o_lat.  Bound by reading U^V (16 MiB) at decode sizes.
+// Per head, out^T[D x rows] = U_h^V[D x R] . o_lat^T[R x rows].  One kernel, up_v_kernel, serves
+// both uses: the up-projection of given fp32 latents (mla_up_v, and the fused call with one
+// split), and the fused merge of split-K attention partials (mla_latent_attn_up_v), whose merged
+// latents never travel through HBM.
 //
-// merge_up_v_kernel fuses the log-sum-exp merge of split-K attention partials into the same
-// product: a workgroup owns one head, half of its 256 output dims (eight waves of 16, their U_h^V
-// rows in registers as above) and a group of up to 16 rows.  It merges its rows' partials straight
-// into the hi / lo LDS staging, so the merged latents never travel through HBM, and the half-0
-// workgroup writes each row's log-sum-exp.  The workgroups of one head run on one XCD.  Its time
-// is set by the bytes each CU pulls in, not by HBM: half of U_h^V (128 KiB) and the partials of 16
-// rows, 256 KiB at decode sizes, where one workgroup per (head, eight rows) covering all 256 dims
-// pulled 256 KiB of U_h^V and 64 KiB of partials.
+// A workgroup owns one head, half of its 256 output dims (eight waves of 16) and a group of rows.
+// U^V rows are the MFMA A operand, loaded straight into registers (16 dims x 512 latents per wave,
+// 64 VGPRs) and kept for every row of the group.  Rows are taken in passes of 16 (the MFMA's 16 B
+// columns), spread over just enough row groups to give every CU a workgroup; each pass's latents
+// (given, or merged from the partials, the merging workgroup of half 0 also writing each row's
+// log-sum-exp) are staged in LDS as two bf16 terms (hi = bf16(x), lo = bf16(x - hi)) and read as
+// the B operand of two MFMA 16x16x32 per k-step, so the result keeps about 16 bits of the latent.
+// The next pass's loads are issued before this pass's products.  The workgroups of one head run
+// on one XCD.  The time is set by the bytes each CU pulls in, not by HBM: half of U_h^V (128 KiB)
+// and the latents or partials of its rows.
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
 
 namespace {
-
-constexpr int kDBlock = 64;           // output dims per workgroup (16 per wave)
-constexpr int kUpWaves = 4;
-constexpr int kThreads = 64 * kUpWaves;
-constexpr int kUpRows = 32;           // o_lat rows staged per pass
-constexpr int kMaxRowGroups = 32;
 
 __device__ __forceinline__ f32x4 mfma16x16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -37,87 +31,6 @@ __device__ __forceinline__ f32x4 mfma16x16(const bf16x8& a, const bf16x8& b, con
 // LDS rows of 512 bf16 (64 chunks of 16 bytes); chunk c of row r at slot c ^ (r & 15), so the
 // B-operand reads (16 consecutive rows at one chunk) fall in sixteen different bank groups
 __device__ __forceinline__ int up_slot(int r, int c) { return c ^ (r & 15); }
-
-__global__ __launch_bounds__(kThreads) void up_v_kernel(const float* __restrict__ o_lat,
-                                                        const uint16_t* __restrict__ w_v,
-                                                        float* __restrict__ out, int rows, int H) {
-  __shared__ __attribute__((aligned(1024))) uint8_t hi_t[kUpRows * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lo_t[kUpRows * kRowBytes];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int ndb = kHeadDim / kDBlock;
-  const int h = blockIdx.x / ndb;
-  const int d0 = (blockIdx.x % ndb) * kDBlock + 16 * wave;
-  const int ql = lane & 15, g = lane >> 4;
-
-  // A operand: U_h^V row d0 + ql, latents 32s + 8g .. +7
-  bf16x8 wa[16];
-  {
-    const uint16_t* wrow = w_v + ((size_t)h * kHeadDim + d0 + ql) * kLatent + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) wa[s] = *(const bf16x8*)(wrow + 32 * s);
-  }
-
-  const int npass = (rows + kUpRows - 1) / kUpRows;
-  for (int pass = blockIdx.y; pass < npass; pass += gridDim.y) {
-    const int row0 = pass * kUpRows;
-    __syncthreads();  // the previous pass's reads are done
-    // stage rows row0 .. row0+31: task t = 8 consecutive latents (chunk t % 64) of row t / 64.
-    // Every load is issued before any is used (rows past the end reload the last row and are
-    // zeroed after), so the staging is one memory round trip.
-    constexpr int kTasks = kUpRows * 64 / kThreads;
-    f32x4 xs[kTasks][2];
-#pragma unroll
-    for (int k = 0; k < kTasks; ++k) {
-      const int task = threadIdx.x + kThreads * k;
-      const int row = min(row0 + (task >> 6), rows - 1);
-      const float* src = o_lat + ((size_t)row * H + h) * kLatent + 8 * (task & 63);
-      xs[k][0] = *(const f32x4*)src;
-      xs[k][1] = *(const f32x4*)(src + 4);
-    }
-#pragma unroll
-    for (int k = 0; k < kTasks; ++k) {
-      const int task = threadIdx.x + kThreads * k;
-      const int r = task >> 6, c = task & 63;
-      f32x4 x0 = xs[k][0], x1 = xs[k][1];
-      if (row0 + r >= rows) x0 = x1 = (f32x4){0.f, 0.f, 0.f, 0.f};
-      bf16x8 vh, vl;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = e < 4 ? x0[e] : x1[e - 4];
-        const __bf16 bh = (__bf16)x;
-        vh[e] = bh;
-        vl[e] = (__bf16)(x - (float)bh);
-      }
-      const int off = r * kRowBytes + 16 * up_slot(r, c);
-      *(bf16x8*)(hi_t + off) = vh;
-      *(bf16x8*)(lo_t + off) = vl;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < kUpRows / 16; ++rb) {
-      const int r = 16 * rb + ql;
-      // every operand of the block read from LDS before the first product (one LDS round trip)
-      bf16x8 bh[16], bl[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int off = r * kRowBytes + 16 * up_slot(r, 4 * s + g);
-        bh[s] = *(const bf16x8*)(hi_t + off);
-        bl[s] = *(const bf16x8*)(lo_t + off);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        acc = mfma16x16(wa[s], bh[s], acc);
-        acc = mfma16x16(wa[s], bl[s], acc);
-      }
-      // lane holds row row0 + r, output dims d0 + 4g .. +3
-      const int row = row0 + r;
-      if (row < rows) *(f32x4*)(out + ((size_t)row * H + h) * kHeadDim + d0 + 4 * g) = acc;
-    }
-  }
-}
 
 constexpr int kFuseWaves = 8;                // 16 output channels each: half of a head's 256
 constexpr int kFuseThreads = 64 * kFuseWaves;
@@ -172,11 +85,12 @@ __device__ __forceinline__ void fuse_merge(const FuseRaw<NS>& f, int S, float* l
   }
 }
 
-// AHEAD: passes of 16 rows and at most eight splits, the next pass's partials loaded during this
-// pass's products; otherwise the general merge, passes of 16 or 8 rows.  NS split slots loaded
-// (merge_slots).
-template <bool AHEAD, int NS>
-__global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a) {
+// LATENTS: the rows' fp32 latents are given (o_lat); otherwise they are merged from split-K
+// partials.  AHEAD: passes of 16 rows (with partials, at most eight splits), the next pass's loads
+// issued before this pass's products; otherwise passes of 16 or 8 rows, each loaded when it starts
+// (with partials, the general merge).  NS split slots loaded (merge_slots).
+template <bool LATENTS, bool AHEAD, int NS>
+__global__ __launch_bounds__(kFuseThreads) void up_v_kernel(MergeUpArgs a) {
   // two staging buffers: pass p writes buffer p & 1, so one barrier a pass suffices
   __shared__ __attribute__((aligned(1024))) uint8_t hi_t[2][kFuseRows * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lo_t[2][kFuseRows * kRowBytes];
@@ -201,20 +115,29 @@ __global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a)
     for (int s = 0; s < 16; ++s) wa[s] = *(const bf16x8*)(wrow + 32 * s);
   }
 
-  // merge: with 16 rows a pass, thread t takes row t / 32 and its chunks of eight latents c and
-  // c + 32 (c = t % 32); with 8 rows a pass (a single pass), row t / 64 and chunk t % 64.  With 16
-  // rows and at most eight splits the loads of the next pass are issued before this pass's
-  // products (rows past the end reload the last row; their results are dropped).
+  // with 16 rows a pass, thread t takes row t / 32 and its chunks of eight latents c and c + 32
+  // (c = t % 32); with 8 rows a pass (a single pass), row t / 64 and chunk t % 64.  Loads issued
+  // ahead for rows past the end reload the last row; their results are dropped.
   const size_t prows = (size_t)a.rows * a.H;  // partial rows per split
   const size_t o_step = prows * kLatent, ml_step = 2 * prows;
   const bool two = AHEAD || rpp == kFuseRows;
   const int r = two ? threadIdx.x >> 5 : threadIdx.x >> 6;
   const int c = two ? threadIdx.x & 31 : threadIdx.x & 63;
-  FuseRaw<NS> f;
+  FuseRaw<NS> f;        // partials of the next pass
+  f32x4 fl[2][2];       // latents of the next pass
   auto issue = [&](int p) {
     const size_t prow = (size_t)min(row0 + p * rpp + r, a.rows - 1) * a.H + h;
-    const uint16_t* po = a.part_o + prow * kLatent;
-    fuse_load(f, po + 8 * c, po + 8 * (c + 32), a.part_ml + 2 * prow, o_step, ml_step, a.num_splits);
+    if constexpr (LATENTS) {
+      const float* src = a.o_lat + prow * kLatent + 8 * c;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        fl[k][0] = *(const f32x4*)(src + 256 * k);
+        fl[k][1] = *(const f32x4*)(src + 256 * k + 4);
+      }
+    } else {
+      const uint16_t* po = a.part_o + prow * kLatent;
+      fuse_load(f, po + 8 * c, po + 8 * (c + 32), a.part_ml + 2 * prow, o_step, ml_step, a.num_splits);
+    }
   };
   if constexpr (AHEAD) issue(0);
 
@@ -226,9 +149,25 @@ __global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a)
     f32x4 x[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
     float lse2 = 0.f;
     if constexpr (AHEAD) {
-      fuse_merge(f, a.num_splits, &lse2, x);
-      __builtin_amdgcn_sched_barrier(0);  // this pass's partials consumed before the next ones land
+      if constexpr (LATENTS) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          x[k][0] = fl[k][0];
+          x[k][1] = fl[k][1];
+        }
+      } else {
+        fuse_merge(f, a.num_splits, &lse2, x);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // this pass's loads consumed before the next ones land
       if (p + 1 < a.passes) issue(p + 1);
+    } else if (LATENTS && row < a.rows) {
+      const float* src = a.o_lat + prow * kLatent + 8 * c;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (k == 1 && !two) break;
+        x[k][0] = *(const f32x4*)(src + 256 * k);
+        x[k][1] = *(const f32x4*)(src + 256 * k + 4);
+      }
     } else if (row < a.rows) {  // the general merge
       const uint16_t* po = a.part_o + prow * kLatent;
       const float* pml = a.part_ml + 2 * prow;
@@ -238,9 +177,9 @@ __global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a)
         merge_splits8<NS>(po + 8 * (c + 32), pml, o_step, ml_step, a.num_splits, &unused, x[1]);
       }
     }
-    if (row < a.rows && a.lse != nullptr && half == 0 && c == 0) a.lse[prow] = lse2 * 0.69314718055994531f;
-    // the merged latents as hi / lo bf16 terms; chunk cc of row r at slot cc ^ (r & 15); rows
-    // past the end are zero
+    if (!LATENTS && row < a.rows && a.lse != nullptr && half == 0 && c == 0) a.lse[prow] = lse2 * 0.69314718055994531f;
+    // the latents as hi / lo bf16 terms; chunk cc of row r at slot cc ^ (r & 15); rows past the
+    // end are zero
     uint8_t* hb = hi_t[p & 1];
     uint8_t* lb = lo_t[p & 1];
 #pragma unroll
@@ -286,18 +225,12 @@ __global__ __launch_bounds__(kFuseThreads) void merge_up_v_kernel(MergeUpArgs a)
 
 }  // namespace
 
-hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H,
-                       hipStream_t stream) {
-  void* args[] = {(void*)&o_lat, (void*)&w_v, (void*)&out, (void*)&rows, (void*)&H};
-  const int npass = (rows + kUpRows - 1) / kUpRows;
-  const dim3 grid(H * (kHeadDim / kDBlock), npass < kMaxRowGroups ? npass : kMaxRowGroups), block(kThreads);
-  return hipLaunchKernel((const void*)&up_v_kernel, grid, block, args, 0, stream);
-}
+namespace {
 
-hipError_t launch_merge_up_v(MergeUpArgs a, int cus, hipStream_t stream) {
-  // passes of 16 rows, spread evenly over just enough row groups to give every CU a workgroup
-  // (each pass after the first reuses the U_h^V half in registers); passes of 8 rows, one each,
-  // where a single pass of 16 would already leave CUs idle
+// passes of 16 rows, spread evenly over just enough row groups to give every CU a workgroup (each
+// pass after the first reuses the U_h^V half in registers); passes of 8 rows, one each, where a
+// single pass of 16 would already leave CUs idle
+void plan_rows(MergeUpArgs& a, int cus) {
   const int p16 = (a.rows + kFuseRows - 1) / kFuseRows;
   if (2 * a.H * p16 >= cus) {
     const int want = (cus + 2 * a.H - 1) / (2 * a.H);  // row groups that fill the CUs
@@ -311,15 +244,38 @@ hipError_t launch_merge_up_v(MergeUpArgs a, int cus, hipStream_t stream) {
   const int per = a.rows_per_pass * a.passes;
   a.groups = (a.rows + per - 1) / per;
   a.total_wg = a.H * a.groups * 2;
+}
+
+}  // namespace
+
+hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H, int cus,
+                       hipStream_t stream) {
+  MergeUpArgs a{};
+  a.o_lat = o_lat;
+  a.num_splits = 1;
+  a.rows = rows;
+  a.H = H;
+  a.w_v = w_v;
+  a.out = out;
+  plan_rows(a, cus);
+  void* args[] = {(void*)&a};
+  const void* fn = a.rows_per_pass == kFuseRows ? (const void*)&up_v_kernel<true, true, 2>
+                                                : (const void*)&up_v_kernel<true, false, 2>;
+  return hipLaunchKernel(fn, dim3(a.total_wg), dim3(kFuseThreads), args, 0, stream);
+}
+
+hipError_t launch_merge_up_v(MergeUpArgs a, int cus, hipStream_t stream) {
+  a.o_lat = nullptr;
+  plan_rows(a, cus);
   void* args[] = {(void*)&a};
   const bool ahead = a.rows_per_pass == kFuseRows && a.num_splits <= 8;
   const int ns = merge_slots(a.num_splits);
-  const void* fn = ahead ? (ns == 2   ? (const void*)&merge_up_v_kernel<true, 2>
-                            : ns == 4 ? (const void*)&merge_up_v_kernel<true, 4>
-                                      : (const void*)&merge_up_v_kernel<true, 8>)
-                         : (ns == 2   ? (const void*)&merge_up_v_kernel<false, 2>
-                            : ns == 4 ? (const void*)&merge_up_v_kernel<false, 4>
-                                      : (const void*)&merge_up_v_kernel<false, 8>);
+  const void* fn = ahead ? (ns == 2   ? (const void*)&up_v_kernel<false, true, 2>
+                            : ns == 4 ? (const void*)&up_v_kernel<false, true, 4>
+                                      : (const void*)&up_v_kernel<false, true, 8>)
+                         : (ns == 2   ? (const void*)&up_v_kernel<false, false, 2>
+                            : ns == 4 ? (const void*)&up_v_kernel<false, false, 4>
+                                      : (const void*)&up_v_kernel<false, false, 8>);
   return hipLaunchKernel(fn, dim3(a.total_wg), dim3(kFuseThreads), args, 0, stream);
 }
 
