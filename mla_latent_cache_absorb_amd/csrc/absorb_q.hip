@@ -19,6 +19,9 @@ constexpr int kRBlock = 128;                 // latents per workgroup
 constexpr int kSlabRowBytes = kRBlock * 2;   // 256 B per d-row of the slab
 constexpr int kThreads = 128;
 
+// AHEAD (more than one block of 32 rows): the next block's queries are loaded while this block
+// multiplies; with one block the kernel is the plain form
+template <bool AHEAD>
 __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ w_k,
                                                             uint16_t* __restrict__ q_abs, int rows,
@@ -33,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
   const int hl = lane & 31, hf = lane >> 5;
   const int nblocks = (rows + 31) / 32;
   // queries of row block nb as the B operand: lane (row hl, half hf) holds d = 16ks + 8hf .. +7
-  bf16x8 bq[16];
+  bf16x8 bq[16], bq_next[AHEAD ? 16 : 1];
   auto load_q = [&](int nb) {
     const int row = nb * 32 + hl;
     const bool rvalid = row < rows;
@@ -43,6 +46,15 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
       bf16x8 v = *(const bf16x8*)(qsrc + 16 * ks);
       if (!rvalid) v = (bf16x8)(s16x8){0, 0, 0, 0, 0, 0, 0, 0};
       bq[ks] = v;
+    }
+  };
+  // the next block's rows, zeroed when used if past the end
+  auto load_next = [&](int nb) {
+    if constexpr (AHEAD) {
+      const int row = nb * 32 + hl;
+      const uint16_t* qsrc = q + ((size_t)(row < rows ? row : 0) * H + h) * kHeadDim + 8 * hf;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) bq_next[ks] = *(const bf16x8*)(qsrc + 16 * ks);
     }
   };
   load_q(0);  // issued before the slab copies, so the two memory latencies overlap
@@ -69,7 +81,15 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
   for (int nb = 0; nb < nblocks; ++nb) {
     const int row = nb * 32 + hl;
     const bool rvalid = row < rows;
-    if (nb > 0) load_q(nb);
+    if constexpr (AHEAD) {
+      if (nb > 0) {
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) bq[ks] = rvalid ? bq_next[ks] : (bf16x8)(s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      }
+      if (nb + 1 < nblocks) load_next(nb + 1);
+    } else if (nb > 0) {
+      load_q(nb);
+    }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int mb = 2 * wave + m;
@@ -108,7 +128,8 @@ hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_a
                            float prescale, hipStream_t stream) {
   void* args[] = {(void*)&q, (void*)&w_k, (void*)&q_abs, (void*)&rows, (void*)&H, (void*)&prescale};
   const dim3 grid(H * (kLatent / kRBlock)), block(kThreads);
-  return hipLaunchKernel((const void*)&absorb_q_kernel, grid, block, args, 0, stream);
+  const void* k = rows > 32 ? (const void*)&absorb_q_kernel<true> : (const void*)&absorb_q_kernel<false>;
+  return hipLaunchKernel(k, grid, block, args, 0, stream);
 }
 
 }  // namespace mla
