@@ -65,7 +65,9 @@ def test_absorb_q_prescale_is_exact_power_of_two():
 
 
 # ------------------------------------------------------------------ stage: up_v
-@pytest.mark.parametrize("rows", [1, 32, 37, 128])
+# rows in passes of 16: 1 (a pass of 8), 32, 37 (a second group of one partial pass), 128, 300
+# (groups of ten passes, the last one of twelve rows), 1,100 (sixteen passes a group, the cap)
+@pytest.mark.parametrize("rows", [1, 32, 37, 128, 300, 1100])
 def test_up_v_matches_definition(rows):
     w = wl.make_workload(wl.make_spec(1, 1, 1, workload_id=220))
     rng = np.random.default_rng(rows)
