@@ -683,9 +683,10 @@ def time_qlen_sweep(steps: int = 20, warmup: int = 20):
 def time_other_configs(steps: int = 20, warmup: int = 20):
     """The headline attention call (mla_latent_attn / mla_latent_attn_indexed) on the two other
     full-size workloads: decode of 4 sequences of 131,072 positions with 1% of each sequence's
-    latents scaled by 8, and the indexed verification of 32 sequences (4 queries, lengths
+    latents scaled by 8 (with one and with two query terms; the second is what that workload needs
+    to meet the parity bar), and the indexed verification of 32 sequences (4 queries, lengths
     uniform in [4096, 65536]) over 2,048 positions drawn per query from the committed prefix plus
-    the causal tail.  Inputs are drawn on the GPU with those shapes and structures (timing only;
+    the causal tail; and the headline decode shape with one and with two query terms.  Inputs are drawn on the GPU with those shapes and structures (timing only;
     the parity tests use the seeded CPU workloads).  Two input sets alternate; each call is timed
     over `steps` back-to-back calls (the median of five chunks, chunked_ms)."""
     import torch
@@ -716,15 +717,45 @@ def time_other_configs(steps: int = 20, warmup: int = 20):
     o = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
     ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, L, 0), 1), dtype=torch.uint8, device=dev)
-    ms, ms_med = run(lambda k: binding.mla_latent_attn(sets[k][1], sets[k][0], cl, L, wl.SCALE, 0, o_lat=o, lse=lse,
-                                                       workspace=ws), 2)
+    # the second query term (what the two-term call reads beside the first): a remainder below
+    # half a bf16 step of the first term
+    q_lo = [(s[1].float() * torch.randn(s[1].shape, generator=gen, device=dev) * 2.0 ** -10).to(torch.bfloat16)
+            for s in sets]
     lat = B * L * R * 2
-    gbs = lat / (ms * 1e-3) / 1e9
-    out.append({"workload": "decode_b4_l131072_spiked", "call": "mla_latent_attn", "ms": round(ms, 5),
-                "median_chunk_ms": round(ms_med, 5),
-                "splits": binding.mla_latent_attn_num_splits(B, Q, H, L, 0), "latent_bytes": lat,
-                "GB/s": round(gbs, 2), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
-    del sets, o, lse, ws
+    for two_term in (False, True):
+        lo = (lambda k: q_lo[k]) if two_term else (lambda k: None)
+        ms, ms_med = run(lambda k: binding.mla_latent_attn(sets[k][1], sets[k][0], cl, L, wl.SCALE, 0, o_lat=o,
+                                                           lse=lse, workspace=ws, q_abs_lo=lo(k)), 2)
+        gbs = lat / (ms * 1e-3) / 1e9
+        out.append({"workload": "decode_b4_l131072_spiked", "call": "mla_latent_attn",
+                    "query_terms": 2 if two_term else 1, "ms": round(ms, 5), "median_chunk_ms": round(ms_med, 5),
+                    "splits": binding.mla_latent_attn_num_splits(B, Q, H, L, 0), "latent_bytes": lat,
+                    "GB/s": round(gbs, 2), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    del sets, o, lse, ws, q_lo
+    torch.cuda.empty_cache()
+
+    # decode, 32 x 8192, the attention call with one and with two query terms (the cost of the
+    # second term at the headline decode shape)
+    B, Q, L = 32, 1, 8192
+    sets = [((torch.randn(B, L, R, generator=gen, device=dev)).to(torch.bfloat16),
+             (torch.randn(B, Q, H, R, generator=gen, device=dev) * 0.5 ** 0.5).to(torch.bfloat16)) for _ in range(2)]
+    q_lo = [(s[1].float() * torch.randn(s[1].shape, generator=gen, device=dev) * 2.0 ** -10).to(torch.bfloat16)
+            for s in sets]
+    cl = torch.full((B,), L, dtype=torch.int32, device=dev)
+    o = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, L, 0), 1), dtype=torch.uint8, device=dev)
+    lat = B * L * R * 2
+    for two_term in (False, True):
+        lo = (lambda k: q_lo[k]) if two_term else (lambda k: None)
+        ms, ms_med = run(lambda k: binding.mla_latent_attn(sets[k][1], sets[k][0], cl, L, wl.SCALE, 0, o_lat=o,
+                                                           lse=lse, workspace=ws, q_abs_lo=lo(k)), 2)
+        gbs = lat / (ms * 1e-3) / 1e9
+        out.append({"workload": "decode_b32_l8192", "call": "mla_latent_attn", "query_terms": 2 if two_term else 1,
+                    "ms": round(ms, 5), "median_chunk_ms": round(ms_med, 5),
+                    "splits": binding.mla_latent_attn_num_splits(B, Q, H, L, 0), "latent_bytes": lat,
+                    "GB/s": round(gbs, 2), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    del sets, o, lse, ws, q_lo
     torch.cuda.empty_cache()
 
     # indexed verification, 32 x 4, ragged

@@ -73,13 +73,20 @@ const char* mla_status_string(int status);
  *   w_k    [H][D][R]    bf16   U_h^K for every head, as stored in the checkpoint (D x R per head)
  *   q_abs  [rows][H][R] bf16   output: prescale * (U_h^K)^T q_h, accumulated in fp32 and
  *                              rounded to nearest-even bf16
+ *   q_abs_lo [rows][H][R] bf16 output (may be NULL): the second term of the same value, the
+ *                              nearest-even bf16 of (x - q_abs) for the fp32 result x, so that
+ *                              q_abs + q_abs_lo carries x to within 2^-17 |x|.  Pass it to the
+ *                              attention calls when scores need more than bf16's 8 bits of the
+ *                              absorbed query (latents with large outliers, as in a stress case
+ *                              with 1% of positions scaled x8, where one term moves a few outputs
+ *                              by about 1% of the output's largest value)
  *   prescale                   1.0f, or a power of two such as the softmax scale 1/16 (then
  *                              pass scale = 1 to the attention call); must be finite
  * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (rows < 1 or unsupported dims), MLA_ERR_ARG
  * (non-finite prescale), MLA_ERR_DEVICE, MLA_ERR_HIP.
  */
-int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int32_t rows, int32_t H,
-                 int32_t D, int32_t R, float prescale, void* stream);
+int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, uint16_t* q_abs_lo, int32_t rows,
+                 int32_t H, int32_t D, int32_t R, float prescale, void* stream);
 
 /*
  * Number of position splits a latent-attention call will use (split-K over the positions,
@@ -115,6 +122,11 @@ size_t mla_latent_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R
  * directly through the absorbed query; the value sum accumulates in latent space and is
  * expanded later; the scale is that of the original q.k).
  *   q_abs      [B][Q][H][R] bf16   absorbed queries (mla_absorb_q)
+ *   q_abs_lo   [B][Q][H][R] bf16   second query term (mla_absorb_q), or NULL.  Given, every
+ *                                  score is c_j . q_abs + c_j . q_abs_lo, both products summed in
+ *                                  one fp32 accumulator; each query then runs in a workgroup of its
+ *                                  own (about 10% slower for Q = 1; dense calls with an even Q lose
+ *                                  the query pairing), with the split count of the one-term call
  *   cache      bf16 latent rows: row j of sequence b starts at cache + b*cache_batch_stride
  *              + j*R; cache_batch_stride (elements) >= max_cache_len * R
  *   cache_len  [B] int32 (device)  positions held by each sequence, including the Q new ones
@@ -129,15 +141,15 @@ size_t mla_latent_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R
  * Cache rows at or past min(cache_len[b], max_cache_len) are never read.  A query whose
  * visible set is empty (cache_len[b] < Q) gets o_lat = NaN and lse = -inf.
  * Results are deterministic for a fixed num_splits (no atomics in any reduction), and for the
- * same split count equal bit for bit those of mla_latent_attn_indexed given every causal
- * position.  With several splits each split's normalised partial is kept in fp16 between the
+ * same split count and query terms equal bit for bit those of mla_latent_attn_indexed given
+ * every causal position.  With several splits each split's normalised partial is kept in fp16 between the
  * two kernels (2^-11 relative; a convex combination of cached latents, so the cache's values
  * must stay below 65,504 in magnitude); maxima, sums and lse stay fp32.
  */
-int mla_latent_attn(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
-                    const int32_t* cache_len, int32_t B, int32_t Q, int32_t H, int32_t R,
-                    int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat, float* lse,
-                    void* workspace, size_t workspace_bytes, void* stream);
+int mla_latent_attn(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t* cache,
+                    int64_t cache_batch_stride, const int32_t* cache_len, int32_t B, int32_t Q, int32_t H,
+                    int32_t R, int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Indexed latent attention: as mla_latent_attn, but query i of sequence b attends exactly
@@ -152,11 +164,12 @@ int mla_latent_attn(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_
  * usable position gets o_lat = NaN and lse = -inf.  Workspace: pass K_max as max_positions
  * to mla_latent_attn_workspace_size.
  */
-int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
-                            const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len,
-                            int32_t K_max, int32_t B, int32_t Q, int32_t H, int32_t R,
-                            int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat,
-                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t* cache,
+                            int64_t cache_batch_stride, const int32_t* cache_len, const int32_t* idx,
+                            const int32_t* idx_len, int32_t K_max, int32_t B, int32_t Q, int32_t H,
+                            int32_t R, int32_t max_cache_len, float scale, int32_t num_splits,
+                            float* o_lat, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * k-pooled sparse-attention indexer: the three steps that turn indexer keys into the position
@@ -296,8 +309,8 @@ int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, 
  * through device memory as a separate array.  The result has the same bits as mla_up_v applied
  * to the o_lat of the separate attention call with the same split count (same merge arithmetic in
  * the same order, same up-projection).
- *   q_abs, cache, cache_batch_stride, cache_len, B, Q, H, R, max_cache_len, scale, num_splits
- *                      as in mla_latent_attn
+ *   q_abs, q_abs_lo, cache, cache_batch_stride, cache_len, B, Q, H, R, max_cache_len, scale,
+ *   num_splits         as in mla_latent_attn
  *   idx, idx_len, K_max  as in mla_latent_attn_indexed, or idx = idx_len = NULL (K_max ignored)
  *                      for dense attention
  *   w_v    [H][D][R] bf16   U_h^V (D == 256)
@@ -312,11 +325,12 @@ int mla_up_v(const float* o_lat, const uint16_t* w_v, float* out, int32_t rows, 
  */
 size_t mla_latent_attn_up_v_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R,
                                            int32_t max_positions, int32_t num_splits, int32_t indexed);
-int mla_latent_attn_up_v(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
-                         const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t K_max,
-                         int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len, float scale,
-                         int32_t num_splits, const uint16_t* w_v, int32_t D, float* out, float* lse,
-                         void* workspace, size_t workspace_bytes, void* stream);
+int mla_latent_attn_up_v(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t* cache,
+                         int64_t cache_batch_stride, const int32_t* cache_len, const int32_t* idx,
+                         const int32_t* idx_len, int32_t K_max, int32_t B, int32_t Q, int32_t H, int32_t R,
+                         int32_t max_cache_len, float scale, int32_t num_splits, const uint16_t* w_v,
+                         int32_t D, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * Debug check of the attention calls' device-side preconditions (the calls themselves do not
@@ -380,11 +394,11 @@ int mla_stream_read(const void* src, size_t bytes, uint32_t never, uint32_t* sin
  * Errors: those of mla_latent_attn_up_v except MLA_ERR_WORKSPACE, plus MLA_ERR_SCRATCH.
  */
 #define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
-int mla_latent_attn_up_v_noalloc(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
-                                 const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len,
-                                 int32_t K_max, int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len,
-                                 float scale, int32_t num_splits, const uint16_t* w_v, int32_t D, float* out,
-                                 float* lse, void* stream);
+int mla_latent_attn_up_v_noalloc(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t* cache,
+                                 int64_t cache_batch_stride, const int32_t* cache_len, const int32_t* idx,
+                                 const int32_t* idx_len, int32_t K_max, int32_t B, int32_t Q, int32_t H,
+                                 int32_t R, int32_t max_cache_len, float scale, int32_t num_splits,
+                                 const uint16_t* w_v, int32_t D, float* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -51,24 +51,24 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
-        L.mla_absorb_q.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, vp]
+        L.mla_absorb_q.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
         L.mla_absorb_q.restype = ctypes.c_int
         L.mla_latent_attn_num_splits.argtypes = [i32, i32, i32, i32, i32, i32]
         L.mla_latent_attn_num_splits.restype = i32
         L.mla_latent_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.mla_latent_attn_workspace_size.restype = sz
-        L.mla_latent_attn.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+        L.mla_latent_attn.argtypes = [vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
         L.mla_latent_attn.restype = ctypes.c_int
-        L.mla_latent_attn_indexed.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp,
-                                              vp, vp, sz, vp]
+        L.mla_latent_attn_indexed.argtypes = [vp, vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                              vp, vp, vp, sz, vp]
         L.mla_latent_attn_indexed.restype = ctypes.c_int
         L.mla_latent_attn_up_v_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.mla_latent_attn_up_v_workspace_size.restype = sz
-        L.mla_latent_attn_up_v.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32,
-                                           vp, vp, vp, sz, vp]
+        L.mla_latent_attn_up_v.argtypes = [vp, vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+                                           i32, vp, vp, vp, sz, vp]
         L.mla_latent_attn_up_v.restype = ctypes.c_int
-        L.mla_latent_attn_up_v_noalloc.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
-                                                   vp, i32, vp, vp, vp]
+        L.mla_latent_attn_up_v_noalloc.argtypes = [vp, vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                                   i32, vp, i32, vp, vp, vp]
         L.mla_latent_attn_up_v_noalloc.restype = ctypes.c_int
         L.mla_stream_read.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
         L.mla_stream_read.restype = ctypes.c_int
@@ -142,8 +142,10 @@ def _nbytes(t: Optional[torch.Tensor]) -> int:
 
 # ----------------------------------------------------------------------------------------
 def mla_absorb_q(q: torch.Tensor, w_k: torch.Tensor, q_abs: Optional[torch.Tensor] = None,
-                 prescale: float = 1.0, stream=None) -> torch.Tensor:
-    """q [..., H, D] bf16, w_k [H, D, R] bf16 -> q_abs [..., H, R] bf16 = prescale * W_k^T q."""
+                 prescale: float = 1.0, stream=None, lo: bool = False, q_abs_lo: Optional[torch.Tensor] = None):
+    """q [..., H, D] bf16, w_k [H, D, R] bf16 -> q_abs [..., H, R] bf16 = prescale * W_k^T q.
+    With lo=True (or q_abs_lo given) the second bf16 term is written too and (q_abs, q_abs_lo) is
+    returned."""
     _need(q, torch.bfloat16, "q")
     _need(w_k, torch.bfloat16, "w_k")
     if w_k.dim() != 3:
@@ -152,15 +154,19 @@ def mla_absorb_q(q: torch.Tensor, w_k: torch.Tensor, q_abs: Optional[torch.Tenso
     if q.dim() < 2 or tuple(q.shape[-2:]) != (H, D):
         raise ValueError("q must end in [H, D]")
     rows = q.numel() // (H * D)
-    if q_abs is not None:
-        _need(q_abs, torch.bfloat16, "q_abs")
-        _shape(q_abs, tuple(q.shape[:-1]) + (R,), "q_abs")
-    _gpu(q, w_k, q_abs)
+    lo = lo or q_abs_lo is not None
+    for t, nm in ((q_abs, "q_abs"), (q_abs_lo, "q_abs_lo")):
+        if t is not None:
+            _need(t, torch.bfloat16, nm)
+            _shape(t, tuple(q.shape[:-1]) + (R,), nm)
+    _gpu(q, w_k, q_abs, q_abs_lo)
     if q_abs is None:
         q_abs = torch.empty(q.shape[:-1] + (R,), dtype=torch.bfloat16, device=q.device)
-    _check(lib().mla_absorb_q(_ptr(q), _ptr(w_k), _ptr(q_abs), rows, H, D, R, float(prescale), _stream(stream)),
-           "mla_absorb_q")
-    return q_abs
+    if lo and q_abs_lo is None:
+        q_abs_lo = torch.empty(q.shape[:-1] + (R,), dtype=torch.bfloat16, device=q.device)
+    _check(lib().mla_absorb_q(_ptr(q), _ptr(w_k), _ptr(q_abs), _ptr(q_abs_lo), rows, H, D, R, float(prescale),
+                              _stream(stream)), "mla_absorb_q")
+    return (q_abs, q_abs_lo) if lo else q_abs
 
 
 def mla_latent_attn_num_splits(B: int, Q: int, H: int, max_positions: int, num_splits: int = 0,
@@ -181,9 +187,12 @@ def _cache_stride(cache: torch.Tensor) -> int:
     return int(cache.stride(0))
 
 
-def _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx=None, idx_len=None):
+def _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx=None, idx_len=None, q_abs_lo=None):
     """dtype and extent checks shared by the attention calls; returns (B, Q, H, R, K_max)."""
     _need(q_abs, torch.bfloat16, "q_abs")
+    if q_abs_lo is not None:
+        _need(q_abs_lo, torch.bfloat16, "q_abs_lo")
+        _shape(q_abs_lo, tuple(q_abs.shape), "q_abs_lo")
     _need(cache, torch.bfloat16, "cache", contiguous=False)
     _need(cache_len, torch.int32, "cache_len")
     if q_abs.dim() != 4:
@@ -286,17 +295,18 @@ def _debug_check(cache_len, Q, max_cache_len, idx=None, idx_len=None, stream=Non
 
 def mla_latent_attn(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int,
                     scale: float, num_splits: int = 0, o_lat=None, lse=None, workspace=None, want_lse=True,
-                    stream=None):
-    """Dense latent attention.  q_abs [B, Q, H, R] bf16; cache [B, L_max, R] bf16 (a view with any
-    batch stride); cache_len [B] int32 on the GPU.  Returns (o_lat [B, Q, H, R] fp32, lse [B, Q, H])."""
-    B, Q, H, R, _ = _attn_inputs(q_abs, cache, cache_len, max_cache_len)
+                    stream=None, q_abs_lo=None):
+    """Dense latent attention.  q_abs [B, Q, H, R] bf16 (and optionally its second term q_abs_lo);
+    cache [B, L_max, R] bf16 (a view with any batch stride); cache_len [B] int32 on the GPU.
+    Returns (o_lat [B, Q, H, R] fp32, lse [B, Q, H])."""
+    B, Q, H, R, _ = _attn_inputs(q_abs, cache, cache_len, max_cache_len, q_abs_lo=q_abs_lo)
     o_lat, lse = _attn_outputs(q_abs, o_lat, lse, want_lse)
-    _gpu(q_abs, cache, cache_len, o_lat, lse, _workspace_arg(workspace))
+    _gpu(q_abs, q_abs_lo, cache, cache_len, o_lat, lse, _workspace_arg(workspace))
     o_lat, lse = _alloc_outputs(q_abs, o_lat, lse, want_lse)
     _debug_check(cache_len, Q, max_cache_len, stream=stream)
     need = mla_latent_attn_workspace_size(B, Q, H, R, max_cache_len, num_splits)
     workspace = _workspace(workspace, need, q_abs.device)
-    _check(lib().mla_latent_attn(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), B, Q, H, R,
+    _check(lib().mla_latent_attn(_ptr(q_abs), _ptr(q_abs_lo), _ptr(cache), _cache_stride(cache), _ptr(cache_len), B, Q, H, R,
                                  int(max_cache_len), float(scale), int(num_splits), _ptr(o_lat), _ptr(lse),
                                  _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "mla_latent_attn")
@@ -305,18 +315,18 @@ def mla_latent_attn(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.T
 
 def mla_latent_attn_indexed(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor, idx: torch.Tensor,
                             idx_len: torch.Tensor, max_cache_len: int, scale: float, num_splits: int = 0,
-                            o_lat=None, lse=None, workspace=None, want_lse=True, stream=None):
+                            o_lat=None, lse=None, workspace=None, want_lse=True, stream=None, q_abs_lo=None):
     """Indexed latent attention: idx [B, Q, K_max] int32 (sorted positions), idx_len [B, Q] int32."""
     if idx is None or idx_len is None:
         raise ValueError("the indexed call needs idx and idx_len")
-    B, Q, H, R, K_max = _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx, idx_len)
+    B, Q, H, R, K_max = _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx, idx_len, q_abs_lo)
     o_lat, lse = _attn_outputs(q_abs, o_lat, lse, want_lse)
-    _gpu(q_abs, cache, cache_len, idx, idx_len, o_lat, lse, _workspace_arg(workspace))
+    _gpu(q_abs, q_abs_lo, cache, cache_len, idx, idx_len, o_lat, lse, _workspace_arg(workspace))
     o_lat, lse = _alloc_outputs(q_abs, o_lat, lse, want_lse)
     _debug_check(cache_len, Q, max_cache_len, idx, idx_len, stream=stream)
     need = mla_latent_attn_workspace_size(B, Q, H, R, K_max, num_splits, indexed=True)
     workspace = _workspace(workspace, need, q_abs.device)
-    _check(lib().mla_latent_attn_indexed(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
+    _check(lib().mla_latent_attn_indexed(_ptr(q_abs), _ptr(q_abs_lo), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
                                          _ptr(idx_len), K_max, B, Q, H, R, int(max_cache_len), float(scale),
                                          int(num_splits), _ptr(o_lat), _ptr(lse), _ptr(workspace),
                                          _nbytes(workspace), _stream(stream)),
@@ -352,11 +362,11 @@ def mla_latent_attn_up_v_workspace_size(B: int, Q: int, H: int, R: int, max_posi
 def mla_latent_attn_up_v(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor, max_cache_len: int,
                          scale: float, w_v: torch.Tensor, idx: Optional[torch.Tensor] = None,
                          idx_len: Optional[torch.Tensor] = None, num_splits: int = 0, out=None, lse=None,
-                         workspace=None, want_lse=True, stream=None):
+                         workspace=None, want_lse=True, stream=None, q_abs_lo=None):
     """Latent attention (dense, or indexed when idx / idx_len are given) followed by the value
     up-projection, the split merge fused into the latter.  Returns (out [B, Q, H, D] fp32,
     lse [B, Q, H] fp32)."""
-    B, Q, H, R, K_max = _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx, idx_len)
+    B, Q, H, R, K_max = _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx, idx_len, q_abs_lo)
     _need(w_v, torch.bfloat16, "w_v")
     if w_v.dim() != 3 or w_v.shape[0] != H or w_v.shape[2] != R:
         raise ValueError(f"w_v must be [H={H}, D, R={R}], got {tuple(w_v.shape)}")
@@ -368,7 +378,7 @@ def mla_latent_attn_up_v(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: to
     if lse is not None:
         _need(lse, torch.float32, "lse")
         _shape(lse, (B, Q, H), "lse")
-    _gpu(q_abs, cache, cache_len, w_v, idx, idx_len, out, lse, _workspace_arg(workspace))
+    _gpu(q_abs, q_abs_lo, cache, cache_len, w_v, idx, idx_len, out, lse, _workspace_arg(workspace))
     if out is None:
         out = torch.empty((B, Q, H, D), dtype=torch.float32, device=q_abs.device)
     if lse is None and want_lse:
@@ -376,7 +386,7 @@ def mla_latent_attn_up_v(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: to
     _debug_check(cache_len, Q, max_cache_len, idx, idx_len, stream=stream)
     need = mla_latent_attn_up_v_workspace_size(B, Q, H, R, K_max if indexed else max_cache_len, num_splits, indexed)
     workspace = _workspace(workspace, need, q_abs.device)
-    _check(lib().mla_latent_attn_up_v(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
+    _check(lib().mla_latent_attn_up_v(_ptr(q_abs), _ptr(q_abs_lo), _ptr(cache), _cache_stride(cache), _ptr(cache_len), _ptr(idx),
                                       _ptr(idx_len), K_max, B, Q, H, R, int(max_cache_len), float(scale),
                                       int(num_splits), _ptr(w_v), D, _ptr(out), _ptr(lse), _ptr(workspace),
                                       _nbytes(workspace), _stream(stream)),
@@ -387,11 +397,12 @@ def mla_latent_attn_up_v(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: to
 def mla_latent_attn_up_v_noalloc(q_abs: torch.Tensor, cache: torch.Tensor, cache_len: torch.Tensor,
                                  max_cache_len: int, scale: float, w_v: torch.Tensor, out: torch.Tensor,
                                  lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
-                                 idx_len: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None):
+                                 idx_len: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None,
+                                 q_abs_lo: Optional[torch.Tensor] = None):
     """mla_latent_attn_up_v with the split partials in the library's fixed device scratch: neither
     the library nor this wrapper allocates (the caller passes out, and lse or None).  Calls that
     overlap on one GPU race on that scratch.  Returns (out, lse)."""
-    B, Q, H, R, K_max = _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx, idx_len)
+    B, Q, H, R, K_max = _attn_inputs(q_abs, cache, cache_len, max_cache_len, idx, idx_len, q_abs_lo)
     _need(w_v, torch.bfloat16, "w_v")
     if w_v.dim() != 3 or w_v.shape[0] != H or w_v.shape[2] != R:
         raise ValueError(f"w_v must be [H={H}, D, R={R}], got {tuple(w_v.shape)}")
@@ -403,8 +414,8 @@ def mla_latent_attn_up_v_noalloc(q_abs: torch.Tensor, cache: torch.Tensor, cache
     if lse is not None:
         _need(lse, torch.float32, "lse")
         _shape(lse, (B, Q, H), "lse")
-    _gpu(q_abs, cache, cache_len, w_v, idx, idx_len, out, lse)
-    _check(lib().mla_latent_attn_up_v_noalloc(_ptr(q_abs), _ptr(cache), _cache_stride(cache), _ptr(cache_len),
+    _gpu(q_abs, q_abs_lo, cache, cache_len, w_v, idx, idx_len, out, lse)
+    _check(lib().mla_latent_attn_up_v_noalloc(_ptr(q_abs), _ptr(q_abs_lo), _ptr(cache), _cache_stride(cache), _ptr(cache_len),
                                               _ptr(idx), _ptr(idx_len), K_max, B, Q, H, R, int(max_cache_len),
                                               float(scale), int(num_splits), _ptr(w_v), D, _ptr(out), _ptr(lse),
                                               _stream(stream)), "mla_latent_attn_up_v_noalloc")
@@ -629,10 +640,14 @@ def mla_indexer(q: torch.Tensor, k: torch.Tensor, g: torch.Tensor, cache_len: to
 
 
 def mla_forward(q, w_k, w_v, cache, cache_len, max_cache_len, scale, idx=None, idx_len=None, num_splits=0,
-                stream=None):
+                stream=None, two_term=False):
     """The whole absorbed path: absorb_q -> latent attention (dense or indexed) with the
-    up-projection fused into the split merge (mla_latent_attn_up_v).
+    up-projection fused into the split merge (mla_latent_attn_up_v); two_term carries the
+    absorbed query as two bf16 terms into the scores.
     Returns (out [B, Q, H, D] fp32, lse [B, Q, H] fp32)."""
-    q_abs = mla_absorb_q(q, w_k, stream=stream)
+    if two_term:
+        q_abs, q_abs_lo = mla_absorb_q(q, w_k, stream=stream, lo=True)
+    else:
+        q_abs, q_abs_lo = mla_absorb_q(q, w_k, stream=stream), None
     return mla_latent_attn_up_v(q_abs, cache, cache_len, max_cache_len, scale, w_v, idx, idx_len, num_splits,
-                                stream=stream)
+                                stream=stream, q_abs_lo=q_abs_lo)

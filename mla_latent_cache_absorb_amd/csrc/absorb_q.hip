@@ -7,7 +7,8 @@
 // its transpose is the A operand: a [256 d x 128 r] slab of it is staged in LDS (64 KiB,
 // 16-byte chunks swizzled per row) and read with the LDS transpose read.  The queries are the
 // B operand, 16-byte loads straight from memory.  Accumulation is fp32, the result is rounded
-// to nearest-even bf16.
+// to nearest-even bf16; on request the rounding's remainder is written as a second bf16 term
+// (lo = bf16(x - hi)), so that hi + lo carries x to about 2^-17 of its magnitude.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -24,7 +25,8 @@ constexpr int kThreads = 128;
 template <bool AHEAD>
 __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ w_k,
-                                                            uint16_t* __restrict__ q_abs, int rows,
+                                                            uint16_t* __restrict__ q_abs,
+                                                            uint16_t* __restrict__ q_abs_lo, int rows,
                                                             int H, float prescale) {
   __shared__ __attribute__((aligned(1024))) uint8_t slab[kHeadDim * kSlabRowBytes];
   const int lane = threadIdx.x & 63;
@@ -109,13 +111,20 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
       }
       if (rvalid) {
         // lane holds query row `row`, latents r0 + 32mb + 8ii + 4hf + j
-        uint16_t* dst = q_abs + ((size_t)row * H + h) * kLatent + r0 + 32 * mb + 4 * hf;
+        const size_t off = ((size_t)row * H + h) * kLatent + r0 + 32 * mb + 4 * hf;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          s16x4 v;
+          s16x4 v, vl;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (short)f32_to_bf16_bits(acc[4 * ii + j] * prescale);
-          *(s16x4*)(dst + 8 * ii) = v;
+          for (int j = 0; j < 4; ++j) {
+            const float x = acc[4 * ii + j] * prescale;
+            const uint16_t hb = f32_to_bf16_bits(x);
+            v[j] = (short)hb;
+            // x - hi is exact in fp32 (hi is x's nearest bf16)
+            vl[j] = (short)f32_to_bf16_bits(x - bf16_bits_to_f32(hb));
+          }
+          *(s16x4*)(q_abs + off + 8 * ii) = v;
+          if (q_abs_lo != nullptr) *(s16x4*)(q_abs_lo + off + 8 * ii) = vl;
         }
       }
     }
@@ -124,9 +133,10 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
 
 }  // namespace
 
-hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int rows, int H,
-                           float prescale, hipStream_t stream) {
-  void* args[] = {(void*)&q, (void*)&w_k, (void*)&q_abs, (void*)&rows, (void*)&H, (void*)&prescale};
+hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, uint16_t* q_abs_lo, int rows,
+                           int H, float prescale, hipStream_t stream) {
+  void* args[] = {(void*)&q, (void*)&w_k, (void*)&q_abs, (void*)&q_abs_lo, (void*)&rows, (void*)&H,
+                  (void*)&prescale};
   const dim3 grid(H * (kLatent / kRBlock)), block(kThreads);
   const void* k = rows > 32 ? (const void*)&absorb_q_kernel<true> : (const void*)&absorb_q_kernel<false>;
   return hipLaunchKernel(k, grid, block, args, 0, stream);

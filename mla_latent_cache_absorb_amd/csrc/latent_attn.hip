@@ -33,6 +33,11 @@
 // the same twelve waves take two adjacent queries over one run of tiles, so that each LDS read of
 // a tile feeds twice the matrix work (the single-query form is bound by its LDS traffic).
 //
+// A call given the absorbed query in two bf16 terms (q_abs + q_abs_lo, the second the rounding
+// remainder of the first) runs the single-query form for every query: each score wave holds both
+// terms and each tile read feeds two MFMAs into the same accumulator, so the scores see the query
+// to about 2^-17 of its size instead of bf16's 2^-9.
+//
 // The split partials (m, l, u = o / l) are merged by log-sum-exp (merge_splits8): combine_kernel
 // for up to eight splits, combine_wide_kernel above that (one thread group per group of eight
 // splits), or the fused merge and up-projection of mla_latent_attn_up_v; all three give the same
@@ -192,7 +197,9 @@ __device__ __forceinline__ void copy_partial_block(const AttnArgs& a, size_t fir
     *(float2*)(a.part_ml + 2 * (first + threadIdx.x)) = float2{m_row[threadIdx.x], l_row[threadIdx.x]};
 }
 
-template <bool INDEXED>
+// LO: the absorbed query comes as two bf16 terms (q_abs + q_abs_lo) and each score takes both
+// products into one fp32 accumulator
+template <bool INDEXED, bool LO>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void latent_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing][kTileBytes];
@@ -240,12 +247,16 @@ void latent_attn_kernel(AttnArgs a) {
     const int c = lane & 15, G = lane >> 4;  // head 16s + c; k / row group G
     const int h = min(hg * 64 + 16 * s + c, a.H - 1);  // a partial group's missing heads reuse the last
     const float c2 = a.scale_log2;
-    // absorbed query as the B operand: latents 32ks + 8G .. +7
-    bf16x8 qf[16];
+    // absorbed query as the B operand: latents 32ks + 8G .. +7 (and its second term with LO)
+    bf16x8 qf[16], ql[LO ? 16 : 1];
     {
-      const uint16_t* qrow = a.q_abs + ((size_t)bq * a.H + h) * kLatent + 8 * G;
+      const size_t qoff = ((size_t)bq * a.H + h) * kLatent + 8 * G;
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) qf[ks] = *(const bf16x8*)(qrow + 32 * ks);
+      for (int ks = 0; ks < 16; ++ks) qf[ks] = *(const bf16x8*)(a.q_abs + qoff + 32 * ks);
+      if constexpr (LO) {
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) ql[ks] = *(const bf16x8*)(a.q_abs_lo + qoff + 32 * ks);
+      }
     }
     float m_run = -INFINITY;  // running maximum of scale*log2(e)*score (this lane's head)
     float l_run = 0.f;        // running sum of 2^(scale*log2(e)*score - m_run)
@@ -273,7 +284,9 @@ void latent_attn_kernel(AttnArgs a) {
         return *(const bf16x8*)(rb + 16 * kRowBytes * (n & 1) + 256 * (ks >> 2) + (((ks & 3) ^ hi) << 6));
       };
       f32x4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      constexpr int kAhead = 7;  // reads in flight ahead of the MFMA that consumes them
+      // reads in flight ahead of the MFMA that consumes them (with LO each read feeds two MFMAs,
+      // and the second query term leaves registers for two)
+      constexpr int kAhead = LO ? 2 : 7;
       bf16x8 av[kAhead + 1];
 #pragma unroll
       for (int n = 0; n < kAhead; ++n) av[n] = rd(n);
@@ -282,6 +295,7 @@ void latent_attn_kernel(AttnArgs a) {
         if (n + kAhead < 32) av[(n + kAhead) % (kAhead + 1)] = rd(n + kAhead);
         __builtin_amdgcn_sched_barrier(0);
         sc[n & 1] = mfma16(av[n % (kAhead + 1)], qf[n >> 1], sc[n & 1]);
+        if constexpr (LO) sc[n & 1] = mfma16(av[n % (kAhead + 1)], ql[n >> 1], sc[n & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
       // lane holds positions 16 blk + 4jj + G of head c; mask those past the visible set
@@ -787,9 +801,13 @@ __global__ __launch_bounds__(512) void combine_wide_kernel(AttnArgs a) {
 hipError_t launch_latent_attn(const AttnArgs& a, bool indexed, hipStream_t stream) {
   void* args[] = {const_cast<AttnArgs*>(&a)};
   const dim3 grid(a.total_wg), block(kThreads);
-  const void* k = indexed                    ? (const void*)&latent_attn_kernel<true>
-                  : queries_per_wg(false, a.Q) == 2 ? (const void*)&latent_attn_pair_kernel
-                                                    : (const void*)&latent_attn_kernel<false>;
+  const void* k;
+  if (a.q_abs_lo != nullptr)
+    k = indexed ? (const void*)&latent_attn_kernel<true, true> : (const void*)&latent_attn_kernel<false, true>;
+  else
+    k = indexed                            ? (const void*)&latent_attn_kernel<true, false>
+        : queries_per_wg(false, a.Q) == 2 ? (const void*)&latent_attn_pair_kernel
+                                          : (const void*)&latent_attn_kernel<false, false>;
   return hipLaunchKernel(k, grid, block, args, 0, stream);
 }
 

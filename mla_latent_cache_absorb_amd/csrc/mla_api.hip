@@ -138,7 +138,8 @@ int device_cus_or_default() {
   return cus > 0 ? cus : 256;
 }
 
-int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride, const int32_t* cache_len,
+int attn_common(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t* cache, int64_t cache_batch_stride,
+                const int32_t* cache_len,
                 const int32_t* idx, const int32_t* idx_len, int32_t K_max, bool indexed, int32_t B, int32_t Q,
                 int32_t H, int32_t R, int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat,
                 float* lse, void* workspace, size_t workspace_bytes, void* stream, const uint16_t* w_v = nullptr,
@@ -168,11 +169,14 @@ int attn_common(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batc
     workspace_bytes = kScratchBytes;
   }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
-  const int64_t total = (int64_t)B * mla::query_units(indexed, Q) * head_groups(H) * s;
+  // a two-term query runs every query in a workgroup of its own (same split count)
+  const int64_t units = q_abs_lo != nullptr ? Q : mla::query_units(indexed, Q);
+  const int64_t total = (int64_t)B * units * head_groups(H) * s;
   if (total > 0x7fffffff || (int64_t)B * Q * H > 0x7fffffff) return MLA_ERR_SHAPE;
 
   mla::AttnArgs a;
   a.q_abs = q_abs;
+  a.q_abs_lo = q_abs_lo;
   a.cache = (const uint8_t*)cache;
   a.cache_bstride_bytes = cache_batch_stride * 2;
   a.cache_len = cache_len;
@@ -231,14 +235,15 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int32_t rows, int32_t H, int32_t D,
-                 int32_t R, float prescale, void* stream) {
+int mla_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, uint16_t* q_abs_lo, int32_t rows,
+                 int32_t H, int32_t D, int32_t R, float prescale, void* stream) {
   if (!q || !w_k || !q_abs) return MLA_ERR_NULL;
   if (!supported(H, D, R) || rows < 1 || (int64_t)rows * H > 0x7fffffff) return MLA_ERR_SHAPE;
   if (!isfinite(prescale)) return MLA_ERR_ARG;
   const int dst = check_device(nullptr);
   if (dst != MLA_OK) return dst;
-  if (mla::launch_absorb_q(q, w_k, q_abs, rows, H, prescale, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  if (mla::launch_absorb_q(q, w_k, q_abs, q_abs_lo, rows, H, prescale, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
   return MLA_OK;
 }
 
@@ -255,19 +260,20 @@ size_t mla_latent_attn_workspace_size(int32_t B, int32_t Q, int32_t H, int32_t R
   return workspace_bytes_for(B, Q, H, s);
 }
 
-int mla_latent_attn(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride, const int32_t* cache_len,
-                    int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len, float scale, int32_t num_splits,
-                    float* o_lat, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return attn_common(q_abs, cache, cache_batch_stride, cache_len, nullptr, nullptr, 0, false, B, Q, H, R,
+int mla_latent_attn(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t* cache, int64_t cache_batch_stride,
+                    const int32_t* cache_len, int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len,
+                    float scale, int32_t num_splits, float* o_lat, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return attn_common(q_abs, q_abs_lo, cache, cache_batch_stride, cache_len, nullptr, nullptr, 0, false, B, Q, H, R,
                      max_cache_len, scale, num_splits, o_lat, lse, workspace, workspace_bytes, stream);
 }
 
-int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
-                            const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t K_max,
-                            int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len, float scale,
-                            int32_t num_splits, float* o_lat, float* lse, void* workspace, size_t workspace_bytes,
-                            void* stream) {
-  return attn_common(q_abs, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, true, B, Q, H, R,
+int mla_latent_attn_indexed(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t* cache,
+                            int64_t cache_batch_stride, const int32_t* cache_len, const int32_t* idx,
+                            const int32_t* idx_len, int32_t K_max, int32_t B, int32_t Q, int32_t H, int32_t R,
+                            int32_t max_cache_len, float scale, int32_t num_splits, float* o_lat, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_common(q_abs, q_abs_lo, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, true, B, Q, H, R,
                      max_cache_len, scale, num_splits, o_lat, lse, workspace, workspace_bytes, stream);
 }
 
@@ -279,28 +285,28 @@ size_t mla_latent_attn_up_v_workspace_size(int32_t B, int32_t Q, int32_t H, int3
   return fused_workspace_bytes_for(B, Q, H, s);
 }
 
-int mla_latent_attn_up_v(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
-                         const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t K_max,
+int mla_latent_attn_up_v(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t* cache,
+                         int64_t cache_batch_stride, const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len, int32_t K_max,
                          int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len, float scale,
                          int32_t num_splits, const uint16_t* w_v, int32_t D, float* out, float* lse, void* workspace,
                          size_t workspace_bytes, void* stream) {
   if (!w_v) return MLA_ERR_NULL;
   if ((idx == nullptr) != (idx_len == nullptr)) return MLA_ERR_NULL;
   if (!supported(H, D, R)) return MLA_ERR_SHAPE;
-  return attn_common(q_abs, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, idx != nullptr, B, Q, H, R,
-                     max_cache_len, scale, num_splits, nullptr, lse, workspace, workspace_bytes, stream, w_v, out);
+  return attn_common(q_abs, q_abs_lo, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, idx != nullptr, B,
+                     Q, H, R, max_cache_len, scale, num_splits, nullptr, lse, workspace, workspace_bytes, stream, w_v, out);
 }
 
-int mla_latent_attn_up_v_noalloc(const uint16_t* q_abs, const uint16_t* cache, int64_t cache_batch_stride,
-                                 const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len,
+int mla_latent_attn_up_v_noalloc(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t* cache,
+                                 int64_t cache_batch_stride, const int32_t* cache_len, const int32_t* idx, const int32_t* idx_len,
                                  int32_t K_max, int32_t B, int32_t Q, int32_t H, int32_t R, int32_t max_cache_len,
                                  float scale, int32_t num_splits, const uint16_t* w_v, int32_t D, float* out,
                                  float* lse, void* stream) {
   if (!w_v) return MLA_ERR_NULL;
   if ((idx == nullptr) != (idx_len == nullptr)) return MLA_ERR_NULL;
   if (!supported(H, D, R)) return MLA_ERR_SHAPE;
-  return attn_common(q_abs, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, idx != nullptr, B, Q, H, R,
-                     max_cache_len, scale, num_splits, nullptr, lse, nullptr, 0, stream, w_v, out, true);
+  return attn_common(q_abs, q_abs_lo, cache, cache_batch_stride, cache_len, idx, idx_len, K_max, idx != nullptr, B,
+                     Q, H, R, max_cache_len, scale, num_splits, nullptr, lse, nullptr, 0, stream, w_v, out, true);
 }
 
 int mla_stream_read(const void* src, size_t bytes, uint32_t never, uint32_t* sink, void* stream) {

@@ -11,6 +11,7 @@ constexpr int kMaxSplits = 1024;
 
 struct AttnArgs {
   const uint16_t* q_abs;          // [B][Q][H][R] bf16
+  const uint16_t* q_abs_lo;       // [B][Q][H][R] bf16 second term of the absorbed query, or null
   const uint8_t* cache;           // latent rows (bytes)
   int64_t cache_bstride_bytes;    // bytes between sequences
   const int32_t* cache_len;       // [B]
@@ -30,7 +31,9 @@ struct AttnArgs {
 
 // queries one workgroup of the split kernel takes: dense calls with an even number of queries
 // per sequence pair adjacent queries, so one run of tiles serves both (with an odd count the lone
-// query's workgroup would cost a pair's time for one query's work)
+// query's workgroup would cost a pair's time for one query's work).  Split counts are planned
+// with this form; a call given the second query term runs every query alone (the pair form has
+// no registers for a second term) with the same split count.
 inline int queries_per_wg(bool indexed, int32_t Q) { return !indexed && Q % 2 == 0 ? 2 : 1; }
 // workgroups per (sequence, head group, split)
 inline int32_t query_units(bool indexed, int32_t Q) { return queries_per_wg(indexed, Q) == 2 ? (Q + 1) / 2 : Q; }
@@ -116,8 +119,8 @@ struct NaiveArgs {
 hipError_t launch_expand_kv(const ExpandArgs& a, hipStream_t stream);
 hipError_t launch_naive_attn(const NaiveArgs& a, hipStream_t stream);
 
-hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, int rows, int H,
-                           float prescale, hipStream_t stream);
+hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_k, uint16_t* q_abs, uint16_t* q_abs_lo, int rows,
+                           int H, float prescale, hipStream_t stream);
 hipError_t launch_up_v(const float* o_lat, const uint16_t* w_v, float* out, int rows, int H, int cus,
                        hipStream_t stream);
 

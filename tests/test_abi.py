@@ -46,28 +46,29 @@ def test_host_validation_without_device(L):
     vp = ctypes.c_void_p
     fake = vp(0x1000)
     # null pointers and shapes are rejected before any device call
-    assert L.mla_absorb_q(None, fake, fake, 1, 64, 256, 512, 1.0, None) == binding.MLA_ERR_NULL
-    assert L.mla_absorb_q(fake, fake, fake, 1, 64, 128, 512, 1.0, None) == binding.MLA_ERR_SHAPE
-    assert L.mla_absorb_q(fake, fake, fake, 1, 40, 256, 512, 1.0, None) == binding.MLA_ERR_SHAPE  # H % 16 != 0
-    assert L.mla_absorb_q(fake, fake, fake, 0, 64, 256, 512, 1.0, None) == binding.MLA_ERR_SHAPE
-    assert L.mla_absorb_q(fake, fake, fake, 1, 64, 256, 512, float("nan"), None) == binding.MLA_ERR_ARG
+    assert L.mla_absorb_q(None, fake, fake, None, 1, 64, 256, 512, 1.0, None) == binding.MLA_ERR_NULL
+    assert L.mla_absorb_q(fake, fake, fake, None, 1, 64, 128, 512, 1.0, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_absorb_q(fake, fake, fake, None, 1, 40, 256, 512, 1.0, None) == binding.MLA_ERR_SHAPE  # H % 16 != 0
+    assert L.mla_absorb_q(fake, fake, fake, None, 0, 64, 256, 512, 1.0, None) == binding.MLA_ERR_SHAPE
+    assert L.mla_absorb_q(fake, fake, fake, None, 1, 64, 256, 512, float("nan"), None) == binding.MLA_ERR_ARG
     assert L.mla_up_v(fake, None, fake, 1, 64, 256, 512, None) == binding.MLA_ERR_NULL
     assert L.mla_up_v(fake, fake, fake, 1, 64, 256, 256, None) == binding.MLA_ERR_SHAPE
     a = dict(q=fake, c=fake, st=512 * 100, cl=fake)
-    assert L.mla_latent_attn(fake, fake, 51200, None, 1, 1, 64, 512, 100, 0.0625, 0, fake, None, None, 0, None) \
+    assert L.mla_latent_attn(fake, None, fake, 51200, None, 1, 1, 64, 512, 100, 0.0625, 0, fake, None, None, 0, None) \
         == binding.MLA_ERR_NULL
-    assert L.mla_latent_attn(fake, fake, 51200, fake, 1, 1, 64, 512, 100, 0.0625, -1, fake, None, None, 0, None) \
+    assert L.mla_latent_attn(fake, None, fake, 51200, fake, 1, 1, 64, 512, 100, 0.0625, -1, fake, None, None, 0, None) \
         == binding.MLA_ERR_ARG
     # batch stride shorter than max_cache_len rows
-    assert L.mla_latent_attn(fake, fake, 512 * 99, fake, 1, 1, 64, 512, 100, 0.0625, 0, fake, None, None, 0, None) \
+    assert L.mla_latent_attn(fake, None, fake, 512 * 99, fake,
+                             1, 1, 64, 512, 100, 0.0625, 0, fake, None, None, 0, None) \
         == binding.MLA_ERR_ARG
-    assert L.mla_latent_attn(fake, fake, 51200, fake, 1, 1, 64, 512, 100, -1.0, 0, fake, None, None, 0, None) \
+    assert L.mla_latent_attn(fake, None, fake, 51200, fake, 1, 1, 64, 512, 100, -1.0, 0, fake, None, None, 0, None) \
         == binding.MLA_ERR_ARG
-    assert L.mla_latent_attn(fake, fake, 51200, fake, 1, 4, 64, 512, 3, 0.0625, 0, fake, None, None, 0, None) \
+    assert L.mla_latent_attn(fake, None, fake, 51200, fake, 1, 4, 64, 512, 3, 0.0625, 0, fake, None, None, 0, None) \
         == binding.MLA_ERR_ARG
-    assert L.mla_latent_attn_indexed(fake, fake, 51200, fake, None, fake, 8, 1, 1, 64, 512, 100, 0.0625, 0, fake,
+    assert L.mla_latent_attn_indexed(fake, None, fake, 51200, fake, None, fake, 8, 1, 1, 64, 512, 100, 0.0625, 0, fake,
                                      None, None, 0, None) == binding.MLA_ERR_NULL
-    assert L.mla_latent_attn_indexed(fake, fake, 51200, fake, fake, fake, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake,
+    assert L.mla_latent_attn_indexed(fake, None, fake, 51200, fake, fake, fake, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake,
                                      None, None, 0, None) == binding.MLA_ERR_ARG
 
 
@@ -146,14 +147,15 @@ def test_append_host_validation(L):
 def test_fused_up_projection_host_validation(L):
     fake = ctypes.c_void_p(0x1000)
     f = L.mla_latent_attn_up_v
-    # args: q_abs cache stride cache_len idx idx_len K_max B Q H R max_len scale splits w_v D out lse ws bytes stream
-    ok = [fake, fake, 51200, fake, None, None, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake, 256, fake, None, fake, 1 << 30,
-          None]
+    # args: q_abs q_abs_lo cache stride cache_len idx idx_len K_max B Q H R max_len scale splits w_v D out lse ws
+    # bytes stream
+    ok = [fake, None, fake, 51200, fake, None, None, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake, 256, fake, None, fake,
+          1 << 30, None]
 
     def call(**kw):
         a = list(ok)
-        names = ["q", "c", "st", "cl", "idx", "idx_len", "K", "B", "Q", "H", "R", "L", "scale", "s", "w_v", "D", "out",
-                 "lse", "ws", "wsb", "stream"]
+        names = ["q", "q_lo", "c", "st", "cl", "idx", "idx_len", "K", "B", "Q", "H", "R", "L", "scale", "s", "w_v", "D",
+                 "out", "lse", "ws", "wsb", "stream"]
         for k, v in kw.items():
             a[names.index(k)] = v
         return f(*a)
@@ -178,10 +180,10 @@ def test_fused_up_projection_host_validation(L):
 def test_noalloc_host_validation(L):
     fake = ctypes.c_void_p(0x1000)
     f = L.mla_latent_attn_up_v_noalloc
-    # args: q_abs cache stride cache_len idx idx_len K_max B Q H R max_len scale splits w_v D out lse stream
-    ok = [fake, fake, 51200, fake, None, None, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake, 256, fake, None, None]
-    names = ["q", "c", "st", "cl", "idx", "idx_len", "K", "B", "Q", "H", "R", "L", "scale", "s", "w_v", "D", "out",
-             "lse", "stream"]
+    # args: q_abs q_abs_lo cache stride cache_len idx idx_len K_max B Q H R max_len scale splits w_v D out lse stream
+    ok = [fake, None, fake, 51200, fake, None, None, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake, 256, fake, None, None]
+    names = ["q", "q_lo", "c", "st", "cl", "idx", "idx_len", "K", "B", "Q", "H", "R", "L", "scale", "s", "w_v", "D",
+             "out", "lse", "stream"]
 
     def call(**kw):
         a = list(ok)
@@ -209,6 +211,26 @@ def test_noalloc_host_validation(L):
     with pytest.raises(ValueError):
         binding.mla_latent_attn_up_v_noalloc(_bf(1, 1, 64, 512), _bf(1, 40, 512), _i32(1), 40, 0.0625,
                                              _bf(64, 256, 512), None)
+
+
+def test_second_query_term_host_validation(L):
+    # a second query term must match the first's dtype and shape; checked before any device use
+    import torch
+    qa, c, cl, wv = _bf(1, 1, 64, 512), _bf(1, 40, 512), _i32(1), _bf(64, 256, 512)
+    with pytest.raises(ValueError):
+        binding.mla_latent_attn(qa, c, cl, 40, 0.0625, q_abs_lo=_bf(1, 1, 64, 256))
+    with pytest.raises(TypeError):
+        binding.mla_latent_attn(qa, c, cl, 40, 0.0625, q_abs_lo=torch.zeros(1, 1, 64, 512))
+    with pytest.raises(ValueError):
+        binding.mla_latent_attn_up_v(qa, c, cl, 40, 0.0625, wv, q_abs_lo=_bf(2, 1, 64, 512))
+    with pytest.raises(ValueError):
+        binding.mla_latent_attn_indexed(qa, c, cl, _i32(1, 1, 8), _i32(1, 1), 40, 0.0625, q_abs_lo=_bf(1, 1, 48, 512))
+    with pytest.raises(ValueError):
+        binding.mla_absorb_q(_bf(1, 64, 256), _bf(64, 256, 512), q_abs_lo=_bf(1, 64, 256))
+    # the C ABI takes NULL for the second term and validates the rest as before
+    fake = ctypes.c_void_p(0x1000)
+    assert L.mla_latent_attn_up_v(None, fake, fake, 51200, fake, None, None, 0, 1, 1, 64, 512, 100, 0.0625, 0, fake,
+                                  256, fake, None, fake, 1 << 30, None) == binding.MLA_ERR_NULL
 
 
 def test_stream_read_host_validation(L):

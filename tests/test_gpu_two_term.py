@@ -1,0 +1,123 @@
+"""GPU parity of the two-term absorbed query, called through the C ABI.
+
+mla_absorb_q can write the rounding remainder of q~ as a second bf16 term (q_abs_lo), and the
+attention calls then score with c_j . (q_abs + q_abs_lo) (page "Module 05 -- MLA: Compressing
+Per-Token History", section 3: the score of a cached latent is its dot product with the absorbed
+query; the two terms carry that query to about 2^-17 of its size instead of bf16's 2^-9).
+
+* absorb: the first term keeps its bits, the second is below half a bf16 step of the first, and
+  their sum is within 2^-16 of the exact q~ plus the fp32 accumulation bound.
+* attention: given two-term queries drawn on the CPU from the oracle's q~ (rounded there), the
+  calls match the oracle run on the sum of the two terms, at every output row; dense and indexed
+  calls with the same positions and split count give the same bits, and so do the fused, the
+  separate and the no-allocation calls.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_cache_absorb_amd import binding, workloads as wl
+from tests.gpu_util import assert_parity, bf16, bits, i32
+
+pytestmark = pytest.mark.gpu
+
+F = oracle.bf16_bits_to_f64
+to_bf16 = oracle.latent_append.f64_to_bf16_bits
+
+
+def two_term_bits(q_exact):
+    """q~ (fp64) -> (hi, lo) bf16 bit arrays: hi the nearest bf16, lo the nearest bf16 of the rest."""
+    hi = to_bf16(q_exact)
+    return hi, to_bf16(q_exact - F(hi))
+
+
+@pytest.mark.parametrize("rows,prescale", [(1, 1.0), (37, 1.0), (130, 1.0), (33, 1.0 / 16)])
+def test_absorb_second_term(rows, prescale):
+    w = wl.make_workload(wl.make_spec(rows, 1, 1, workload_id=1300 + rows))
+    q, wk = bf16(w.q), bf16(w.w_k)
+    one = binding.mla_absorb_q(q, wk, prescale=prescale)
+    hi, lo = binding.mla_absorb_q(q, wk, prescale=prescale, lo=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(hi), bits(one))
+    h, l = F(bits(hi)), F(bits(lo))
+    assert np.isfinite(h).all() and np.isfinite(l).all()
+    # the remainder of a nearest rounding is at most half a step: 2^-8 of |hi| at most (rounded)
+    assert (np.abs(l) <= 2.0 ** -8 * np.abs(h)).all()
+    ref = oracle.absorbed_query(w.q, w.w_k) * prescale
+    # sum over d of |U^K[d, r]| |q[d]|: the scale of the fp32 accumulation error (256 exact products)
+    s_abs = oracle.absorbed_query(w.q & np.uint16(0x7FFF), w.w_k & np.uint16(0x7FFF)) * prescale
+    bound = 2.0 ** -16 * np.abs(ref) + 256 * 2.0 ** -24 * s_abs
+    err = np.abs(h + l - ref)
+    print(f"absorb two-term rows={rows}: max err/bound = {float((err / bound).max()):.3f}, "
+          f"one-term max err/bound = {float((np.abs(h - ref) / bound).max()):.1f}", flush=True)
+    assert (err <= bound).all()
+
+
+CASES = [
+    # (B, Q, L, min_len, n_index, heads, splits)
+    (3, 1, 700, 200, 0, 64, 0),     # decode, automatic split count
+    (2, 2, 500, 100, 0, 64, 3),     # even Q: every query in a workgroup of its own
+    (2, 3, 400, 150, 0, 128, 2),    # odd Q, two head groups
+    (2, 4, 600, 300, 100, 64, 3),   # indexed
+    (4, 1, 1000, 1000, 0, 48, 1),   # one split, a partial head group
+    (2, 1, 5000, 3000, 0, 64, 11),  # more than eight splits
+]
+
+
+@pytest.mark.parametrize("B,Q,L,min_len,n_index,heads,splits", CASES)
+def test_two_term_attention_matches_oracle(B, Q, L, min_len, n_index, heads, splits):
+    spec = wl.make_spec(B, Q, L, min_cache_len=min_len, n_index=n_index, heads=heads, spike_frac=0.01,
+                        spike_scale=8.0, workload_id=1320 + B * 7 + Q + heads)
+    w = wl.make_workload(spec)
+    print(f"two-term B={B} Q={Q} L={L} H={heads} splits={splits}", flush=True)
+    hi, lo = two_term_bits(oracle.absorbed_query(w.q, w.w_k))
+    qh, ql, c, cl, wv = bf16(hi), bf16(lo), bf16(w.cache), i32(w.cache_len), bf16(w.w_v)
+    Lmax = int(w.cache.shape[1])
+    idx = idx_len = None
+    if w.idx is not None:
+        idx, idx_len = i32(w.idx), i32(w.idx_len)
+        o_lat, lse = binding.mla_latent_attn_indexed(qh, c, cl, idx, idx_len, Lmax, w.scale, splits, q_abs_lo=ql)
+    else:
+        o_lat, lse = binding.mla_latent_attn(qh, c, cl, Lmax, w.scale, splits, q_abs_lo=ql)
+    out_s = binding.mla_up_v(o_lat, wv)
+    out_f, lse_f = binding.mla_latent_attn_up_v(qh, c, cl, Lmax, w.scale, wv, idx, idx_len, splits, q_abs_lo=ql)
+    out_n = torch.empty_like(out_f)
+    lse_n = torch.empty_like(lse_f)
+    binding.mla_latent_attn_up_v_noalloc(qh, c, cl, Lmax, w.scale, wv, out_n, lse_n, idx, idx_len, splits,
+                                         q_abs_lo=ql)
+    torch.cuda.synchronize()
+    # fused, separate and no-allocation calls: the same kernels in the same order
+    for a, b, what in ((out_f, out_s, "fused / separate out"), (lse_f, lse, "fused / separate lse"),
+                       (out_n, out_f, "no-alloc / fused out"), (lse_n, lse_f, "no-alloc / fused lse")):
+        n = int((a.view(torch.int32) != b.view(torch.int32)).sum())
+        assert n == 0, f"{what}: {n} values differ"
+    o_ref, lse_ref = oracle.latent_attention(F(hi) + F(lo), w.cache, w.cache_len, w.scale, idx=w.idx,
+                                             idx_len=w.idx_len)
+    assert_parity(o_lat.cpu().numpy(), o_ref, "two-term o_lat, every row")
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=1e-3)
+    ref = oracle.up_project(o_ref, w.w_v)
+    assert_parity(out_f.cpu().numpy(), ref, "two-term fused out, every row")
+
+
+def test_two_term_dense_equals_indexed_over_every_causal_position():
+    # the same kernel with the same split boundaries: listing every causal position gives the bits
+    # of the dense call
+    B, Q, L = 2, 3, 600
+    w = wl.make_workload(wl.make_spec(B, Q, L, min_cache_len=250, workload_id=1340))
+    hi, lo = two_term_bits(oracle.absorbed_query(w.q, w.w_k))
+    qh, ql, c, cl = bf16(hi), bf16(lo), bf16(w.cache), i32(w.cache_len)
+    idx = np.zeros((B, Q, L), np.int32)
+    idx_len = np.zeros((B, Q), np.int32)
+    for b in range(B):
+        for i in range(Q):
+            n = int(w.cache_len[b]) - Q + i + 1
+            idx[b, i, :n] = np.arange(n)
+            idx_len[b, i] = n
+    for splits in (1, 4):
+        o_d, l_d = binding.mla_latent_attn(qh, c, cl, L, w.scale, splits, q_abs_lo=ql)
+        o_i, l_i = binding.mla_latent_attn_indexed(qh, c, cl, i32(idx), i32(idx_len), L, w.scale, splits,
+                                                   q_abs_lo=ql)
+        torch.cuda.synchronize()
+        assert torch.equal(o_d.view(torch.int32), o_i.view(torch.int32)), f"o_lat bits, {splits} splits"
+        assert torch.equal(l_d.view(torch.int32), l_i.view(torch.int32)), f"lse bits, {splits} splits"
