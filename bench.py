@@ -680,15 +680,67 @@ def time_qlen_sweep(steps: int = 20, warmup: int = 20):
     return {"batch": B, "cache_len": L, "rows": rows}
 
 
-def time_other_configs(steps: int = 20, warmup: int = 20):
-    """The headline attention call (mla_latent_attn / mla_latent_attn_indexed) on the two other
-    full-size workloads: decode of 4 sequences of 131,072 positions with 1% of each sequence's
-    latents scaled by 8 (with one and with two query terms; the second is what that workload needs
-    to meet the parity bar), and the indexed verification of 32 sequences (4 queries, lengths
-    uniform in [4096, 65536]) over 2,048 positions drawn per query from the committed prefix plus
-    the causal tail; and the headline decode shape with one and with two query terms.  Inputs are drawn on the GPU with those shapes and structures (timing only;
-    the parity tests use the seeded CPU workloads).  Two input sets alternate; each call is timed
-    over `steps` back-to-back calls (the median of five chunks, chunked_ms)."""
+def time_query_terms(name: str, terms=(1, 2), steps: int = 20, warmup: int = 20, gen=None):
+    """The dense attention call (mla_latent_attn) at a full-size decode workload, with the absorbed
+    query in one and/or two bf16 terms.  decode_b4_l131072_spiked: 4 sequences of 131,072
+    positions with 1% of each sequence's latents scaled by 8 (the workload that needs the second
+    term to meet the parity bar); decode_b32_l8192: the headline decode shape.  Inputs are drawn on
+    the GPU with those shapes and structures (timing only; the parity tests use the seeded CPU
+    workloads); the second term is a remainder below half a bf16 step of the first.  Two input
+    sets alternate; each call is timed over `steps` back-to-back calls (the median of five chunks,
+    chunked_ms)."""
+    import torch
+    from mla_latent_cache_absorb_amd import binding, workloads as wl
+
+    dev = torch.device("cuda:0")
+    if gen is None:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0xC3)
+    H, R = wl.HEADS, wl.LATENT
+    B, Q, L, spiked = {"decode_b4_l131072_spiked": (4, 1, 131072, True),
+                       "decode_b32_l8192": (32, 1, 8192, False)}[name]
+    sets = []
+    for _ in range(2):
+        c = torch.randn(B, L, R, generator=gen, device=dev)
+        if spiked:
+            for b in range(B):
+                pos = torch.randperm(L, generator=gen, device=dev)[: round(0.01 * L)]
+                c[b, pos] *= 8.0
+        qa = (torch.randn(B, Q, H, R, generator=gen, device=dev) * 0.5 ** 0.5).to(torch.bfloat16)
+        q_lo = (qa.float() * torch.randn(qa.shape, generator=gen, device=dev) * 2.0 ** -10).to(torch.bfloat16)
+        sets.append((c.to(torch.bfloat16), qa, q_lo))
+        del c
+    cl = torch.full((B,), L, dtype=torch.int32, device=dev)
+    o = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, L, 0), 1), dtype=torch.uint8, device=dev)
+    lat = B * L * R * 2
+    out = []
+    for nt in terms:
+        def call(k):
+            c, qa, q_lo = sets[k % 2]
+            binding.mla_latent_attn(qa, c, cl, L, wl.SCALE, 0, o_lat=o, lse=lse, workspace=ws,
+                                    q_abs_lo=q_lo if nt == 2 else None)
+        warm_up(call, warmup)
+        ms, ms_med = chunked_ms(call, steps)
+        gbs = lat / (ms * 1e-3) / 1e9
+        out.append({"workload": name, "call": "mla_latent_attn", "query_terms": nt, "ms": round(ms, 5),
+                    "median_chunk_ms": round(ms_med, 5), "splits": binding.mla_latent_attn_num_splits(B, Q, H, L, 0),
+                    "latent_bytes": lat, "GB/s": round(gbs, 2), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    del sets, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_other_configs(steps: int = 20, warmup: int = 20, two_term: bool = True):
+    """The headline attention call on the two other full-size workloads: the spiked decode of 4
+    sequences of 131,072 positions (time_query_terms: with one query term, and with two unless
+    two_term is False), and mla_latent_attn_indexed on the indexed verification of 32 sequences
+    (4 queries, lengths uniform in [4096, 65536]) over 2,048 positions drawn per query from the
+    committed prefix plus the causal tail; then, with two_term, the headline decode shape with one
+    and two query terms.  Inputs are drawn on the GPU with those shapes and structures (timing
+    only; the parity tests use the seeded CPU workloads).  Two input sets alternate; each call is
+    timed over `steps` back-to-back calls (the median of five chunks, chunked_ms)."""
     import torch
     from mla_latent_cache_absorb_amd import binding, workloads as wl
 
@@ -696,67 +748,12 @@ def time_other_configs(steps: int = 20, warmup: int = 20):
     gen = torch.Generator(device=dev)
     gen.manual_seed(0xC3)
     H, R = wl.HEADS, wl.LATENT
-    out = []
 
     def run(call, nsets):
         warm_up(lambda k: call(k % nsets), warmup)
         return chunked_ms(lambda k: call(k % nsets), steps)
 
-    # decode, 4 x 131072, spiked
-    B, Q, L = 4, 1, 131072
-    sets = []
-    for _ in range(2):
-        c = torch.randn(B, L, R, generator=gen, device=dev)
-        for b in range(B):
-            pos = torch.randperm(L, generator=gen, device=dev)[: round(0.01 * L)]
-            c[b, pos] *= 8.0
-        sets.append((c.to(torch.bfloat16), (torch.randn(B, Q, H, R, generator=gen, device=dev) * 0.5 ** 0.5)
-                     .to(torch.bfloat16)))
-        del c
-    cl = torch.full((B,), L, dtype=torch.int32, device=dev)
-    o = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, L, 0), 1), dtype=torch.uint8, device=dev)
-    # the second query term (what the two-term call reads beside the first): a remainder below
-    # half a bf16 step of the first term
-    q_lo = [(s[1].float() * torch.randn(s[1].shape, generator=gen, device=dev) * 2.0 ** -10).to(torch.bfloat16)
-            for s in sets]
-    lat = B * L * R * 2
-    for two_term in (False, True):
-        lo = (lambda k: q_lo[k]) if two_term else (lambda k: None)
-        ms, ms_med = run(lambda k: binding.mla_latent_attn(sets[k][1], sets[k][0], cl, L, wl.SCALE, 0, o_lat=o,
-                                                           lse=lse, workspace=ws, q_abs_lo=lo(k)), 2)
-        gbs = lat / (ms * 1e-3) / 1e9
-        out.append({"workload": "decode_b4_l131072_spiked", "call": "mla_latent_attn",
-                    "query_terms": 2 if two_term else 1, "ms": round(ms, 5), "median_chunk_ms": round(ms_med, 5),
-                    "splits": binding.mla_latent_attn_num_splits(B, Q, H, L, 0), "latent_bytes": lat,
-                    "GB/s": round(gbs, 2), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
-    del sets, o, lse, ws, q_lo
-    torch.cuda.empty_cache()
-
-    # decode, 32 x 8192, the attention call with one and with two query terms (the cost of the
-    # second term at the headline decode shape)
-    B, Q, L = 32, 1, 8192
-    sets = [((torch.randn(B, L, R, generator=gen, device=dev)).to(torch.bfloat16),
-             (torch.randn(B, Q, H, R, generator=gen, device=dev) * 0.5 ** 0.5).to(torch.bfloat16)) for _ in range(2)]
-    q_lo = [(s[1].float() * torch.randn(s[1].shape, generator=gen, device=dev) * 2.0 ** -10).to(torch.bfloat16)
-            for s in sets]
-    cl = torch.full((B,), L, dtype=torch.int32, device=dev)
-    o = torch.empty((B, Q, H, R), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(binding.mla_latent_attn_workspace_size(B, Q, H, R, L, 0), 1), dtype=torch.uint8, device=dev)
-    lat = B * L * R * 2
-    for two_term in (False, True):
-        lo = (lambda k: q_lo[k]) if two_term else (lambda k: None)
-        ms, ms_med = run(lambda k: binding.mla_latent_attn(sets[k][1], sets[k][0], cl, L, wl.SCALE, 0, o_lat=o,
-                                                           lse=lse, workspace=ws, q_abs_lo=lo(k)), 2)
-        gbs = lat / (ms * 1e-3) / 1e9
-        out.append({"workload": "decode_b32_l8192", "call": "mla_latent_attn", "query_terms": 2 if two_term else 1,
-                    "ms": round(ms, 5), "median_chunk_ms": round(ms_med, 5),
-                    "splits": binding.mla_latent_attn_num_splits(B, Q, H, L, 0), "latent_bytes": lat,
-                    "GB/s": round(gbs, 2), "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)})
-    del sets, o, lse, ws, q_lo
-    torch.cuda.empty_cache()
+    out = time_query_terms("decode_b4_l131072_spiked", (1, 2) if two_term else (1,), steps, warmup, gen)
 
     # indexed verification, 32 x 4, ragged
     B, Q, Lmax, n_index = 32, 4, 65536, 2048
@@ -795,6 +792,8 @@ def time_other_configs(steps: int = 20, warmup: int = 20):
                 "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})
     del sets, o, lse, ws, idx, idx_len
     torch.cuda.empty_cache()
+    if two_term:
+        out += time_query_terms("decode_b32_l8192", (1, 2), steps, warmup, gen)
     return out
 
 
@@ -844,6 +843,10 @@ def main():
     ap.add_argument("--no-crossover", action="store_true")
     ap.add_argument("--no-qlen-sweep", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--no-two-term", action="store_true",
+                    help="other configs: leave out the two-term query timings (one kernel per workload per run)")
+    ap.add_argument("--query-terms-only", metavar="WORKLOAD", default=None,
+                    help="only the attention call at this decode workload with one and two query terms")
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true")
     ap.add_argument("--read-ceiling-only", action="store_true",
@@ -895,7 +898,10 @@ def main():
         print(json.dumps({"latency_b1": time_latency()}), flush=True)
         return
     if args.other_configs_only:
-        print(json.dumps({"other_configs": time_other_configs()}), flush=True)
+        print(json.dumps({"other_configs": time_other_configs(two_term=not args.no_two_term)}), flush=True)
+        return
+    if args.query_terms_only:
+        print(json.dumps({"query_terms": time_query_terms(args.query_terms_only)}), flush=True)
         return
     if args.qlen_sweep_only:
         print(json.dumps({"qlen_sweep": time_qlen_sweep()}), flush=True)
