@@ -294,6 +294,52 @@ __device__ __forceinline__ void merge_one_group8(const MergeGroup (&g)[2], int S
   }
 }
 
+// merge_one_group8 for NB blocks of four latents whose splits share their (m, l) (the blocks of one
+// row): merge_group's steps, then merge_fold into the empty state, for each block, with the
+// split weights computed once instead of once a block.  Each value goes through the same
+// operations in the same order as in merge_splits8, so the bits are its bits.
+template <int NB>
+__device__ __forceinline__ void merge_one_group8_blocks(const float (&mm)[8], const float (&ll)[8],
+                                                        const f32x4 (&v)[NB][8], int S, float* lse2,
+                                                        f32x4 (&out)[NB]) {
+  float Mg = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (k < S && ll[k] > 0.f) Mg = fmaxf(Mg, mm[k]);
+  float M = -INFINITY, L = 0.f;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (Mg != -INFINITY) {
+    float wl[8], Lg = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = (k < S && ll[k] > 0.f) ? __builtin_amdgcn_exp2f(mm[k] - Mg) : 0.f;
+      wl[k] = w * ll[k];
+      Lg = __builtin_fmaf(w, ll[k], Lg);
+    }
+    // merge_fold of (Mg, Lg, group sum) into (M, L, acc) = (-inf, 0, 0)
+    const float Mn = fmaxf(M, Mg);
+    const float bw = __builtin_amdgcn_exp2f(Mg - Mn);
+    L = __builtin_fmaf(Lg, bw, __builtin_fmaf(L, 0.f, 0.f));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[e] = __builtin_fmaf(wl[k], v[b][k][e], g[e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[b][e] = __builtin_fmaf(g[e], bw, __builtin_fmaf(acc[b][e], 0.f, 0.f));
+    }
+    M = Mn;
+  }
+  // __builtin_amdgcn_logf is the hardware base-2 logarithm
+  *lse2 = M + __builtin_amdgcn_logf(L);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) out[b] = acc[b] * (1.0f / L);
+}
+
 // merge slots to load for S splits in one group (2, 4 or 8)
 __host__ __device__ constexpr int merge_slots(int S) { return S <= 2 ? 2 : S <= 4 ? 4 : 8; }
 

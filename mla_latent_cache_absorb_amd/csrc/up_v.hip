@@ -14,9 +14,9 @@
 // (given, or merged from the partials, the merging workgroup of half 0 also writing each row's
 // log-sum-exp) are staged in LDS as two bf16 terms (hi = bf16(x), lo = bf16(x - hi)) and read as
 // the B operand of two MFMA 16x16x32 per k-step, so the result keeps about 16 bits of the latent.
-// The next pass's loads are issued before this pass's products.  The workgroups of one head run
-// on one XCD.  The time is set by the bytes each CU pulls in, not by HBM: half of U_h^V (128 KiB)
-// and the latents or partials of its rows.
+// The first pass's loads are issued before U_h^V's, the next pass's before this pass's products.
+// The workgroups of one head run on one XCD.  The time is set by the bytes each CU pulls in, not
+// by HBM: half of U_h^V (128 KiB) and the latents or partials of its rows.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -59,30 +59,32 @@ __device__ __forceinline__ void fuse_load(FuseRaw<NS>& f, const uint16_t* po0, c
   }
 }
 
-// merge_splits8's steps for each chunk of a FuseRaw (one group, merge_one_group8; the slots not
-// loaded filled as in merge_load8), so the bits are those of merge_splits8
+// merge_splits8's steps for the two chunks of a FuseRaw (one group, merge_one_group8_blocks over
+// their four blocks of four latents; the slots not loaded weigh nothing, as merge_slot_empty's), so
+// the bits are those of merge_splits8
 template <int NS>
 __device__ __forceinline__ void fuse_merge(const FuseRaw<NS>& f, int S, float* lse2, f32x4 (&out)[2][2]) {
+  float mm[8], ll[8];
+  f32x4 v[4][8];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    MergeGroup g[2];
+  for (int k = 0; k < 8; ++k) {
+    mm[k] = k < NS ? f.ml[k].x : 0.f;
+    ll[k] = k < NS ? f.ml[k].y : 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (k >= NS) {
-          merge_slot_empty(g[h], k);
-          continue;
-        }
-        g[h].mm[k] = f.ml[k].x;
-        g[h].ll[k] = f.ml[k].y;
-        g[h].v[k] = __builtin_convertvector(
-            (f16x4){f.v[c][k][4 * h], f.v[c][k][4 * h + 1], f.v[c][k][4 * h + 2], f.v[c][k][4 * h + 3]}, f32x4);
-      }
-    float chunk_lse2;  // the same for both chunks (it depends only on the splits' (m, l))
-    merge_one_group8(g, S, &chunk_lse2, out[c]);
-    if (c == 0) *lse2 = chunk_lse2;
+      for (int h = 0; h < 2; ++h)
+        v[2 * c + h][k] = k < NS ? __builtin_convertvector((f16x4){f.v[c][k][4 * h], f.v[c][k][4 * h + 1],
+                                                                    f.v[c][k][4 * h + 2], f.v[c][k][4 * h + 3]},
+                                                           f32x4)
+                                 : (f32x4){0.f, 0.f, 0.f, 0.f};
   }
+  f32x4 o[4];
+  merge_one_group8_blocks<4>(mm, ll, v, S, lse2, o);
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) out[c][h] = o[2 * c + h];
 }
 
 // LATENTS: the rows' fp32 latents are given (o_lat); otherwise they are merged from split-K
@@ -107,13 +109,6 @@ __global__ __launch_bounds__(kFuseThreads) void up_v_kernel(MergeUpArgs a) {
   const int d0 = half * kFuseHalf + 16 * wave;
   const int ql = lane & 15, g = lane >> 4;
 
-  // A operand: U_h^V row d0 + ql, latents 32s + 8g .. +7, in registers for the whole kernel
-  bf16x8 wa[16];
-  {
-    const uint16_t* wrow = a.w_v + ((size_t)h * kHeadDim + d0 + ql) * kLatent + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) wa[s] = *(const bf16x8*)(wrow + 32 * s);
-  }
 
   // with 16 rows a pass, thread t takes row t / 32 and its chunks of eight latents c and c + 32
   // (c = t % 32); with 8 rows a pass (a single pass), row t / 64 and chunk t % 64.  Loads issued
@@ -140,6 +135,17 @@ __global__ __launch_bounds__(kFuseThreads) void up_v_kernel(MergeUpArgs a) {
     }
   };
   if constexpr (AHEAD) issue(0);
+  // the first pass's latents or partials are requested before U_h^V (kept in that order by the
+  // scheduling barrier): the merge or the staging of the first pass, which needs only them, then
+  // runs while U_h^V is still arriving
+  __builtin_amdgcn_sched_barrier(0);
+  // A operand: U_h^V row d0 + ql, latents 32s + 8g .. +7, in registers for the whole kernel
+  bf16x8 wa[16];
+  {
+    const uint16_t* wrow = a.w_v + ((size_t)h * kHeadDim + d0 + ql) * kLatent + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) wa[s] = *(const bf16x8*)(wrow + 32 * s);
+  }
 
   for (int p = 0; p < a.passes; ++p) {
     const int prow0 = row0 + p * rpp;
