@@ -737,10 +737,15 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(AttnArgs a) 
   const size_t row = (size_t)blockIdx.x * kCombineRows + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int t = threadIdx.x & 63;
+  // at most eight splits: one group, merged as merge_splits8 does (merge_one_group8_blocks)
+  MergeGroup g[2];
+  merge_load8<NS>(g, a.part_o + row * kLatent + 8 * t, a.part_ml + 2 * row, rows * kLatent, 2 * rows, a.num_splits,
+                  0);
+  const f32x4 v[2][8] = {{g[0].v[0], g[0].v[1], g[0].v[2], g[0].v[3], g[0].v[4], g[0].v[5], g[0].v[6], g[0].v[7]},
+                         {g[1].v[0], g[1].v[1], g[1].v[2], g[1].v[3], g[1].v[4], g[1].v[5], g[1].v[6], g[1].v[7]}};
   float lse2;
   f32x4 o[2];
-  merge_splits8<NS>(a.part_o + row * kLatent + 8 * t, a.part_ml + 2 * row, rows * kLatent, 2 * rows, a.num_splits,
-                    &lse2, o);
+  merge_one_group8_blocks<2>(g[0].mm, g[0].ll, v, a.num_splits, &lse2, o);
   float* dst = a.o_lat + row * kLatent + 8 * t;
   *(f32x4*)dst = o[0];
   *(f32x4*)(dst + 4) = o[1];
