@@ -11,6 +11,8 @@ query; the two terms carry that query to about 2^-17 of its size instead of bf16
   calls match the oracle run on the sum of the two terms, at every output row; dense and indexed
   calls with the same positions and split count give the same bits, and so do the fused, the
   separate and the no-allocation calls.
+* at the four full sizes, a second term of zeros gives the one-term call's bits (selection and
+  split boundaries included).
 """
 import numpy as np
 import pytest
@@ -121,3 +123,28 @@ def test_two_term_dense_equals_indexed_over_every_causal_position():
         torch.cuda.synchronize()
         assert torch.equal(o_d.view(torch.int32), o_i.view(torch.int32)), f"o_lat bits, {splits} splits"
         assert torch.equal(l_d.view(torch.int32), l_i.view(torch.int32)), f"lse bits, {splits} splits"
+
+
+@pytest.mark.parametrize("name", ["decode_b32_l8192", "verify_b16_q6_l32768", "decode_b4_l131072_spiked",
+                                  "indexed_verify_b32_q4_ragged"])
+def test_zero_second_term_gives_the_one_term_bits(name):
+    # at the full sizes and split counts: a second term of zeros adds +0 products to every score, so
+    # the two-term kernel (a workgroup per query) must give the one-term call's bits (the pair kernel
+    # where Q is even), selection included
+    print(f"zero second term {name}", flush=True)
+    w = wl.make_workload(name)
+    q_abs = binding.mla_absorb_q(bf16(w.q), bf16(w.w_k))
+    zero = torch.zeros_like(q_abs)
+    c, cl = bf16(w.cache), i32(w.cache_len)
+    Lmax = int(w.cache.shape[1])
+    if w.idx is not None:
+        idx, idx_len = i32(w.idx), i32(w.idx_len)
+        one = binding.mla_latent_attn_indexed(q_abs, c, cl, idx, idx_len, Lmax, w.scale)
+        two = binding.mla_latent_attn_indexed(q_abs, c, cl, idx, idx_len, Lmax, w.scale, q_abs_lo=zero)
+    else:
+        one = binding.mla_latent_attn(q_abs, c, cl, Lmax, w.scale)
+        two = binding.mla_latent_attn(q_abs, c, cl, Lmax, w.scale, q_abs_lo=zero)
+    torch.cuda.synchronize()
+    for a, b, what in ((one[0], two[0], "o_lat"), (one[1], two[1], "lse")):
+        n = int((a.view(torch.int32) != b.view(torch.int32)).sum())
+        assert n == 0, f"{name} {what}: {n} of {a.numel()} values differ"
