@@ -279,25 +279,11 @@ __device__ __forceinline__ void merge_splits8(const uint16_t* part_o, const floa
   for (int h = 0; h < 2; ++h) out[h] = acc[h] * (1.0f / L[h]);
 }
 
-// merge_splits8's steps for one group of slots already loaded (at most eight splits), so the bits
-// are those of merge_splits8
-__device__ __forceinline__ void merge_one_group8(const MergeGroup (&g)[2], int S, float* lse2, f32x4 (&out)[2]) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float M = -INFINITY, L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    MergePartial r;
-    if (merge_group(g[h], S, 0, r)) merge_fold(M, L, acc, r);
-    // __builtin_amdgcn_logf is the hardware base-2 logarithm
-    if (h == 0) *lse2 = M + __builtin_amdgcn_logf(L);
-    out[h] = acc * (1.0f / L);
-  }
-}
-
-// merge_one_group8 for NB blocks of four latents whose splits share their (m, l) (the blocks of one
-// row): merge_group's steps, then merge_fold into the empty state, for each block, with the
-// split weights computed once instead of once a block.  Each value goes through the same
-// operations in the same order as in merge_splits8, so the bits are its bits.
+// merge_splits8's steps for one group of slots already loaded (at most eight splits), for NB
+// blocks of four latents whose splits share their (m, l) (the blocks of one row): merge_group's
+// steps, then merge_fold into the empty state, for each block, with the split weights computed
+// once instead of once a block.  Each value goes through the same operations in the same order
+// as in merge_splits8, so the bits are its bits.
 template <int NB>
 __device__ __forceinline__ void merge_one_group8_blocks(const float (&mm)[8], const float (&ll)[8],
                                                         const f32x4 (&v)[NB][8], int S, float* lse2,
