@@ -58,6 +58,28 @@ def test_decode_step_in_a_graph():
     replay_and_check(step, [q_abs, o_lat, lse, out])
 
 
+def test_two_term_fused_decode_step_in_a_graph():
+    # the absorbed query in two bf16 terms, then the fused attention and up-projection
+    spec = wl.make_spec(4, 1, 3000, min_cache_len=1000, spike_frac=0.01, spike_scale=8.0, workload_id=902)
+    w = wl.make_workload(spec)
+    q, wk, wv, cache, cl = bf16(w.q), bf16(w.w_k), bf16(w.w_v), bf16(w.cache), i32(w.cache_len)
+    B, Q, H, D = w.q.shape
+    R = w.cache.shape[2]
+    q_abs = torch.empty((B, Q, H, R), dtype=torch.bfloat16, device=q.device)
+    q_lo = torch.empty_like(q_abs)
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device)
+    out = torch.empty((B, Q, H, D), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(binding.mla_latent_attn_up_v_workspace_size(B, Q, H, R, 3000), 1), dtype=torch.uint8,
+                     device=q.device)
+
+    def step():
+        binding.mla_absorb_q(q, wk, q_abs=q_abs, q_abs_lo=q_lo)
+        binding.mla_latent_attn_up_v(q_abs, cache, cl, 3000, spec.scale, wv, out=out, lse=lse, workspace=ws,
+                                     q_abs_lo=q_lo)
+
+    replay_and_check(step, [q_abs, q_lo, lse, out])
+
+
 def test_verify_step_with_indexer_and_append_in_a_graph():
     spec = wl.make_spec(2, 4, 2500, min_cache_len=1500, workload_id=901)
     w = wl.make_workload(spec)

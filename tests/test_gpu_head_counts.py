@@ -2,9 +2,10 @@
 groups of 64, and the last group of such a call is partial.
 
 * Latent attention (dense single-query, dense query pairs, odd Q, indexed; one split, the
-  automatic count, three splits) against the fp64 oracle's latent-space attention (page "Module 05
-  -- MLA: Compressing Per-Token History", section 3), with o_lat and lse written into views of
-  larger buffers whose tails hold a sentinel: nothing may be written past the last head's row.
+  automatic count, three splits; and with the absorbed query in two bf16 terms) against the fp64
+  oracle's latent-space attention (page "Module 05 -- MLA: Compressing Per-Token History", section
+  3), with o_lat and lse written into views of larger buffers whose tails hold a sentinel: nothing
+  may be written past the last head's row.
 * The whole path (absorb, attention, up-projection) and the fused call: bit-equal to each other,
   and sampled against the oracle's expanded form (sections 1 and 4).
 """
@@ -60,6 +61,33 @@ def test_partial_head_group_matches_oracle(H, B, Q, L, n_index, splits):
     assert bool((l_buf[lse.numel():] == SENTINEL).all()), "lse written past the last head's row"
     ref, lse_ref = oracle.latent_attention(F(qa), w.cache, w.cache_len, w.scale, idx=w.idx, idx_len=w.idx_len)
     assert_parity(o_lat.cpu().numpy(), ref, f"o_lat H{H}")
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=1e-3)
+
+
+@pytest.mark.parametrize("H,B,Q,L,n_index", CASES)
+def test_partial_head_group_two_term_query(H, B, Q, L, n_index):
+    # the two-term kernels (a workgroup per query) with a partial last group of heads: the second
+    # term is the first scaled by 2^-10 (exact), so the oracle's query is their exact sum
+    spec = wl.make_spec(B, Q, L, min_cache_len=L // 2, n_index=n_index, heads=H, workload_id=2650 + H + Q + B)
+    w = wl.make_workload(spec)
+    qa = wl.latent_query_bits(spec)
+    lo = oracle.latent_append.f64_to_bf16_bits(F(qa) * 2.0 ** -10)
+    print(f"two-term H={H} B={B} Q={Q} L={L} indexed={n_index > 0}", flush=True)
+    o_lat, o_buf = views_with_tail((B, Q, H, 512), 64 * 512)
+    lse, l_buf = views_with_tail((B, Q, H), 64)
+    q_abs, q_lo, c, cl = bf16(qa), bf16(lo), bf16(w.cache), i32(w.cache_len)
+    if n_index:
+        binding.mla_latent_attn_indexed(q_abs, c, cl, i32(w.idx), i32(w.idx_len), L, w.scale, 0, o_lat=o_lat,
+                                        lse=lse, q_abs_lo=q_lo)
+    else:
+        binding.mla_latent_attn(q_abs, c, cl, L, w.scale, 0, o_lat=o_lat, lse=lse, q_abs_lo=q_lo)
+    torch.cuda.synchronize()
+    assert bool((o_buf[o_lat.numel():] == SENTINEL).all()), "o_lat written past the last head's row"
+    assert bool((l_buf[lse.numel():] == SENTINEL).all()), "lse written past the last head's row"
+    np.testing.assert_array_equal(F(lo), F(qa) * 2.0 ** -10)
+    ref, lse_ref = oracle.latent_attention(F(qa) + F(lo), w.cache, w.cache_len, w.scale, idx=w.idx,
+                                           idx_len=w.idx_len)
+    assert_parity(o_lat.cpu().numpy(), ref, f"two-term o_lat H{H}")
     np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=1e-3)
 
 
