@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak
+WEIGHT_ROTATION_BYTES = 384 << 20   # weight copies a step rotates over: more than the Infinity Cache
 NSETS = 3
 
 
@@ -201,15 +202,26 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
                    binding.mla_latent_attn_up_v_workspace_size(B, Q, H, R, K_max, 0, indexed=indexed))
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    # Weights rotate over copies holding WEIGHT_ROTATION_BYTES or more, so that a step never finds
+    # its layer's W^UK / W^UV in the 256 MB Infinity Cache from an earlier step: in a model a
+    # layer's weights come back only after every other layer's weights and caches have streamed.
+    # (The caches' non-temporal stream leaves the cache to data that is reused, and three weight
+    # sets of 32 MiB would otherwise stay resident.)
+    wts = [(d["w_k"], d["w_v"]) for d in sets]
+    pair_bytes = wts[0][0].numel() * 2 + wts[0][1].numel() * 2
+    while len(wts) * pair_bytes < WEIGHT_ROTATION_BYTES:
+        wk, wv = wts[len(wts) % nsets]
+        wts.append((wk.clone(), wv.clone()))
+    nw = len(wts)
 
-    def attn_up_v(d):
-        binding.mla_latent_attn_up_v(q_abs, d["cache"], d["cache_len"], Lmax, w0.scale, d["w_v"], d.get("idx"),
+    def attn_up_v(d, s):
+        binding.mla_latent_attn_up_v(q_abs, d["cache"], d["cache_len"], Lmax, w0.scale, wts[s % nw][1], d.get("idx"),
                                      d.get("idx_len"), 0, out=out, lse=lse, workspace=workspace)
 
     def step(s):
         d = sets[s % nsets]
-        binding.mla_absorb_q(d["q"], d["w_k"], q_abs=q_abs)
-        attn_up_v(d)
+        binding.mla_absorb_q(d["q"], wts[s % nw][0], q_abs=q_abs)
+        attn_up_v(d, s)
 
     # no collector pauses inside the timed regions: it runs now, before the warm-up (run between the
     # warm-up and the timing, it would leave the device idle and the first timed steps below the
@@ -238,9 +250,9 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
     def one_stage(k, s):
         d = sets[s % nsets]
         if k == "absorb_q":
-            binding.mla_absorb_q(d["q"], d["w_k"], q_abs=q_abs)
+            binding.mla_absorb_q(d["q"], wts[s % nw][0], q_abs=q_abs)
         elif k == "latent_attn_up_v":
-            attn_up_v(d)
+            attn_up_v(d, s)
         elif k == "latent_attn" and indexed:
             binding.mla_latent_attn_indexed(q_abs, d["cache"], d["cache_len"], d["idx"], d["idx_len"], Lmax,
                                             w0.scale, 0, o_lat=o_lat, lse=lse, workspace=workspace)
@@ -248,7 +260,7 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
             binding.mla_latent_attn(q_abs, d["cache"], d["cache_len"], Lmax, w0.scale, 0, o_lat=o_lat, lse=lse,
                                     workspace=workspace)
         else:
-            binding.mla_up_v(o_lat, d["w_v"], out=out)
+            binding.mla_up_v(o_lat, wts[s % nw][1], out=out)
 
     stage, pct, stage_med = {}, {}, {}
     for k in ("absorb_q", "latent_attn_up_v", "latent_attn", "up_v"):
@@ -279,9 +291,9 @@ def time_path(name: str, steps: int, warmup: int, nsets: int):
         stage[k] = e0.elapsed_time(e1) / steps
         del graph
     gc.enable()
-    del sets
+    del sets, wts
     torch.cuda.empty_cache()
-    return dict(ms_step=ms_step, wall_s=wall, stage_ms=stage, stage_median_chunk_ms=stage_med, stage_pct_ms=pct,
+    return dict(weight_sets_rotated=nw, ms_step=ms_step, wall_s=wall, stage_ms=stage, stage_median_chunk_ms=stage_med, stage_pct_ms=pct,
                 splits=splits, workload=w0)
 
 
@@ -943,7 +955,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "q_len": Q, "cache_len": int(w.cache.shape[1]),
                    "heads": H, "head_dim": D, "latent": R, "softmax_scale": w.scale, "splits": r["splits"],
-                   "input_sets_rotated": NSETS, "parallelism": "none (1 GPU)"},
+                   "input_sets_rotated": NSETS, "weight_sets_rotated": r["weight_sets_rotated"],
+                   "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "mla_latent_attn (split kernel + merge)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

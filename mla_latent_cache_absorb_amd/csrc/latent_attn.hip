@@ -198,8 +198,9 @@ __device__ __forceinline__ void copy_partial_block(const AttnArgs& a, size_t fir
 }
 
 // LO: the absorbed query comes as two bf16 terms (q_abs + q_abs_lo) and each score takes both
-// products into one fp32 accumulator
-template <bool INDEXED, bool LO>
+// products into one fp32 accumulator.  NT: the tile copies are non-temporal (no other workgroup of
+// the call reads these rows).
+template <bool INDEXED, bool LO, bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void latent_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing][kTileBytes];
@@ -367,12 +368,12 @@ void latent_attn_kernel(AttnArgs a) {
         const bool ok = p >= 0 && p < L;
         if (lane == 0) vrow[t % kRing][r] = ok;
         p = ok ? p : 0;
-        row_to_lds(seq + (size_t)p * kRowBytes, dst, lane16, (uint32_t)(swz(r) << 4));
+        row_to_lds<NT>(seq + (size_t)p * kRowBytes, dst, lane16, (uint32_t)(swz(r) << 4));
       } else {
         const int first = s_begin + t * kTile;
         const int row = min(r, s_end - 1 - first);
-        row_to_lds_at(seq + (size_t)first * kRowBytes, (uint32_t)(row * kRowBytes), dst, lane16,
-                      (uint32_t)(swz(r) << 4));
+        row_to_lds_at<NT>(seq + (size_t)first * kRowBytes, (uint32_t)(row * kRowBytes), dst, lane16,
+                          (uint32_t)(swz(r) << 4));
       }
     };
     // Every row read is a visible row: rows past the split repeat its last row and indexed
@@ -490,6 +491,8 @@ void latent_attn_kernel(AttnArgs a) {
 // in the last tile; a split that holds only that position gives the earlier query an empty
 // partial (m = -inf, l = 0, o = 0), which the merge handles.  Each query's products, softmax and
 // sums are those of the single-query form in the same order, so the two forms give the same bits.
+// NT as for latent_attn_kernel.
+template <bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void latent_attn_pair_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing][kTileBytes];
@@ -623,8 +626,8 @@ void latent_attn_pair_kernel(AttnArgs a) {
       const uint32_t dst = lds0 + (t % kRing) * kTileBytes + r * kRowBytes;
       const int first = s_begin + t * kTile;
       const int row = min(r, s_end - 1 - first);
-      row_to_lds_at(seq + (size_t)first * kRowBytes, (uint32_t)(row * kRowBytes), dst, lane16,
-                    (uint32_t)(swz(r) << 4));
+      row_to_lds_at<NT>(seq + (size_t)first * kRowBytes, (uint32_t)(row * kRowBytes), dst, lane16,
+                        (uint32_t)(swz(r) << 4));
     };
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -807,12 +810,23 @@ hipError_t launch_latent_attn(const AttnArgs& a, bool indexed, hipStream_t strea
   void* args[] = {const_cast<AttnArgs*>(&a)};
   const dim3 grid(a.total_wg), block(kThreads);
   const void* k;
-  if (a.q_abs_lo != nullptr)
-    k = indexed ? (const void*)&latent_attn_kernel<true, true> : (const void*)&latent_attn_kernel<false, true>;
-  else
-    k = indexed                            ? (const void*)&latent_attn_kernel<true, false>
-        : queries_per_wg(false, a.Q) == 2 ? (const void*)&latent_attn_pair_kernel
-                                          : (const void*)&latent_attn_kernel<false, false>;
+  if (a.stream_once) {
+    if (a.q_abs_lo != nullptr)
+      k = indexed ? (const void*)&latent_attn_kernel<true, true, true>
+                  : (const void*)&latent_attn_kernel<false, true, true>;
+    else
+      k = indexed                            ? (const void*)&latent_attn_kernel<true, false, true>
+          : queries_per_wg(false, a.Q) == 2 ? (const void*)&latent_attn_pair_kernel<true>
+                                            : (const void*)&latent_attn_kernel<false, false, true>;
+  } else {
+    if (a.q_abs_lo != nullptr)
+      k = indexed ? (const void*)&latent_attn_kernel<true, true, false>
+                  : (const void*)&latent_attn_kernel<false, true, false>;
+    else
+      k = indexed                            ? (const void*)&latent_attn_kernel<true, false, false>
+          : queries_per_wg(false, a.Q) == 2 ? (const void*)&latent_attn_pair_kernel<false>
+                                            : (const void*)&latent_attn_kernel<false, false, false>;
+  }
   return hipLaunchKernel(k, grid, block, args, 0, stream);
 }
 

@@ -192,6 +192,9 @@ int attn_common(const uint16_t* q_abs, const uint16_t* q_abs_lo, const uint16_t*
   a.num_splits = s;
   a.split_len = split_length(max_positions, s);
   a.total_wg = (int32_t)total;
+  // one workgroup per (sequence, split): no other workgroup reads its rows, so they are streamed
+  // non-temporally; with several queries or head groups per sequence the rows are shared in L2
+  a.stream_once = units * head_groups(H) == 1;
   a.o_lat = fused ? (s > 1 ? nullptr : (float*)workspace) : o_lat;
   a.lse = lse;
   const size_t rows = (size_t)s * B * Q * H;

@@ -73,6 +73,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Cache policy of the row copies below: NT marks the copy non-temporal, for a stream whose rows no
+// other workgroup of the call reads (they are not kept for reuse in L2 or the Infinity Cache, so
+// the stream does not push out data that is read again, and a plain read of 256 MiB ran at 6.8
+// against 6.1 TB/s with it).  Rows that several workgroups share through L2 (the queries of one
+// sequence on one XCD) take the default policy.
+//
 // One 1 KiB row, global -> LDS without passing through registers: lane s copies the 16
 // bytes at row + (lane16(s) ^ sw) to lds + 16 * s, lane16 = 16 * s.  `row`, `lds` and `sw`
 // are wave-uniform (SGPRs).  Issued from asm so that the compiler does not wait for these
@@ -81,6 +87,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // live in the caller; the load reads it when it issues.  M0 is written one wait state before
 // the copy uses it; the kernels that call this use M0 for nothing else (no LDS-DMA builtins, no
 // indirect register indexing), so clobbering it is safe.
+template <bool NT>
 __device__ __forceinline__ void row_to_lds(const uint8_t* row, uint32_t lds, uint32_t lane16, uint32_t sw) {
   // the operands are wave-uniform by construction; readfirstlane makes them SGPRs for certain
   const uint64_t ra = (uint64_t)(uintptr_t)row;
@@ -91,18 +98,28 @@ __device__ __forceinline__ void row_to_lds(const uint8_t* row, uint32_t lds, uin
   uint32_t voff;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "v_xor_b32 %0, %2, %3\n\t"
-      "global_load_lds_dwordx4 %0, %4"
-      : "=&v"(voff)
-      : "s"(ls), "s"(ss), "v"(lane16), "s"(rs)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "v_xor_b32 %0, %2, %3\n\t"
+        "global_load_lds_dwordx4 %0, %4 nt"
+        : "=&v"(voff)
+        : "s"(ls), "s"(ss), "v"(lane16), "s"(rs)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "v_xor_b32 %0, %2, %3\n\t"
+        "global_load_lds_dwordx4 %0, %4"
+        : "=&v"(voff)
+        : "s"(ls), "s"(ss), "v"(lane16), "s"(rs)
+        : "memory", "m0");
 #pragma clang diagnostic pop
 }
 
 // As row_to_lds, for a row `off` bytes past a wave-uniform `base`: the lane offset is
 // (lane16 ^ sw) + off, so consecutive rows share one base address.
+template <bool NT>
 __device__ __forceinline__ void row_to_lds_at(const uint8_t* base, uint32_t off, uint32_t lds, uint32_t lane16,
                                               uint32_t sw) {
   const uint64_t ra = (uint64_t)(uintptr_t)base;
@@ -114,14 +131,24 @@ __device__ __forceinline__ void row_to_lds_at(const uint8_t* base, uint32_t off,
   uint32_t voff;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "v_xor_b32 %0, %2, %3\n\t"
-      "v_add_u32 %0, %4, %0\n\t"
-      "global_load_lds_dwordx4 %0, %5"
-      : "=&v"(voff)
-      : "s"(ls), "s"(ss), "v"(lane16), "s"(os), "s"(rs)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "v_xor_b32 %0, %2, %3\n\t"
+        "v_add_u32 %0, %4, %0\n\t"
+        "global_load_lds_dwordx4 %0, %5 nt"
+        : "=&v"(voff)
+        : "s"(ls), "s"(ss), "v"(lane16), "s"(os), "s"(rs)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "v_xor_b32 %0, %2, %3\n\t"
+        "v_add_u32 %0, %4, %0\n\t"
+        "global_load_lds_dwordx4 %0, %5"
+        : "=&v"(voff)
+        : "s"(ls), "s"(ss), "v"(lane16), "s"(os), "s"(rs)
+        : "memory", "m0");
 #pragma clang diagnostic pop
 }
 

@@ -23,6 +23,8 @@ struct AttnArgs {
   float scale_log2;               // softmax scale * log2(e)
   int32_t num_splits, split_len;  // split_len: positions (or index slots) per split, multiple of the tile
   int32_t total_wg;
+  int32_t stream_once;            // 1: every cache row is read by one workgroup only (launches the
+                                  // split kernel instance whose tile copies are non-temporal)
   float* o_lat;                   // [B][Q][H][R] fp32 (written directly when num_splits == 1)
   float* lse;                     // [B][Q][H] or null
   uint16_t* part_o;               // [S][B*Q][H][R] fp16 bits: the split's normalised partial o / l

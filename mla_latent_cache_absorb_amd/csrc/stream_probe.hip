@@ -1,5 +1,6 @@
 // Streaming-read measurement for gfx950 (not a step of the attention path).  It reads a buffer
-// once with 16-byte vector loads: each workgroup takes 32 KiB chunks in turn (chunk c by workgroup
+// once with 16-byte non-temporal vector loads (the policy the attention kernels give a cache stream
+// that no other workgroup shares): each workgroup takes 32 KiB chunks in turn (chunk c by workgroup
 // c mod grid, so consecutive workgroups read consecutive chunks), eight loads in flight per lane,
 // and folds the bytes into one value that is stored only if it equals a caller-given value, so
 // that no load can be dropped and practically nothing is written.  Its rate is the device's plain
@@ -17,14 +18,16 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 constexpr int kGrid = 8192;
 
-__global__ __launch_bounds__(kThreads) void stream_read_kernel(const int4* __restrict__ src, size_t chunks,
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const i32x4* __restrict__ src, size_t chunks,
                                                                uint32_t never, uint32_t* __restrict__ sink) {
   uint32_t acc = 0;
   for (size_t c = blockIdx.x; c < chunks; c += gridDim.x) {
-    const int4* p = src + c * (kThreads * kUnroll);
-    int4 v[kUnroll];
+    const i32x4* p = src + c * (kThreads * kUnroll);
+    i32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = p[u * kThreads + threadIdx.x];
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(p + u * kThreads + threadIdx.x);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= (uint32_t)(v[u].x ^ v[u].y ^ v[u].z ^ v[u].w);
   }
@@ -36,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const int4* __res
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t never, uint32_t* sink, hipStream_t stream) {
   const size_t chunks = bytes / kStreamChunkBytes;
   const int grid = chunks < (size_t)kGrid ? (int)chunks : kGrid;
-  const int4* s = (const int4*)src;
+  const i32x4* s = (const i32x4*)src;
   void* args[] = {(void*)&s, (void*)&chunks, (void*)&never, (void*)&sink};
   return hipLaunchKernel((const void*)&stream_read_kernel, dim3(grid), dim3(kThreads), args, 0, stream);
 }
