@@ -749,9 +749,11 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(AttnArgs a) 
   float lse2;
   f32x4 o[2];
   merge_one_group8_blocks<2>(g[0].mm, g[0].ll, v, a.num_splits, &lse2, o);
+  // the merged rows are the call's output, written once and not read again here: non-temporal
+  // stores (16 MiB of o_lat at 32 x 4 indexed: 66.4 -> 64.6 us for the call)
   float* dst = a.o_lat + row * kLatent + 8 * t;
-  *(f32x4*)dst = o[0];
-  *(f32x4*)(dst + 4) = o[1];
+  __builtin_nontemporal_store(o[0], (f32x4*)dst);
+  __builtin_nontemporal_store(o[1], (f32x4*)(dst + 4));
   if (a.lse != nullptr && t == 0) a.lse[row] = lse2 * 0.69314718055994531f;
 }
 
@@ -796,9 +798,9 @@ __global__ __launch_bounds__(512) void combine_wide_kernel(AttnArgs a) {
     __syncthreads();  // the round's slots are rewritten by the next round
   }
   if (q == 0) {
-    float* dst = a.o_lat + row * kLatent + 8 * t;
-    *(f32x4*)dst = acc[0] * (1.0f / L[0]);
-    *(f32x4*)(dst + 4) = acc[1] * (1.0f / L[1]);
+    float* dst = a.o_lat + row * kLatent + 8 * t;  // output: non-temporal, as in combine_kernel
+    __builtin_nontemporal_store(acc[0] * (1.0f / L[0]), (f32x4*)dst);
+    __builtin_nontemporal_store(acc[1] * (1.0f / L[1]), (f32x4*)(dst + 4));
     // __builtin_amdgcn_logf is the hardware base-2 logarithm
     if (a.lse != nullptr && t == 0) a.lse[row] = (M[0] + __builtin_amdgcn_logf(L[0])) * 0.69314718055994531f;
   }

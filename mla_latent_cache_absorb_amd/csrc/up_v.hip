@@ -225,7 +225,8 @@ __global__ __launch_bounds__(kFuseThreads) void up_v_kernel(MergeUpArgs a) {
     // lane holds row prow0 + ql, output dims d0 + 4g .. +3 (with 8 rows a pass, rows 8..15 of the
     // staging were not written: those columns are dropped)
     const int orow = prow0 + ql;
-    if (orow < a.rows && ql < rpp) *(f32x4*)(a.out + ((size_t)orow * a.H + h) * kHeadDim + d0 + 4 * g) = acc;
+    if (orow < a.rows && ql < rpp)  // the call's output: a non-temporal store
+      __builtin_nontemporal_store(acc, (f32x4*)(a.out + ((size_t)orow * a.H + h) * kHeadDim + d0 + 4 * g));
   }
 }
 
