@@ -453,13 +453,7 @@ void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         if (n + kAhead < 8) load(n + kAhead, (n + kAhead) % (kAhead + 1));
-        // the step's four row copies go out together, before its first product (indexed 32 x 4:
-        // 64.0 us against 64.4-66.3 us with one copy between every other product, in one process
-        // on each of two boxes; dense calls unchanged)
-        if (n == 0 && cp < ntiles) {
-#pragma unroll
-          for (int rr = 0; rr < kRowsPerVWave; ++rr) issue_row(cp, rr);
-        }
+        if ((n & 1) == 0 && cp < ntiles) issue_row(cp, n >> 1);
         __builtin_amdgcn_sched_barrier(0);
         o[n & 3] = mfma32(concat_bf16(tv[n % (kAhead + 1)][0], tv[n % (kAhead + 1)][1]), pf[n >> 2], o[n & 3]);
         __builtin_amdgcn_sched_barrier(0);
@@ -699,10 +693,7 @@ void latent_attn_pair_kernel(AttnArgs a) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         if (n + kAhead < 8) load(n + kAhead, (n + kAhead) % (kAhead + 1));
-        if (n == 0 && cp < ntiles) {  // the step's row copies together, as in latent_attn_kernel
-#pragma unroll
-          for (int rr = 0; rr < kRowsPerVWave; ++rr) issue_row(cp, rr);
-        }
+        if ((n & 1) == 0 && cp < ntiles) issue_row(cp, n >> 1);
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8 av = concat_bf16(tv[n % (kAhead + 1)][0], tv[n % (kAhead + 1)][1]);
         o[0][n & 3] = mfma32(av, pf[0], o[0][n & 3]);
